@@ -1,0 +1,158 @@
+/*
+ * kdtopk.h - C ABI of the MI355X (gfx950) fused top-K knowledge-distillation
+ * library: the chunked LM head + sparse top-K KD loss (forward and backward)
+ * and the companion teacher-cache build.
+ *
+ * Sources, cited by title and section:
+ *  [TG]  "The Gradient That Top-k Distillation Never Computes" (Khanbayov,
+ *        Kurban): abstract; Figure 2 (renormalized objective, tail masses);
+ *        Figure 3 (top-k cache of the teacher's logits; z = U g + b from a
+ *        hidden-state cache, 2dV FLOP per token).
+ *  [TA]  "Tail-Aware Top-k On-Policy Distillation" (Huang, Wei), abstract:
+ *        top-k bins plus one tail bin carrying the tail probability.
+ *  [TT]  "Unbiased Top-k Estimation for On-Policy Distillation" (Meng et
+ *        al.), abstract and Table 2: reverse KL over normalized top-k
+ *        distributions, the student's own top-16 as the support.
+ *  [FK]  "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits
+ *        and a Fused Chunked KL Loss": section 3.2, identity (2) (partial
+ *        retained mass, only log Z spans the vocabulary) and Eq. (3) (logit
+ *        gradient = M * softmax minus a sparse teacher term); the fused
+ *        chunked loss never materialises the [T, V] logits.
+ *  [SS]  "Sparse Teacher Support Cuts LLM Distillation Cost Without Losing
+ *        Accuracy": the adaptive support k_rho = min{k : top-k mass >= rho}.
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers (HIP device memory of the
+ *    current device) unless marked "host".  Row-major, no strides.
+ *  - bf16 arrays are passed as their 16-bit patterns (kd_bf16).
+ *  - The caller owns every buffer, including the workspace `ws`, whose size
+ *    comes from the matching *_workspace() query.  The library allocates no
+ *    device memory.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t, NULL = the
+ *    default stream).  Argument errors are detected on the host before any
+ *    launch and return a non-zero status with nothing enqueued; a launch
+ *    failure returns KD_EHIP.  kd_last_error() then describes the problem.
+ *  - No atomics touch floating-point results: outputs are bitwise
+ *    reproducible from run to run on the same device.
+ *  - Shape limits: 1 <= K <= min(V, 1024); d % 64 == 0; d <= 16384;
+ *    T >= 0; V >= 1.
+ */
+#ifndef KDTOPK_H
+#define KDTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t kd_bf16;
+
+typedef enum {
+  KD_OK = 0,
+  KD_EINVAL = 1,        /* invalid argument (shape, null pointer, mode) */
+  KD_EUNSUPPORTED = 2,  /* valid but outside this build's limits */
+  KD_ENOWS = 3,         /* workspace too small */
+  KD_EHIP = 4           /* a HIP runtime call or launch failed */
+} kd_status;
+
+/* Loss modes.  Per token t, with z = W h_t, p = softmax(z), S = the cached
+ * indices, q_v = exp(teacher_logp_v) on S, Q = sum_S q, m_p = 1 - sum_S p,
+ * p_hat / q_hat = p / q renormalized over S:
+ *   KD_RENORM  L = KL(q_hat || p_hat)                    [TG abstract, Fig. 2]
+ *   KD_TAIL    L = sum_S q log(q/p) + m_q log(m_q/m_p)   [TA abstract; the
+ *              (K+1)-bin KL, read in the forward direction]
+ *   KD_FULL    L = sum_S q (log q - z) + Q * logsumexp(z) [FK sec. 3.2, (2);
+ *              equals the dense KL(q || p) when S covers the vocabulary]
+ *   KD_REVERSE L = KL(p_hat || q_hat)                    [TT abstract]
+ * The gradient dL/dz is the exact derivative of L; for KD_FULL it is Eq. (3). */
+typedef enum { KD_RENORM = 0, KD_TAIL = 1, KD_FULL = 2, KD_REVERSE = 3 } kd_mode;
+
+/* Bytes of device workspace kd_topk_loss_fwd_bwd needs for these sizes.
+ * Linear in T for fixed (d, V, K, chunk).  Returns 0 for invalid sizes. */
+size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk);
+
+/* Fused chunked LM head + top-K KD loss, forward and backward [FK sec. 3.2].
+ *
+ * In:  h            [T, d] bf16   student final hidden states
+ *      W            [V, d] bf16   LM-head (unembedding) rows
+ *      idx          [T, K] int32  retained indices per token, distinct within a
+ *                                 row, in [0, V) or -1 for an ignored padding slot;
+ *                                 any order.  Values >= V are rejected on the
+ *                                 device by writing NaN to *loss.
+ *      teacher_logp [T, K] fp32   teacher log-probabilities at idx.  KD_TAIL and
+ *                                 KD_FULL expect full-vocabulary-normalised values;
+ *                                 KD_RENORM and KD_REVERSE accept any per-row shift.
+ *      m_q          [T]    fp32   teacher tail mass (KD_TAIL only; may be NULL
+ *                                 for the other modes)
+ *      mode         kd_mode
+ *      chunk        vocabulary rows per chunk of the backward (> 0; e.g. 8192).
+ *                   Vocabulary-sized scratch is bounded by chunk rows.
+ *      scale        loss = scale * sum_t L_t (e.g. 1/T for the token mean)
+ * Out: loss         [1]    fp32   the scalar loss
+ *      loss_tok     [T]    fp32   per-token L_t (unscaled), or NULL
+ *      lse          [T]    fp32   logsumexp of each token's logits, or NULL
+ *      m_p          [T]    fp32   student tail mass outside S, or NULL
+ *      dh           [T, d] fp32   dloss/dh, fully written
+ *      dW           [V, d] fp32   dloss/dW, fully written
+ * The [T, V] logits are never stored: the forward keeps only per-token
+ * partial logsumexps and the K gathered logits; the backward recomputes
+ * one vocabulary chunk of logits at a time and folds the closed-form dz
+ * into dh and dW. */
+kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                               const float* teacher_logp, const float* m_q,
+                               int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                               int32_t chunk, float scale,
+                               float* loss, float* loss_tok, float* lse, float* m_p,
+                               float* dh, float* dW,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace kd_topk_cache_build needs.  Returns 0 for
+ * invalid sizes. */
+size_t kd_topk_cache_build_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho);
+
+/* Teacher-cache build [TG Fig. 3; FK sec. 3.2; SS]: z = U g + b per token,
+ * then per row the top-K logits, logsumexp, tail mass and adaptive k_rho.
+ *
+ * In:  g        [T, d] bf16   teacher final hidden states
+ *      U        [V, d] bf16   teacher LM-head rows
+ *      b        [V]    fp32   bias, or NULL for none
+ *      K        entries kept per token (1 <= K <= min(V, 1024))
+ *      rho_host [n_rho] fp32  HOST array of target masses in (0, 1], or NULL
+ *               when n_rho == 0 (0 <= n_rho <= 8)
+ * Out: idx      [T, K] int32  retained indices, ordered by logit descending,
+ *                             ties to the lower index (-0.0 ties with +0.0)
+ *      val      [T, K] fp32   the fp32 logits z at idx (bitwise)
+ *      lse      [T]    fp32   logsumexp of z
+ *      m_q      [T]    fp32   1 - sum_{top-K} exp(val - lse), the tail mass
+ *      k_rho    [T, n_rho] int32  smallest k whose top-k mass reaches rho[j]
+ *               over the full row (may exceed K), or NULL when n_rho == 0
+ * Teacher log-probabilities for the loss are val - lse. */
+kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, const float* b,
+                              int64_t T, int64_t d, int64_t V, int32_t K,
+                              const float* rho_host, int32_t n_rho,
+                              int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace kd_topk_rows needs. */
+size_t kd_topk_rows_workspace(int64_t T, int64_t V, int32_t K, int32_t n_rho);
+
+/* The row pass of the cache build on caller-provided fp32 logits z [T, V]
+ * (no NaN): same outputs and ordering rules as kd_topk_cache_build.  On
+ * identical fp32 inputs the selected indices and values are exact. */
+kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K,
+                       const float* rho_host, int32_t n_rho,
+                       int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Message describing the last non-KD_OK status returned on this thread. */
+const char* kd_last_error(void);
+
+/* Library version string. */
+const char* kd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDTOPK_H */

@@ -112,7 +112,7 @@ def _zipf_block(args):
     ranks = r.permuted(np.broadcast_to(np.arange(V, dtype=np.int64), (rows, V)), axis=1)
     eps = r.standard_normal((rows, V), dtype=np.float32)
     base = (-expo * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
-    return base[ranks] + np.float32(noise) * eps
+    return np.ascontiguousarray(base[ranks] + np.float32(noise) * eps)
 
 
 def zipf_teacher_logits(T: int, V: int, seed: int = 0, exponent: float = 1.2,
@@ -132,7 +132,7 @@ def zipf_teacher_logits(T: int, V: int, seed: int = 0, exponent: float = 1.2,
         jobs.append((seed, b, min(BLOCK, T - r0), V, exponent, noise))
     if not jobs:
         return np.zeros((0, V), np.float32)
-    return np.concatenate(_map_blocks(_zipf_block, jobs), axis=0)
+    return np.ascontiguousarray(np.concatenate(_map_blocks(_zipf_block, jobs), axis=0))
 
 
 def tie_heavy_logits(rows: int, V: int, seed: int = 0, step: float = 0.25,

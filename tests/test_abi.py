@@ -1,0 +1,84 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function
+include/kdtopk.h declares, sizes workspaces, and rejects bad arguments on
+the host before any GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_kd_loss_amd as kd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kdtopk.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_two_calls():
+    names = _declared()
+    for n in ("kd_topk_loss_fwd_bwd", "kd_topk_cache_build", "kd_topk_loss_workspace",
+              "kd_topk_cache_build_workspace", "kd_topk_rows", "kd_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = kd.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert set(_declared()) == set(kd.EXPORTS)
+    assert "gfx950" in kd.version()
+
+
+def test_workspace_is_linear_in_tokens():
+    L = kd.lib()
+    for mode in (kd.RENORM, kd.TAIL):
+        w = [L.kd_topk_loss_workspace(T, 2560, 151936, 64, mode, 8192) for T in (4096, 8192, 16384, 32768)]
+        assert all(x > 0 for x in w)
+        d1, d2, d3 = w[1] - w[0], w[2] - w[1], w[3] - w[2]
+        # exactly linear up to 256-byte alignment of the sub-buffers
+        assert abs(2 * d1 - d2) < 64 * 256 and abs(2 * d2 - d3) < 64 * 256
+    # the dense-mode scratch is bounded by the chunk, not by V
+    a = L.kd_topk_loss_workspace(4096, 2048, 151936, 15, kd.TAIL, 8192)
+    b = L.kd_topk_loss_workspace(4096, 2048, 151936, 15, kd.TAIL, 16384)
+    assert b > a
+
+
+@pytest.mark.parametrize("args", [
+    (0, 64, 100, 0, 0, 8192),      # K = 0
+    (8, 64, 100, 101, 0, 8192),    # K > V
+    (8, 60, 100, 4, 0, 8192),      # d % 64
+    (8, 64, 100, 4, 7, 8192),      # mode
+    (8, 64, 100, 4, 0, 0),         # chunk
+    (8, 64, 5000, 1025, 0, 8192),  # K > 1024
+])
+def test_invalid_sizes_rejected(args):
+    L = kd.lib()
+    assert L.kd_topk_loss_workspace(*args) == 0
+    T, d, V, K, mode, chunk = args
+    st = L.kd_topk_loss_fwd_bwd(None, None, None, None, None, T, d, V, K, mode, chunk, 1.0,
+                                None, None, None, None, None, None, None, 0, None)
+    assert st == 1  # KD_EINVAL
+    assert L.kd_last_error()
+
+
+def test_workspace_too_small_is_reported_before_launch():
+    L = kd.lib()
+    buf = ctypes.create_string_buffer(16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    st = L.kd_topk_loss_fwd_bwd(p, p, p, p, p, 8, 64, 100, 4, kd.TAIL, 8192, 1.0,
+                                p, None, None, None, p, p, p, 16, None)
+    assert st == 3  # KD_ENOWS
+    assert b"workspace too small" in L.kd_last_error()
+
+
+def test_cache_argument_errors():
+    L = kd.lib()
+    assert L.kd_topk_cache_build_workspace(16, 64, 1000, 8, 2) > 0
+    assert L.kd_topk_cache_build_workspace(16, 64, 1000, 8, 9) == 0
+    rho = (ctypes.c_float * 1)(1.5)
+    st = L.kd_topk_rows(None, 4, 100, 4, rho, 1, None, None, None, None, None, None, 0, None)
+    assert st == 1 and b"rho" in L.kd_last_error()

@@ -1,0 +1,135 @@
+"""GPU parity of the teacher-cache build (kd_topk_rows, kd_topk_cache_build)
+against the fp64 CPU oracle.
+
+Top-K on identical fp32 logits must match bit-exactly (indices and value
+bits; ties to the lower index).  lse and m_q: absolute 1e-5.  k_rho: the
+GPU's k is accepted when the oracle's fp64 cumulative mass satisfies
+C(k) >= rho - 1e-5 and C(k-1) < rho + 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_kd_loss_amd as kd
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+RHO = (0.9, 0.95)
+
+
+def _krho_ok(z_row64, lse, rho, k):
+    p = np.sort(np.exp(z_row64 - lse))[::-1]
+    c = np.cumsum(p)
+    ck = c[k - 1]
+    ckm1 = c[k - 2] if k >= 2 else 0.0
+    return ck >= rho - 1e-5 and ckm1 < rho + 1e-5
+
+
+def _check_rows(z, K, rho=RHO):
+    zt = torch.from_numpy(z).to(DEV)
+    o = kd.topk_rows(zt, K, rho)
+    torch.cuda.synchronize()
+    gi, gv = o.idx.cpu().numpy(), o.val.cpu().numpy()
+    glse, gmq, gk = o.lse.cpu().numpy(), o.m_q.cpu().numpy(), o.k_rho.cpu().numpy()
+    ri, rv, rlse, rmq, rk = oracle.cache_from_logits(z, K, rho)
+    np.testing.assert_array_equal(gi, ri)
+    np.testing.assert_array_equal(gv.view(np.uint32), rv.view(np.uint32))
+    fin = np.isfinite(rlse)
+    np.testing.assert_allclose(glse[fin], rlse[fin], atol=1e-5, rtol=0)
+    np.testing.assert_allclose(gmq[fin], rmq[fin], atol=1e-5, rtol=0)
+    exact = 0
+    for t in range(z.shape[0]):
+        if not fin[t]:
+            continue
+        z64 = z[t].astype(np.float64)
+        for j, r in enumerate(rho):
+            assert _krho_ok(z64, rlse[t], r, int(gk[t, j])), (t, r, int(gk[t, j]), int(rk[t, j]))
+            exact += int(gk[t, j] == rk[t, j])
+    return exact / max(1, z.shape[0] * len(rho))
+
+
+@pytest.mark.parametrize("K", [1, 8, 64, 256, 1024])
+def test_rows_zipf_bit_exact(K):
+    z = synth.zipf_teacher_logits(40, 5000, seed=K)
+    frac = _check_rows(z, K)
+    print(f"K={K} k_rho exact-match fraction {frac:.3f}")
+
+
+def test_rows_ties_signed_zero_neg_inf():
+    z = synth.tie_heavy_logits(24, 3001, seed=1, step=0.25, span=2.0)
+    z[0, :] = 0.5                      # one big tie: lowest indices win
+    z[1, ::2] = -0.0
+    z[1, 1::2] = 0.0
+    z[2, 100:2000] = -np.inf
+    z[3, :] = -np.inf
+    z[3, 17] = 1.0
+    for K in (1, 7, 100, 1024):
+        zz = z.copy()
+        if K > 1:
+            zz[3] = z[3]
+            zz[3, :K] = 0.25           # keep row 3 with at least K finite values
+        _check_rows(zz, K, rho=(0.5,))
+
+
+def test_rows_gaussian_full_vocab_width():
+    """Rows as wide as the Qwen vocabulary (V = 151,936), Gaussian logits."""
+    r = np.random.default_rng(3)
+    z = (r.standard_normal((6, 151936)) * 1.05).astype(np.float32)
+    frac = _check_rows(z, 256)
+    print(f"k_rho exact-match fraction {frac:.3f}")
+
+
+def test_rows_k_equals_v_and_ragged():
+    z = synth.tie_heavy_logits(5, 77, seed=4)
+    _check_rows(z, 77, rho=(0.9,))
+    z = synth.zipf_teacher_logits(9, 1023, seed=4)
+    _check_rows(z, 513)
+
+
+def test_cache_build_small_with_bias():
+    T, d, V, K = 300, 128, 5000, 37
+    g, U, b = synth.teacher_head(T, d, V, seed=2)
+    o = kd.cache_build(g.to(DEV), U.to(DEV), b.to(DEV), K, RHO)
+    torch.cuda.synchronize()
+    z = synth.as_f64(g) @ synth.as_f64(U).T + b.double().numpy()[None, :]
+    ri, rv, rlse, rmq, rk = oracle.cache_from_logits(z, K, RHO)
+    gi, gv = o.idx.cpu().numpy(), o.val.cpu().numpy()
+    np.testing.assert_allclose(o.lse.cpu().numpy(), rlse, atol=1e-4)
+    np.testing.assert_allclose(o.m_q.cpu().numpy(), rmq, atol=1e-5)
+    # values are the logits at the returned indices (fp32 accumulation)
+    np.testing.assert_allclose(gv, np.take_along_axis(z, gi.astype(np.int64), 1), atol=1e-4)
+    # the returned set is a valid top-K of the fp64 logits up to fp32 rounding
+    for t in range(T):
+        kth = np.sort(z[t])[::-1][K - 1]
+        assert np.all(z[t, gi[t]] >= kth - 2e-4)
+        assert len(set(gi[t].tolist())) == K
+    agree = np.mean([len(set(gi[t]) & set(ri[t])) / K for t in range(T)])
+    assert agree > 0.99, agree
+    gk = o.k_rho.cpu().numpy()
+    for t in range(0, T, 7):
+        for j, r in enumerate(RHO):
+            assert _krho_ok(z[t], rlse[t], r, int(gk[t, j]))
+
+
+def test_cache_build_student_head_no_bias():
+    T, d, V, K = 64, 64, 1024, 16
+    h, W = synth.student_head(T, d, V, seed=9)
+    o = kd.cache_build(h.to(DEV), W.to(DEV), None, K)
+    torch.cuda.synchronize()
+    z = synth.as_f64(h) @ synth.as_f64(W).T
+    _, _, rlse, rmq, _ = oracle.cache_from_logits(z, K)
+    np.testing.assert_allclose(o.lse.cpu().numpy(), rlse, atol=1e-4)
+    np.testing.assert_allclose(o.m_q.cpu().numpy(), rmq, atol=1e-5)
+    assert o.k_rho.shape == (T, 0)
+
+
+def test_rows_huge_tie_takes_lowest_indices():
+    """More equal keys than the candidate buffer holds: the ordered pass
+    must still return the lowest indices."""
+    z = np.full((3, 10000), 0.7, np.float32)
+    z[1, 5000:] = -0.0
+    z[1, :5000] = 0.0
+    z[2, 9000:] = 3.0
+    _check_rows(z, 1024, rho=(0.5, 0.9))

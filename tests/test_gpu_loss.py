@@ -1,0 +1,186 @@
+"""GPU parity of kd_topk_loss_fwd_bwd against the fp64 CPU oracle.
+
+Inputs are bf16 h, W (synth), a teacher cache built by the oracle from
+Zipf-like teacher logits, and the same values upcast exactly for the
+oracle.  Bar: loss relative error <= 1e-3; dh and dW relative Frobenius
+error <= 1e-2 (bf16 operands, fp32 accumulation, bf16 dz workspace).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_kd_loss_amd as kd
+from _inputs import rel_err, rel_fro, student_topk_cache, teacher_cache
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LOSS_RTOL = 1e-3
+GRAD_RTOL = 1e-2
+
+
+def _run(h, W, idx, tlp, mq, mode, chunk):
+    out = kd.loss_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV),
+                          torch.from_numpy(mq).to(DEV) if mq is not None else None, mode=mode, chunk=chunk)
+    torch.cuda.synchronize()
+    return {k: getattr(out, k).cpu().numpy() for k in out._fields}
+
+
+def _case(T, d, V, K, mode, seed):
+    h, W = synth.student_head(T, d, V, seed=seed)
+    if mode == kd.REVERSE:
+        idx, tlp = student_topk_cache(h, W, K, T, V, seed=seed)
+        mq = np.zeros(T, np.float32)
+    else:
+        idx, tlp, mq = teacher_cache(T, V, K, seed=seed)
+    return h, W, idx, tlp, mq
+
+
+def _compare(g, r, tag, loss_floor=1e-6):
+    assert np.isfinite(g["loss"]).all(), tag
+    assert rel_err(g["loss"], r["loss"], loss_floor) <= LOSS_RTOL, (tag, float(g["loss"]), r["loss"])
+    np.testing.assert_allclose(g["lse"], r["lse"], atol=2e-4, rtol=0, err_msg=tag)
+    np.testing.assert_allclose(g["m_p"], r["m_p"], atol=2e-4, rtol=0, err_msg=tag)
+    lt = np.abs(g["loss_tok"] - r["loss_tok"]) / np.maximum(np.abs(r["loss_tok"]), 1e-3)
+    assert lt.max() <= 5e-3, (tag, float(lt.max()))
+    e_dh = rel_fro(g["dh"], r["dh"])
+    e_dw = rel_fro(g["dW"], r["dW"])
+    assert e_dh <= GRAD_RTOL and e_dw <= GRAD_RTOL, (tag, e_dh, e_dw)
+    return e_dh, e_dw
+
+
+@pytest.mark.parametrize("mode", [kd.RENORM, kd.TAIL, kd.FULL, kd.REVERSE])
+def test_tiny_config_all_modes(mode):
+    """T=64, d=64, V=1024, K=8: the CPU-seconds workload, every mode."""
+    T, d, V, K = 64, 64, 1024, 8
+    h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=0)
+    g = _run(h, W, idx, tlp, mq, mode, chunk=8192)
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    e = _compare(g, r, f"tiny mode={mode}")
+    print(f"tiny mode={mode} loss={float(g['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
+@pytest.mark.parametrize("mode", [kd.RENORM, kd.TAIL, kd.FULL, kd.REVERSE])
+def test_ragged_multi_chunk(mode):
+    """Sizes that are not multiples of any tile, several chunks, ragged last chunk."""
+    T, d, V, K = 300, 128, 2500, 13
+    h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=3)
+    g = _run(h, W, idx, tlp, mq, mode, chunk=700)  # rounded up to 768 rows per chunk
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    _compare(g, r, f"ragged mode={mode}")
+
+
+def test_worked_example_fig2():
+    """The twelve-token, k=4 example of "The Gradient That Top-k Distillation
+    Never Computes" (Figure 2), embedded with d=64: column 0 of W holds the
+    bf16 logits ln q, column 1 lowers the retained ones by bf16(ln 6)."""
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_fig2.json")))
+    V, k, d = gold["vocab"], gold["k"], 64
+    mq0 = gold["student_tail_mass_before"]
+    head = np.array(gold["renormalized_head"])
+    q = np.concatenate([(1 - mq0) * head, np.full(V - k, mq0 / (V - k))])
+    W = np.zeros((V, d), np.float32)
+    W[:, 0] = np.log(q)
+    W[:k, 1] = -np.log(6.0)
+    Wb = synth.to_bf16(W)
+    h = np.zeros((2, d), np.float32)
+    h[0, 0] = 1.0
+    h[1, 0] = h[1, 1] = 1.0
+    hb = synth.to_bf16(h)
+    idx = np.tile(np.arange(k, dtype=np.int32), (2, 1))
+    lq = np.log(q)
+    tlp = np.tile(lq[:k].astype(np.float32), (2, 1))
+    mq = np.full(2, 1 - q[:k].sum(), np.float32)
+    tol = 0.5 * 10 ** -gold["printed_decimals_full_vocab_kl"]
+    for mode in (kd.RENORM, kd.TAIL, kd.FULL, kd.REVERSE):
+        g = _run(hb, Wb, idx, tlp, mq, mode, chunk=8192)
+        r = oracle.loss_fwd_bwd(synth.as_f64(hb), synth.as_f64(Wb), idx, tlp, mq, mode, scale=0.5)
+        assert abs(float(g["loss"]) - r["loss"]) < 2e-5, (mode, float(g["loss"]), r["loss"])
+        np.testing.assert_allclose(g["m_p"], r["m_p"], atol=1e-5)
+        # dense modes carry dz as bf16 (relative 2^-9 per element)
+        for key in ("dh", "dW"):
+            assert rel_fro(g[key], r[key]) <= GRAD_RTOL, (mode, key, rel_fro(g[key], r[key]))
+            np.testing.assert_allclose(g[key], r[key], atol=4e-3 * np.abs(r[key]).max() + 1e-7)
+        # the printed facts, through the GPU path
+        assert abs(g["m_p"][0] - gold["student_tail_mass_before"]) < 5e-3
+        assert abs(g["m_p"][1] - gold["student_tail_mass_after"]) < 5e-3
+        if mode == kd.RENORM:
+            assert abs(g["loss_tok"][1]) < 1e-4 and abs(g["loss_tok"][0]) < 1e-4
+        if mode == kd.TAIL:
+            assert abs(g["loss_tok"][1] - gold["full_vocab_kl_after_nats"]) < tol + 5e-3
+
+
+def test_full_vocab_k_equals_v_is_dense_kl():
+    """K = V: every forward mode equals the dense KL (computed by torch's
+    kl_div on the fp64 logits), gradient p - q."""
+    T, d, V = 40, 64, 256
+    h, W = synth.student_head(T, d, V, seed=7)
+    zt = synth.zipf_teacher_logits(T, V, seed=7).astype(np.float64)
+    lq = zt - np.log(np.exp(zt - zt.max(1, keepdims=True)).sum(1, keepdims=True)) - zt.max(1, keepdims=True)
+    perm = np.stack([np.random.default_rng(t).permutation(V) for t in range(T)]).astype(np.int32)
+    tlp = np.take_along_axis(lq, perm, axis=1).astype(np.float32)
+    mq = np.zeros(T, np.float32)
+    z = torch.from_numpy(synth.as_f64(h) @ synth.as_f64(W).T)
+    dense = torch.nn.functional.kl_div(torch.log_softmax(z, 1), torch.from_numpy(np.exp(lq)),
+                                       reduction="batchmean").item()
+    for mode in (kd.RENORM, kd.TAIL, kd.FULL):
+        g = _run(h, W, perm, tlp, mq, mode, chunk=8192)
+        assert rel_err(g["loss"], dense) <= 2e-3, (mode, float(g["loss"]), dense)
+        assert np.abs(g["m_p"]).max() < 1e-5
+
+
+def test_padding_and_invalid_indices():
+    T, d, V, K = 50, 64, 777, 6
+    h, W, idx, tlp, mq = _case(T, d, V, K, kd.TAIL, seed=5)
+    pidx = np.concatenate([idx, -np.ones((T, 3), np.int32)], axis=1)
+    ptlp = np.concatenate([tlp, np.full((T, 3), 9.0, np.float32)], axis=1)
+    a = _run(h, W, idx, tlp, mq, kd.TAIL, chunk=8192)
+    b = _run(h, W, pidx, ptlp, mq, kd.TAIL, chunk=8192)
+    assert rel_err(b["loss"], a["loss"]) < 1e-6
+    assert rel_fro(b["dW"], a["dW"]) < 1e-6
+    bad = idx.copy()
+    bad[3, 2] = V + 5
+    c = _run(h, W, bad, tlp, mq, kd.TAIL, chunk=8192)
+    assert np.isnan(c["loss"])
+
+
+def test_bitwise_deterministic():
+    T, d, V, K = 200, 128, 3000, 9
+    for mode in (kd.TAIL, kd.RENORM):
+        h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=11)
+        a = _run(h, W, idx, tlp, mq, mode, chunk=1024)
+        b = _run(h, W, idx, tlp, mq, mode, chunk=1024)
+        for key in ("loss", "dh", "dW", "lse", "m_p"):
+            assert np.array_equal(a[key].view(np.uint32), b[key].view(np.uint32)), (mode, key)
+
+
+def test_empty_tokens():
+    V, d, K = 300, 64, 4
+    W = synth.to_bf16(synth.normal_f32(V, d, 0.1, 0, 2)).to(DEV)
+    h = torch.zeros((0, d), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((0, K), dtype=torch.int32, device=DEV)
+    tlp = torch.zeros((0, K), dtype=torch.float32, device=DEV)
+    out = kd.loss_fwd_bwd(h, W, idx, tlp, torch.zeros(0, device=DEV), mode=kd.TAIL)
+    torch.cuda.synchronize()
+    assert float(out.loss) == 0.0
+    assert float(out.dW.abs().max()) == 0.0
+
+
+def test_argument_errors():
+    V, d, K, T = 300, 64, 4, 8
+    W = torch.zeros((V, d), dtype=torch.bfloat16, device=DEV)
+    h = torch.zeros((T, d), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((T, K), dtype=torch.int32, device=DEV)
+    tlp = torch.zeros((T, K), dtype=torch.float32, device=DEV)
+    with pytest.raises(kd.KDError, match="KD_TAIL needs m_q"):
+        kd.loss_fwd_bwd(h, W, idx, tlp, None, mode=kd.TAIL)
+    with pytest.raises(kd.KDError):
+        kd.loss_fwd_bwd(h[:, :32].contiguous(), W[:, :32].contiguous(), idx, tlp, None, mode=kd.RENORM)
+    with pytest.raises(ValueError):
+        kd.loss_fwd_bwd(h.cpu(), W, idx, tlp, None, mode=kd.RENORM)

@@ -1,0 +1,209 @@
+"""Python binding of libkdtopk.so: the fused top-K KD loss and the teacher
+cache build on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library behind the C ABI declared in include/kdtopk.h.  PyTorch provides
+device memory and the current stream.  There is no CPU fallback: the calls
+raise if the library is not built or the tensors are not on a GPU.
+
+    out = loss_fwd_bwd(h, W, idx, teacher_logp, m_q, mode=TAIL, chunk=8192)
+    out.loss, out.dh, out.dW, out.loss_tok, out.lse, out.m_p
+    idx, val, lse, m_q, k_rho = cache_build(g, U, b, K, rho=(0.9, 0.95))
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional, Sequence
+
+import torch
+
+RENORM, TAIL, FULL, REVERSE = 0, 1, 2, 3
+MODE_BY_NAME = {"renorm": RENORM, "tail": TAIL, "full": FULL, "reverse": REVERSE}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkdtopk.so")
+_lib = None
+
+_i64, _i32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGS = {
+    "kd_topk_loss_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+    "kd_topk_loss_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
+                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_topk_rows_workspace": (_sz, [_i64, _i64, _i32, _i32]),
+    "kd_topk_rows": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_last_error": (ctypes.c_char_p, []),
+    "kd_version": (ctypes.c_char_p, []),
+}
+EXPORTS = tuple(_SIGS)
+
+
+class KDError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkdtopk.so (torch's HIP runtime is already in the process)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KDError(f"{LIB_PATH} is not built; run `python -m top_kd_loss_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().kd_last_error().decode(errors="replace")
+        raise KDError(f"{what} failed with status {status}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device: torch.device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class LossOut(NamedTuple):
+    loss: torch.Tensor      # [] fp32
+    dh: torch.Tensor        # [T, d] fp32
+    dW: torch.Tensor        # [V, d] fp32
+    loss_tok: torch.Tensor  # [T] fp32
+    lse: torch.Tensor       # [T] fp32
+    m_p: torch.Tensor       # [T] fp32
+
+
+def loss_workspace_bytes(T: int, d: int, V: int, K: int, mode: int, chunk: int) -> int:
+    return int(lib().kd_topk_loss_workspace(T, d, V, K, mode, chunk))
+
+
+def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_logp: torch.Tensor,
+                 m_q: Optional[torch.Tensor] = None, mode: int = TAIL, chunk: int = 8192,
+                 scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[LossOut] = None) -> LossOut:
+    """Fused LM head + top-K KD loss, forward and backward (kd_topk_loss_fwd_bwd)."""
+    if isinstance(mode, str):
+        mode = MODE_BY_NAME[mode]
+    dev = h.device
+    T, d = h.shape
+    V = W.shape[0]
+    K = idx.shape[1]
+    _need(h, "h", torch.bfloat16, (T, d), dev)
+    _need(W, "W", torch.bfloat16, (V, d), dev)
+    _need(idx, "idx", torch.int32, (T, K), dev)
+    _need(teacher_logp, "teacher_logp", torch.float32, (T, K), dev)
+    if m_q is not None:
+        _need(m_q, "m_q", torch.float32, (T,), dev)
+    if scale is None:
+        scale = 1.0 / max(T, 1)
+    L = lib()
+    ws_bytes = int(L.kd_topk_loss_workspace(T, d, V, K, mode, chunk))
+    if ws_bytes == 0:
+        _check(L.kd_topk_loss_fwd_bwd(None, None, None, None, None, T, d, V, K, mode, chunk, scale,
+                                      None, None, None, None, None, None, None, 0, None), "kd_topk_loss_fwd_bwd")
+    with torch.cuda.device(dev):
+        if workspace is None or workspace.numel() < ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        if out is None:
+            f32 = dict(dtype=torch.float32, device=dev)
+            out = LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
+                          torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
+        st = L.kd_topk_loss_fwd_bwd(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
+                                    T, d, V, K, mode, chunk, scale,
+                                    _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
+                                    _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "kd_topk_loss_fwd_bwd")
+    return out
+
+
+class CacheOut(NamedTuple):
+    idx: torch.Tensor    # [T, K] int32
+    val: torch.Tensor    # [T, K] fp32
+    lse: torch.Tensor    # [T] fp32
+    m_q: torch.Tensor    # [T] fp32
+    k_rho: torch.Tensor  # [T, n_rho] int32
+
+
+def _rho_arr(rho: Sequence[float]):
+    n = len(rho)
+    arr = (ctypes.c_float * max(n, 1))(*[float(r) for r in rho])
+    return arr, n
+
+
+def cache_build(g: torch.Tensor, U: torch.Tensor, b: Optional[torch.Tensor], K: int,
+                rho: Sequence[float] = (), workspace: Optional[torch.Tensor] = None) -> CacheOut:
+    """Teacher cache: top-K of z = U g + b per token, lse, m_q, k_rho (kd_topk_cache_build)."""
+    dev = g.device
+    T, d = g.shape
+    V = U.shape[0]
+    _need(g, "g", torch.bfloat16, (T, d), dev)
+    _need(U, "U", torch.bfloat16, (V, d), dev)
+    if b is not None:
+        _need(b, "b", torch.float32, (V,), dev)
+    L = lib()
+    arr, n = _rho_arr(rho)
+    ws_bytes = int(L.kd_topk_cache_build_workspace(T, d, V, K, n))
+    with torch.cuda.device(dev):
+        if workspace is None or workspace.numel() < ws_bytes:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        o = CacheOut(torch.empty((T, K), dtype=torch.int32, device=dev),
+                     torch.empty((T, K), dtype=torch.float32, device=dev),
+                     torch.empty(T, dtype=torch.float32, device=dev),
+                     torch.empty(T, dtype=torch.float32, device=dev),
+                     torch.empty((T, n), dtype=torch.int32, device=dev))
+        st = L.kd_topk_cache_build(_ptr(g), _ptr(U), _ptr(b), T, d, V, K, arr, n,
+                                   _ptr(o.idx), _ptr(o.val), _ptr(o.lse), _ptr(o.m_q),
+                                   _ptr(o.k_rho) if n else None, _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "kd_topk_cache_build")
+    return o
+
+
+def topk_rows(z: torch.Tensor, K: int, rho: Sequence[float] = (),
+              workspace: Optional[torch.Tensor] = None) -> CacheOut:
+    """Row pass on fp32 logits z [T, V]: top-K, lse, tail mass, k_rho (kd_topk_rows)."""
+    dev = z.device
+    T, V = z.shape
+    _need(z, "z", torch.float32, (T, V), dev)
+    L = lib()
+    arr, n = _rho_arr(rho)
+    ws_bytes = int(L.kd_topk_rows_workspace(T, V, K, n))
+    with torch.cuda.device(dev):
+        if workspace is None or workspace.numel() < ws_bytes:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        o = CacheOut(torch.empty((T, K), dtype=torch.int32, device=dev),
+                     torch.empty((T, K), dtype=torch.float32, device=dev),
+                     torch.empty(T, dtype=torch.float32, device=dev),
+                     torch.empty(T, dtype=torch.float32, device=dev),
+                     torch.empty((T, n), dtype=torch.int32, device=dev))
+        st = L.kd_topk_rows(_ptr(z), T, V, K, arr, n, _ptr(o.idx), _ptr(o.val), _ptr(o.lse), _ptr(o.m_q),
+                            _ptr(o.k_rho) if n else None, _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "kd_topk_rows")
+    return o
+
+
+def version() -> str:
+    return lib().kd_version().decode()

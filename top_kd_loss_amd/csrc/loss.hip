@@ -1,0 +1,815 @@
+// Fused chunked LM head + sparse top-K KD loss, forward and backward, for
+// gfx950 ("Efficient Knowledge Distillation for LLMs: Offline Top-K Logits
+// and a Fused Chunked KL Loss", section 3.2: the output projection is fused
+// into the loss and the [T, V] logits are never materialised).
+//
+// Pipeline of kd_topk_loss_fwd_bwd (one stream, in order):
+//   prep     sort each token's (idx, teacher_logp) by index; per-token
+//            teacher constants; per-(vocab tile, token) cursor starts.
+//   pass 1   z^T tile = W_tile h_tile^T on the matrix cores; epilogue keeps a
+//            per-(vocab tile, token) running max / sum of exp and gathers z
+//            at the retained indices.  Only log Z spans the vocabulary
+//            (identity (2) of the fused-loss paper), so this is all the
+//            forward needs from the full vocabulary.
+//   combine  per token: logsumexp, student tail mass, the loss of the mode,
+//            the dense coefficient alpha and the sparse coefficients r on S,
+//            so that dL/dz = alpha * softmax(z) + r [v in S] (Eq. (3) for the
+//            partial-mass loss; the other modes by exact differentiation).
+//   pass 2   dense modes, one vocabulary chunk at a time: recompute the z
+//            tile, write dz = scale * dL/dz as bf16 (two layouts), then
+//            dh += dz W_chunk and dW_chunk = dz^T h on the matrix cores.
+//            Sparse modes: dh_t = sum_S r W_v and dW_v = sum_t r h_t over a
+//            CSR-by-vocabulary list, deterministic without float atomics.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kdtopk.h"
+#include "gemm.h"
+#include "kd_internal.h"
+
+namespace {
+
+using TC = TileCfg<256, 256, 64, 2, 2>;
+constexpr int VT = TC::BM;        // vocabulary rows per tile (M of the z^T tile)
+constexpr int TT = TC::BN;        // tokens per tile
+constexpr int KMAX = 1024;
+constexpr int SENT = 0x7fffffff;  // sorted-index sentinel (padding)
+
+// Per-token scalars kept in the workspace (float, stride TOKF).
+enum { TK_LSE = 0, TK_ALPHA = 1, TK_L = 2, TK_MP = 3, TK_Q = 4, TK_LSEQ = 5, TK_NV = 6, TOKF = 8 };
+
+// ---------------------------------------------------------------------------
+// Tile ordering: workgroup id -> (m tile, n tile).  Workgroups are handed to
+// the 8 XCDs round robin; this sends consecutive groups of tiles to one XCD
+// and orders them GROUP_M m-tiles at a time, so the workgroups resident on
+// an XCD share operand tiles in its L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool tile_of(int bid, int nblocks, int nM, int nN, int group_m, int& mi, int& ni) {
+  const int per = nblocks / 8;  // nblocks is a multiple of 8
+  const int L = (bid % 8) * per + bid / 8;
+  if (L >= nM * nN) return false;
+  const int width = group_m * nN;
+  const int group = L / width;
+  const int first_m = group * group_m;
+  const int gsz = min(nM - first_m, group_m);
+  const int r = L - group * width;
+  mi = first_m + r % gsz;
+  ni = r / gsz;
+  return true;
+}
+
+static inline int grid_of(int tiles) { return (int)kd_round_up(tiles, 8); }
+
+// Select accumulator element `sel` (0 .. FM*16-1) of token column fn.
+__device__ __forceinline__ float acc_pick(const Acc<TC>& acc, int fn, int sel) {
+  float v = 0.f;
+#pragma unroll
+  for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (fm * 16 + e == sel) v = acc.v[fm][fn][e];
+  return v;
+}
+
+// Does this lane hold vocabulary row offset `off` (0 .. TM-1 within its
+// wavefront's rows)?  If so, returns the accumulator element index.
+__device__ __forceinline__ int acc_slot(int off, int lane) {
+  const int fm = off >> 5, w = off & 31;
+  if (((w >> 2) & 1) != (lane >> 5)) return -1;
+  return fm * 16 + (w >> 3) * 4 + (w & 3);
+}
+
+// ---------------------------------------------------------------------------
+// prep: one 64-lane workgroup per token.  Sort (idx, tlp) ascending by idx
+// with a bitonic network in LDS; padding slots (idx < 0) and indices >= V
+// sort last as SENT (the latter also raise the error flag).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, const float* __restrict__ tlp,
+                                             int64_t T, int64_t V, int K, int Kp2, int nVT, int64_t Tp,
+                                             int32_t* __restrict__ sidx, float* __restrict__ stlp,
+                                             int32_t* __restrict__ starts, float* __restrict__ tok,
+                                             int32_t* __restrict__ err) {
+  __shared__ int key[KMAX];
+  __shared__ float val[KMAX];
+  const int lane = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  bool bad = false;
+  for (int k = lane; k < Kp2; k += 64) {
+    int id = SENT;
+    float v = 0.f;
+    if (k < K) {
+      const int raw = idx[t * K + k];
+      if (raw >= V) {
+        bad = true;
+      } else if (raw >= 0) {
+        id = raw;
+        v = tlp[t * K + k];
+      }
+    }
+    key[k] = id;
+    val[k] = v;
+  }
+  __syncthreads();
+  for (int size = 2; size <= Kp2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = lane; i < Kp2 / 2; i += 64) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0);
+        const int a = key[lo], b = key[hi];
+        if ((a > b) == up) {
+          key[lo] = b;
+          key[hi] = a;
+          const float x = val[lo];
+          val[lo] = val[hi];
+          val[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int nv = 0;
+  double mx = -INFINITY;
+  for (int k = lane; k < K; k += 64) {
+    const int id = key[k];
+    sidx[t * K + k] = id;
+    stlp[t * K + k] = val[k];
+    if (id != SENT) {
+      ++nv;
+      mx = fmax(mx, (double)val[k]);
+      if (k + 1 < K && key[k + 1] == id) bad = true;  // duplicate index
+    }
+  }
+  nv = wave_sum_i32(nv);
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+  double q = 0.0;
+  for (int k = lane; k < nv; k += 64) q += exp((double)val[k] - mx);
+  q = wave_sum_f64(q);
+  // vocabulary-tile cursor starts: first sorted position with idx >= vt*VT
+  for (int vt = lane; vt < nVT; vt += 64) {
+    int lo = 0, hi = nv;
+    const int target = vt * VT;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (key[mid] < target) lo = mid + 1; else hi = mid;
+    }
+    starts[(int64_t)vt * Tp + t] = lo;
+  }
+  if (lane == 0) {
+    tok[t * TOKF + TK_NV] = (float)nv;
+    tok[t * TOKF + TK_Q] = nv > 0 ? (float)(exp(mx) * q) : 0.f;    // Q = sum_S exp(tlp)
+    tok[t * TOKF + TK_LSEQ] = nv > 0 ? (float)(mx + log(q)) : 0.f;  // logsumexp of tlp over S
+  }
+  if (bad) atomicOr(err, 1);
+}
+
+// ---------------------------------------------------------------------------
+// pass 1: z^T tile (vocab x tokens) with the logsumexp / gather epilogue.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+                                                  int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
+                                                  int64_t Tp, const int32_t* __restrict__ sidx,
+                                                  const int32_t* __restrict__ starts, float* __restrict__ zS,
+                                                  float2* __restrict__ part) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int vt, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 2, vt, tt)) return;
+  const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TC::WN, wn = wave % TC::WN;
+
+  int cur[TC::FN], nxt[TC::FN];
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
+    cur[fn] = K;
+    nxt[fn] = SENT;
+    if (t < T) {
+      cur[fn] = starts[(int64_t)vt * Tp + t];
+      nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
+    }
+  }
+
+  Acc<TC> acc;
+  gemm_tile<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
+
+  float* red = (float*)lds;  // [WM][TT][2] after the main loop
+  const int vw0 = (int)m0 + wm * TC::TM;
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    float mx = -KD_INF;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = (int)m0 + acc_row<TC>(wm, fm, e, lane);
+        if (v < V) mx = fmaxf(mx, acc.v[fm][fn][e]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float s = 0.f;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = (int)m0 + acc_row<TC>(wm, fm, e, lane);
+        if (v < V) s += __expf(acc.v[fm][fn][e] - mx);
+      }
+    s += __shfl_xor(s, 32, 64);
+    const int col = acc_col<TC>(wn, fn, lane);
+    if (lane < 32) {
+      red[(wm * TT + col) * 2 + 0] = mx;
+      red[(wm * TT + col) * 2 + 1] = s;
+    }
+    // gather z at retained indices inside this wavefront's rows
+    const int64_t t = n0 + col;
+    if (t < T) {
+      const int vw1 = vw0 + TC::TM;
+      while (nxt[fn] < vw1) {
+        const int v = nxt[fn];
+        if (v >= vw0) {
+          const int slot = acc_slot(v - vw0, lane);
+          if (slot >= 0) zS[t * K + cur[fn]] = acc_pick(acc, fn, slot);
+        }
+        ++cur[fn];
+        nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
+      }
+    }
+  }
+  __syncthreads();
+  // merge the WM wavefront rows of the tile and write one partial per token
+  for (int col = threadIdx.x; col < TT; col += TC::NT) {
+    float m = -KD_INF, s = 0.f;
+#pragma unroll
+    for (int w = 0; w < TC::WM; ++w) {
+      const float mw = red[(w * TT + col) * 2 + 0], sw = red[(w * TT + col) * 2 + 1];
+      const float mn = fmaxf(m, mw);
+      s = (m == -KD_INF ? 0.f : s * __expf(m - mn)) + (mw == -KD_INF ? 0.f : sw * __expf(mw - mn));
+      m = mn;
+    }
+    const int64_t t = n0 + col;
+    if (t < T) part[(int64_t)vt * Tp + t] = make_float2(m, s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: one wavefront per token.  All per-token math in fp64.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int64_t Tp, int mode, float scale,
+                                                 const float2* __restrict__ part, const float* __restrict__ zS,
+                                                 const int32_t* __restrict__ sidx, const float* __restrict__ stlp,
+                                                 const float* __restrict__ m_q, float* __restrict__ tok,
+                                                 float* __restrict__ coef, float* __restrict__ loss_tok,
+                                                 float* __restrict__ lse_out, float* __restrict__ mp_out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  // logsumexp over the per-tile partials
+  double m = -INFINITY, s = 0.0;
+  for (int vt = lane; vt < nVT; vt += 64) {
+    const float2 p = part[(int64_t)vt * Tp + t];
+    const double mn = fmax(m, (double)p.x);
+    s = (m == -INFINITY ? 0.0 : s * exp(m - mn)) + (double)p.y * exp((double)p.x - mn);
+    m = mn;
+  }
+  double M = m;
+  for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
+  s = (m == -INFINITY) ? 0.0 : s * exp(m - M);
+  s = wave_sum_f64(s);
+  const double lse = M + log(s);
+
+  const float* tk = tok + t * TOKF;
+  const int nv = (int)tk[TK_NV];
+  const double Q = tk[TK_Q], lseq = tk[TK_LSEQ];
+  // student mass on S and the retained-logit logsumexp
+  double zmax = -INFINITY;
+  for (int k = lane; k < nv; k += 64) zmax = fmax(zmax, (double)zS[t * K + k]);
+  for (int o = 32; o > 0; o >>= 1) zmax = fmax(zmax, __shfl_xor(zmax, o, 64));
+  double es = 0.0;
+  for (int k = lane; k < nv; k += 64) es += exp((double)zS[t * K + k] - zmax);
+  es = wave_sum_f64(es);
+  const double lseS = (nv > 0) ? zmax + log(es) : -INFINITY;
+  double mp = (nv > 0) ? -expm1(lseS - lse) : 1.0;
+  if (mp < 0.0) mp = 0.0;
+  const double mq = (mode == KD_TAIL) ? (double)m_q[t] : 0.0;
+  const double tiny = 1.1754943508222875e-38;
+  const double mps = mp > tiny ? mp : tiny;
+  const double ratio = (mode == KD_TAIL && mq > 0.0) ? mq / mps : 0.0;
+
+  // per-entry terms; L accumulates in fp64
+  double L = 0.0;
+  for (int k = lane; k < nv; k += 64) {
+    const double z = zS[t * K + k], tl = stlp[t * K + k];
+    const double q = exp(tl);
+    if (mode == KD_RENORM) {
+      const double lqh = tl - lseq, lph = z - lseS;
+      L += exp(lqh) * (lqh - lph);
+    } else if (mode == KD_TAIL) {
+      L += q * (tl - (z - lse));
+    } else if (mode == KD_FULL) {
+      L += q * (tl - z);
+    } else {
+      const double lqh = tl - lseq, lph = z - lseS;
+      L += exp(lph) * (lph - lqh);
+    }
+  }
+  L = wave_sum_f64(L);
+  if (mode == KD_TAIL && mq > 0.0) L += mq * (log(mq) - log(mps));
+  if (mode == KD_FULL) L += Q * lse;
+
+  double alpha = 0.0;
+  if (mode == KD_TAIL) alpha = Q + mq - ratio;
+  if (mode == KD_FULL) alpha = Q;
+  for (int k = lane; k < K; k += 64) {
+    double r = 0.0;
+    if (k < nv) {
+      const double z = zS[t * K + k], tl = stlp[t * K + k];
+      const double q = exp(tl);
+      if (mode == KD_RENORM) {
+        r = exp(z - lseS) - exp(tl - lseq);
+      } else if (mode == KD_TAIL) {
+        r = -q + ratio * exp(z - lse);
+      } else if (mode == KD_FULL) {
+        r = -q;
+      } else {
+        const double lph = z - lseS, lqh = tl - lseq;
+        r = exp(lph) * (lph - lqh - L);
+      }
+    }
+    coef[t * K + k] = (float)(scale * r);
+  }
+  if (lane == 0) {
+    float* tw = tok + t * TOKF;
+    tw[TK_LSE] = (float)lse;
+    tw[TK_ALPHA] = (float)(scale * alpha);
+    tw[TK_L] = (float)L;
+    tw[TK_MP] = (float)mp;
+    if (loss_tok) loss_tok[t] = (float)L;
+    if (lse_out) lse_out[t] = (float)lse;
+    if (mp_out) mp_out[t] = (float)mp;
+  }
+}
+
+// loss = scale * sum_t L_t in a fixed order; NaN when the prep flagged bad indices.
+__global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const float* __restrict__ tok,
+                                                   const int32_t* __restrict__ err, float* __restrict__ loss) {
+  __shared__ double red[1024];
+  double s = 0.0;
+  for (int64_t t = threadIdx.x; t < T; t += 1024) s += (double)tok[t * TOKF + TK_L];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (*err) ? __builtin_nanf("") : (float)(scale * red[0]);
+}
+
+// ---------------------------------------------------------------------------
+// pass 2 (dense modes): recompute the z^T tile of one vocabulary chunk and
+// write dz = alpha * exp(z - lse) (+ r on S) as bf16 in both layouts:
+// dz [Tp][Cp] (token rows) and dzT [Cp][Tp] (vocabulary rows).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+                                                int64_t T, int64_t d, int64_t V, int K, int64_t Tp, int64_t Cp,
+                                                int64_t c0, int64_t c1, int nCT, int nTT,
+                                                const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
+                                                const float* __restrict__ tok, const float* __restrict__ coef,
+                                                bf16_t* __restrict__ dz, bf16_t* __restrict__ dzT) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int ct, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 2, ct, tt)) return;
+  const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
+  const int vt = (int)(m0 / VT);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TC::WN, wn = wave % TC::WN;
+
+  float lse_t[TC::FN], al_t[TC::FN];
+  int cur[TC::FN], nxt[TC::FN];
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
+    lse_t[fn] = 0.f;
+    al_t[fn] = 0.f;
+    cur[fn] = K;
+    nxt[fn] = SENT;
+    if (t < T) {
+      lse_t[fn] = tok[t * TOKF + TK_LSE];
+      al_t[fn] = tok[t * TOKF + TK_ALPHA];
+      cur[fn] = starts[(int64_t)vt * Tp + t];
+      nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
+    }
+  }
+
+  Acc<TC> acc;
+  gemm_tile<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
+
+  const int vw0 = (int)m0 + wm * TC::TM;
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int col = acc_col<TC>(wn, fn, lane);
+    const int64_t t = n0 + col;
+    const bool tok_ok = t < T;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = g * 4 + r;
+          const int64_t v = m0 + acc_row<TC>(wm, fm, e, lane);
+          x[r] = (tok_ok && v < c1) ? al_t[fn] * __expf(acc.v[fm][fn][e] - lse_t[fn]) : 0.f;
+          dzT[(v - c0) * Tp + t] = f32_to_bf16(x[r]);
+        }
+        const int64_t vl = m0 - c0 + acc_row<TC>(wm, fm, g * 4, lane);
+        uint2 pk;
+        pk.x = pack_bf16x2(x[0], x[1]);
+        pk.y = pack_bf16x2(x[2], x[3]);
+        *(uint2*)(dz + t * Cp + vl) = pk;
+      }
+    // sparse term on S: the owning lane rewrites its element
+    if (tok_ok) {
+      const int vw1 = vw0 + TC::TM;
+      while (nxt[fn] < vw1) {
+        const int v = nxt[fn];
+        if (v >= vw0 && v < c1) {
+          const int slot = acc_slot(v - vw0, lane);
+          if (slot >= 0) {
+            const float z = acc_pick(acc, fn, slot);
+            const float val = al_t[fn] * __expf(z - lse_t[fn]) + coef[t * K + cur[fn]];
+            const bf16_t b = f32_to_bf16(val);
+            dzT[(v - c0) * Tp + t] = b;
+            dz[t * Cp + (v - c0)] = b;
+          }
+        }
+        ++cur[fn];
+        nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Transpose with zero padding: out[c][r] = in[r][c] for r < R, 0 for
+// R <= r < Rp.  in is [R][C] (row pitch ldi), out is [C][Rp].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_transpose(const bf16_t* __restrict__ in, int64_t ldi, int64_t R, int64_t C,
+                                                   bf16_t* __restrict__ out, int64_t Rp) {
+  __shared__ bf16_t tile[64][66];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? in[r * ldi + c] : (bf16_t)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) out[c * Rp + r] = tile[tx][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dh / dW GEMMs of one chunk in a single launch.
+//   dh tiles: dh[t][j] (+)= sum_v dz[t][v] * WT[j][v]     (K = chunk rows)
+//   dW tiles: dW[c0+v][j] = sum_t dzT[v][t] * hT[j][t]    (K = Tp)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, const bf16_t* __restrict__ dzT,
+                                                 const bf16_t* __restrict__ WT, const bf16_t* __restrict__ hT,
+                                                 int64_t T, int64_t d, int64_t Tp, int64_t Cp, int64_t c0,
+                                                 int64_t clen, int kdh, int first_chunk, int nTT, int nDT, int nCT,
+                                                 int grid_dh, float* __restrict__ dh, float* __restrict__ dW) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TC::WN, wn = wave % TC::WN;
+  Acc<TC> acc;
+  if ((int)blockIdx.x < grid_dh) {
+    int ti, dj;
+    if (!tile_of(blockIdx.x, grid_dh, nTT, nDT, 4, ti, dj)) return;
+    const int64_t m0 = (int64_t)ti * TC::BM, n0 = (int64_t)dj * TC::BN;
+    gemm_tile<TC>(dz, Cp, m0, Tp, WT, Cp, n0, d, kdh, lds, acc);
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < TC::FN; ++fn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t t = m0 + acc_row<TC>(wm, fm, e, lane), j = n0 + acc_col<TC>(wn, fn, lane);
+          if (t < T && j < d) {
+            float* p = dh + t * d + j;
+            *p = first_chunk ? acc.v[fm][fn][e] : (*p + acc.v[fm][fn][e]);
+          }
+        }
+  } else {
+    int ci, dj;
+    if (!tile_of(blockIdx.x - grid_dh, gridDim.x - grid_dh, nCT, nDT, 4, ci, dj)) return;
+    const int64_t m0 = (int64_t)ci * TC::BM, n0 = (int64_t)dj * TC::BN;
+    gemm_tile<TC>(dzT, Tp, m0, clen, hT, Tp, n0, d, (int)Tp, lds, acc);
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < TC::FN; ++fn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t v = m0 + acc_row<TC>(wm, fm, e, lane), j = n0 + acc_col<TC>(wn, fn, lane);
+          if (v < clen && j < d) dW[(c0 + v) * d + j] = acc.v[fm][fn][e];
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sparse backward (RENORM, REVERSE): dz is zero off S.
+// ---------------------------------------------------------------------------
+// dh[t] = sum_k r_tk W[s_tk], k ascending.  One workgroup per token.
+__global__ __launch_bounds__(256) void k_sparse_dh(const bf16_t* __restrict__ W, int64_t d, int K,
+                                                   const int32_t* __restrict__ sidx, const float* __restrict__ coef,
+                                                   const float* __restrict__ tok, float* __restrict__ dh) {
+  const int64_t t = blockIdx.x;
+  const int nv = (int)tok[t * TOKF + TK_NV];
+  for (int64_t j0 = (int64_t)threadIdx.x * 8; j0 < d; j0 += 256 * 8) {
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < nv; ++k) {
+      const int v = sidx[t * K + k];
+      const float r = coef[t * K + k];
+      const u32x4 w = *(const u32x4*)(W + (int64_t)v * d + j0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[2 * i] = fmaf(r, __uint_as_float(w[i] << 16), a[2 * i]);
+        a[2 * i + 1] = fmaf(r, __uint_as_float(w[i] & 0xffff0000u), a[2 * i + 1]);
+      }
+    }
+    float4* o = (float4*)(dh + t * d + j0);
+    o[0] = make_float4(a[0], a[1], a[2], a[3]);
+    o[1] = make_float4(a[4], a[5], a[6], a[7]);
+  }
+}
+
+__global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// Count retained entries per vocabulary row (integer atomics: exact).
+__global__ void k_csr_count(int64_t T, int K, const int32_t* __restrict__ sidx, const float* __restrict__ tok,
+                            int32_t* __restrict__ cnt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * K) return;
+  const int64_t t = i / K;
+  const int k = (int)(i % K);
+  if (k < (int)tok[t * TOKF + TK_NV]) atomicAdd(&cnt[sidx[i]], 1);
+}
+
+// Exclusive scan of cnt[0..n) into off[0..n]; one workgroup.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ cnt, int64_t n, int32_t* __restrict__ off) {
+  __shared__ int32_t part[1024];
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t b = threadIdx.x * per, e = min(n, b + per);
+  int32_t s = 0;
+  for (int64_t i = b; i < e; ++i) s += cnt[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t x = ((int)threadIdx.x >= o) ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += x;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - s;
+  for (int64_t i = b; i < e; ++i) {
+    off[i] = run;
+    run += cnt[i];
+  }
+  if (threadIdx.x == 1023) off[n] = part[1023];
+}
+
+// Scatter entries (token, coefficient) into their vocabulary row's bucket.
+// The order inside a bucket is arbitrary; the consumer is order-independent.
+__global__ void k_csr_fill(int64_t T, int K, const int32_t* __restrict__ sidx, const float* __restrict__ coef,
+                           const float* __restrict__ tok, const int32_t* __restrict__ off, int32_t* __restrict__ fillc,
+                           int32_t* __restrict__ ent_t, float* __restrict__ ent_r) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * K) return;
+  const int64_t t = i / K;
+  const int k = (int)(i % K);
+  if (k >= (int)tok[t * TOKF + TK_NV]) return;
+  const int v = sidx[i];
+  const int pos = off[v] + atomicAdd(&fillc[v], 1);
+  ent_t[pos] = (int32_t)t;
+  ent_r[pos] = coef[i];
+}
+
+// dW[v][j] = sum over the bucket of r * h[t][j].  The products are exact in
+// fp64; they are summed as 64-bit fixed point with a per-column exponent
+// chosen from the largest product, so the result is independent of the
+// bucket order (deterministic) and exact to ~2^-60 of the column's scale.
+__global__ __launch_bounds__(256) void k_sparse_dw(const bf16_t* __restrict__ h, int64_t d,
+                                                   const int32_t* __restrict__ off, const int32_t* __restrict__ ent_t,
+                                                   const float* __restrict__ ent_r, float* __restrict__ dW) {
+  const int64_t v = blockIdx.x;
+  const int b = off[v], n = off[v + 1] - b;
+  for (int64_t j = threadIdx.x; j < d; j += 256) {
+    float out = 0.f;
+    if (n == 1) {
+      out = ent_r[b] * bf16_to_f32(h[(int64_t)ent_t[b] * d + j]);
+    } else if (n > 1) {
+      double amax = 0.0;
+      for (int i = 0; i < n; ++i) {
+        const double p = (double)ent_r[b + i] * (double)bf16_to_f32(h[(int64_t)ent_t[b + i] * d + j]);
+        amax = fmax(amax, fabs(p));
+      }
+      if (amax > 0.0) {
+        int ex;
+        frexp(amax * (double)n, &ex);  // amax*n < 2^ex
+        const int sh = 61 - ex;
+        long long acc = 0;
+        for (int i = 0; i < n; ++i) {
+          const double p = (double)ent_r[b + i] * (double)bf16_to_f32(h[(int64_t)ent_t[b + i] * d + j]);
+          acc += llrint(ldexp(p, sh));
+        }
+        out = (float)ldexp((double)acc, -sh);
+      }
+    }
+    dW[v * d + j] = out;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+struct LossPlan {
+  int64_t T, d, V, Tp, Cp, C;
+  int K, Kp2, mode, nVT, nTT, nDT, nchunks;
+  size_t o_sidx, o_stlp, o_zS, o_coef, o_tok, o_starts, o_part, o_err;
+  size_t o_hT, o_dz, o_dzT, o_WT;                    // dense modes
+  size_t o_cnt, o_off, o_fill, o_entt, o_entr;       // sparse modes
+  size_t total;
+};
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, LossPlan& p) {
+  if (T < 0 || d <= 0 || V <= 0 || K < 1 || K > KMAX || K > V || d % 64 != 0 || d > 16384 || chunk <= 0) return false;
+  if (mode < KD_RENORM || mode > KD_REVERSE) return false;
+  if (V > (int64_t)1 << 30 || T > (int64_t)1 << 26) return false;
+  p.T = T;
+  p.d = d;
+  p.V = V;
+  p.K = K;
+  p.mode = mode;
+  p.Kp2 = 1;
+  while (p.Kp2 < K) p.Kp2 <<= 1;
+  p.Tp = kd_round_up(T > 0 ? T : 1, TT);
+  p.C = kd_round_up(chunk, VT);
+  if (p.C > kd_round_up(V, VT)) p.C = kd_round_up(V, VT);
+  p.Cp = p.C;
+  p.nVT = (int)kd_ceil_div(V, VT);
+  p.nTT = (int)(p.Tp / TT);
+  p.nDT = (int)kd_ceil_div(d, TC::BN);
+  p.nchunks = (int)kd_ceil_div(V, p.C);
+  size_t o = 0;
+  const size_t TK = (size_t)(T > 0 ? T : 1) * K;
+  p.o_sidx = o; o = align_up(o + TK * 4);
+  p.o_stlp = o; o = align_up(o + TK * 4);
+  p.o_zS = o; o = align_up(o + TK * 4);
+  p.o_coef = o; o = align_up(o + TK * 4);
+  p.o_tok = o; o = align_up(o + (size_t)p.Tp * TOKF * 4);
+  p.o_starts = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
+  p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
+  p.o_err = o; o = align_up(o + 4);
+  p.o_hT = p.o_dz = p.o_dzT = p.o_WT = 0;
+  p.o_cnt = p.o_off = p.o_fill = p.o_entt = p.o_entr = 0;
+  if (mode == KD_TAIL || mode == KD_FULL) {
+    p.o_hT = o; o = align_up(o + (size_t)d * p.Tp * 2);
+    p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
+    p.o_dzT = o; o = align_up(o + (size_t)p.Cp * p.Tp * 2);
+    p.o_WT = o; o = align_up(o + (size_t)d * p.Cp * 2);
+  } else {
+    p.o_cnt = o; o = align_up(o + (size_t)(V + 1) * 4);
+    p.o_off = o; o = align_up(o + (size_t)(V + 1) * 4);
+    p.o_fill = o; o = align_up(o + (size_t)(V + 1) * 4);
+    p.o_entt = o; o = align_up(o + TK * 4);
+    p.o_entr = o; o = align_up(o + TK * 4);
+  }
+  p.total = o;
+  return true;
+}
+
+template <typename T>
+static T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+}  // namespace
+
+extern "C" size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk) {
+  LossPlan p;
+  if (!plan_loss(T, d, V, K, mode, chunk, p)) return 0;
+  return p.total;
+}
+
+#define KD_LAUNCH_CHECK()                                                              \
+  do {                                                                                 \
+    hipError_t e_ = hipGetLastError();                                                 \
+    if (e_ != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                          const float* teacher_logp, const float* m_q, int64_t T, int64_t d,
+                                          int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale,
+                                          float* loss, float* loss_tok, float* lse, float* m_p, float* dh,
+                                          float* dW, void* ws, size_t ws_bytes, void* stream) {
+  LossPlan p;
+  if (mode < KD_RENORM || mode > KD_REVERSE) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
+  if (!plan_loss(T, d, V, K, mode, chunk, p))
+    return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0)",
+                   (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
+  if (!loss || !dW || !W) return kd_fail(KD_EINVAL, "null required pointer (loss, W, dW)");
+  if (T > 0 && (!h || !idx || !teacher_logp || !dh)) return kd_fail(KD_EINVAL, "null required pointer (h, idx, teacher_logp, dh)");
+  if (T > 0 && mode == KD_TAIL && !m_q) return kd_fail(KD_EINVAL, "KD_TAIL needs m_q");
+  if (!ws || ws_bytes < p.total)
+    return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+
+  int32_t* err = at<int32_t>(ws, p.o_err);
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, s, err, (int64_t)1, 0);
+  KD_LAUNCH_CHECK();
+  if (T == 0) {
+    hipLaunchKernelGGL(k_fill_i32, dim3(1024), dim3(256), 0, s, (int32_t*)dW, V * d, 0);
+    hipLaunchKernelGGL(k_loss_sum, dim3(1), dim3(1024), 0, s, (int64_t)0, scale, at<float>(ws, p.o_tok), err, loss);
+    KD_LAUNCH_CHECK();
+    return KD_OK;
+  }
+  int32_t* sidx = at<int32_t>(ws, p.o_sidx);
+  float* stlp = at<float>(ws, p.o_stlp);
+  float* zS = at<float>(ws, p.o_zS);
+  float* coef = at<float>(ws, p.o_coef);
+  float* tok = at<float>(ws, p.o_tok);
+  int32_t* starts = at<int32_t>(ws, p.o_starts);
+  float2* part = at<float2>(ws, p.o_part);
+  const int lds = TC::LDS_BYTES;
+
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)T), dim3(64), 0, s, idx, teacher_logp, T, V, (int)K,
+                     p.Kp2, p.nVT, p.Tp, sidx, stlp, starts, tok, err);
+  KD_LAUNCH_CHECK();
+  // zero the gathered logits so padding slots read as finite values
+  hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
+  const int g1 = grid_of(p.nVT * p.nTT);
+  hipLaunchKernelGGL(k_pass1, dim3(g1), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
+                     p.nVT, p.nTT, p.Tp, sidx, starts, zS, part);
+  KD_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, (int)K, p.nVT, p.Tp, (int)mode,
+                     scale, part, zS, sidx, stlp, m_q, tok, coef, loss_tok, lse, m_p);
+  KD_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, tok, err, loss);
+  KD_LAUNCH_CHECK();
+
+  if (mode == KD_TAIL || mode == KD_FULL) {
+    bf16_t* hT = at<bf16_t>(ws, p.o_hT);
+    bf16_t* dz = at<bf16_t>(ws, p.o_dz);
+    bf16_t* dzT = at<bf16_t>(ws, p.o_dzT);
+    bf16_t* WT = at<bf16_t>(ws, p.o_WT);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)kd_ceil_div(p.Tp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256), 0,
+                       s, (const bf16_t*)h, d, T, d, hT, p.Tp);
+    KD_LAUNCH_CHECK();
+    for (int c = 0; c < p.nchunks; ++c) {
+      const int64_t c0 = (int64_t)c * p.C;
+      const int64_t c1 = (c0 + p.C < V) ? c0 + p.C : V;
+      const int64_t clen = c1 - c0;
+      const int nCT = (int)kd_ceil_div(clen, VT);
+      const int gz = grid_of(nCT * p.nTT);
+      hipLaunchKernelGGL(k_zdz, dim3(gz), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
+                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, coef, dz, dzT);
+      KD_LAUNCH_CHECK();
+      hipLaunchKernelGGL(k_transpose, dim3((unsigned)kd_ceil_div(p.Cp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256),
+                         0, s, (const bf16_t*)W + c0 * d, d, clen, d, WT, p.Cp);
+      KD_LAUNCH_CHECK();
+      const int kdh = (int)kd_round_up(clen, 64);
+      const int gdh = grid_of(p.nTT * p.nDT);
+      const int nCTw = (int)kd_ceil_div(clen, TC::BM);
+      const int gdw = grid_of(nCTw * p.nDT);
+      hipLaunchKernelGGL(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, dzT, WT, hT, T, d, p.Tp, p.Cp, c0, clen,
+                         kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, dh, dW);
+      KD_LAUNCH_CHECK();
+    }
+  } else {
+    int32_t* cnt = at<int32_t>(ws, p.o_cnt);
+    int32_t* off = at<int32_t>(ws, p.o_off);
+    int32_t* fillc = at<int32_t>(ws, p.o_fill);
+    int32_t* ent_t = at<int32_t>(ws, p.o_entt);
+    float* ent_r = at<float>(ws, p.o_entr);
+    hipLaunchKernelGGL(k_sparse_dh, dim3((unsigned)T), dim3(256), 0, s, (const bf16_t*)W, d, (int)K, sidx, coef, tok, dh);
+    KD_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_fill_i32, dim3(512), dim3(256), 0, s, cnt, V + 1, 0);
+    hipLaunchKernelGGL(k_fill_i32, dim3(512), dim3(256), 0, s, fillc, V + 1, 0);
+    const unsigned ge = (unsigned)kd_ceil_div(T * K, 256);
+    hipLaunchKernelGGL(k_csr_count, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, tok, cnt);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cnt, V, off);
+    hipLaunchKernelGGL(k_csr_fill, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, coef, tok, off, fillc, ent_t, ent_r);
+    hipLaunchKernelGGL(k_sparse_dw, dim3((unsigned)V), dim3(256), 0, s, (const bf16_t*)h, d, off, ent_t, ent_r, dW);
+    KD_LAUNCH_CHECK();
+  }
+  return KD_OK;
+}
