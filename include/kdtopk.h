@@ -149,6 +149,16 @@ kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K,
 /* Message describing the last non-KD_OK status returned on this thread. */
 const char* kd_last_error(void);
 
+/* Launch profiler (diagnostics).  After kd_profile_begin(), every kernel the
+ * library enqueues from this thread is bracketed by a pair of HIP events on
+ * its stream.  kd_profile_end() waits for those events, stops recording and
+ * reports, per distinct kernel name (at most max_kernels entries), the summed
+ * event time in milliseconds and the launch count; it returns the number of
+ * distinct kernels.  names[i] point to static strings.  Any pointer may be
+ * NULL.  Not for use inside HIP graph capture. */
+kd_status kd_profile_begin(void);
+int32_t kd_profile_end(int32_t max_kernels, const char** names, float* total_ms, int32_t* launches);
+
 /* Library version string. */
 const char* kd_version(void);
 

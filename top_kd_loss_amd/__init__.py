@@ -38,6 +38,8 @@ _SIGS = {
     "kd_topk_rows": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_last_error": (ctypes.c_char_p, []),
     "kd_version": (ctypes.c_char_p, []),
+    "kd_profile_begin": (ctypes.c_int, []),
+    "kd_profile_end": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_f32), ctypes.POINTER(_i32)]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -203,6 +205,21 @@ def topk_rows(z: torch.Tensor, K: int, rho: Sequence[float] = (),
                             _ptr(o.k_rho) if n else None, _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "kd_topk_rows")
     return o
+
+
+def profile_begin() -> None:
+    """Start bracketing every library kernel launch with HIP events."""
+    _check(lib().kd_profile_begin(), "kd_profile_begin")
+
+
+def profile_end() -> dict:
+    """Stop recording; {kernel name: (total ms, launches)} of the recorded launches."""
+    n = 64
+    names = (ctypes.c_char_p * n)()
+    ms = (ctypes.c_float * n)()
+    cnt = (ctypes.c_int32 * n)()
+    k = lib().kd_profile_end(n, names, ms, cnt)
+    return {names[i].decode(): (float(ms[i]), int(cnt[i])) for i in range(min(k, n))}
 
 
 def version() -> str:

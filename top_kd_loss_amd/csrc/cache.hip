@@ -393,7 +393,7 @@ static void launch_rows(const float* z, int64_t ldz, int64_t rows, int64_t V, in
                         int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho, hipStream_t s) {
   float r[RHO_MAX] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < n_rho; ++j) r[j] = rho[j];
-  hipLaunchKernelGGL(k_topk_rows, dim3((unsigned)rows), dim3(RT), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
+  KD_LAUNCH(k_topk_rows, dim3((unsigned)rows), dim3(RT), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
                      r[4], r[5], r[6], r[7], idx, val, lse, m_q, k_rho);
 }
 
@@ -425,7 +425,7 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
     const int64_t tb = (T - t0 < p.Tb) ? T - t0 : p.Tb;
     const int nTT = (int)kd_ceil_div(tb, CC::BM), nVT = (int)kd_ceil_div(V, CC::BN);
     const int grid = (int)kd_round_up((int64_t)nTT * nVT, 8);
-    hipLaunchKernelGGL(k_cache_gemm, dim3(grid), dim3(CC::NT), CC::LDS_BYTES, s, (const bf16_t*)g + t0 * d,
+    KD_LAUNCH(k_cache_gemm, dim3(grid), dim3(CC::NT), CC::LDS_BYTES, s, (const bf16_t*)g + t0 * d,
                        (const bf16_t*)U, b, tb, d, V, nTT, nVT, z);
     launch_rows(z, V, tb, V, K, rho_host, n_rho, idx + t0 * K, val + t0 * K, lse + t0, m_q + t0,
                 n_rho ? k_rho + t0 * n_rho : nullptr, s);

@@ -734,11 +734,11 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   hipStream_t s = (hipStream_t)stream;
 
   int32_t* err = at<int32_t>(ws, p.o_err);
-  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, s, err, (int64_t)1, 0);
+  KD_LAUNCH(k_fill_i32, dim3(1), dim3(64), 0, s, err, (int64_t)1, 0);
   KD_LAUNCH_CHECK();
   if (T == 0) {
-    hipLaunchKernelGGL(k_fill_i32, dim3(1024), dim3(256), 0, s, (int32_t*)dW, V * d, 0);
-    hipLaunchKernelGGL(k_loss_sum, dim3(1), dim3(1024), 0, s, (int64_t)0, scale, at<float>(ws, p.o_tok), err, loss);
+    KD_LAUNCH(k_fill_i32, dim3(1024), dim3(256), 0, s, (int32_t*)dW, V * d, 0);
+    KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, (int64_t)0, scale, at<float>(ws, p.o_tok), err, loss);
     KD_LAUNCH_CHECK();
     return KD_OK;
   }
@@ -751,19 +751,19 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   float2* part = at<float2>(ws, p.o_part);
   const int lds = TC::LDS_BYTES;
 
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)T), dim3(64), 0, s, idx, teacher_logp, T, V, (int)K,
+  KD_LAUNCH(k_prep, dim3((unsigned)T), dim3(64), 0, s, idx, teacher_logp, T, V, (int)K,
                      p.Kp2, p.nVT, p.Tp, sidx, stlp, starts, tok, err);
   KD_LAUNCH_CHECK();
   // zero the gathered logits so padding slots read as finite values
-  hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
+  KD_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
   const int g1 = grid_of(p.nVT * p.nTT);
-  hipLaunchKernelGGL(k_pass1, dim3(g1), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
+  KD_LAUNCH(k_pass1, dim3(g1), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
                      p.nVT, p.nTT, p.Tp, sidx, starts, zS, part);
   KD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, (int)K, p.nVT, p.Tp, (int)mode,
+  KD_LAUNCH(k_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, (int)K, p.nVT, p.Tp, (int)mode,
                      scale, part, zS, sidx, stlp, m_q, tok, coef, loss_tok, lse, m_p);
   KD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, tok, err, loss);
+  KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, tok, err, loss);
   KD_LAUNCH_CHECK();
 
   if (mode == KD_TAIL || mode == KD_FULL) {
@@ -771,7 +771,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
     bf16_t* dz = at<bf16_t>(ws, p.o_dz);
     bf16_t* dzT = at<bf16_t>(ws, p.o_dzT);
     bf16_t* WT = at<bf16_t>(ws, p.o_WT);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)kd_ceil_div(p.Tp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256), 0,
+    KD_LAUNCH(k_transpose, dim3((unsigned)kd_ceil_div(p.Tp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256), 0,
                        s, (const bf16_t*)h, d, T, d, hT, p.Tp);
     KD_LAUNCH_CHECK();
     for (int c = 0; c < p.nchunks; ++c) {
@@ -780,17 +780,17 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
       const int64_t clen = c1 - c0;
       const int nCT = (int)kd_ceil_div(clen, VT);
       const int gz = grid_of(nCT * p.nTT);
-      hipLaunchKernelGGL(k_zdz, dim3(gz), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
+      KD_LAUNCH(k_zdz, dim3(gz), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
                          p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, coef, dz, dzT);
       KD_LAUNCH_CHECK();
-      hipLaunchKernelGGL(k_transpose, dim3((unsigned)kd_ceil_div(p.Cp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256),
+      KD_LAUNCH(k_transpose, dim3((unsigned)kd_ceil_div(p.Cp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256),
                          0, s, (const bf16_t*)W + c0 * d, d, clen, d, WT, p.Cp);
       KD_LAUNCH_CHECK();
       const int kdh = (int)kd_round_up(clen, 64);
       const int gdh = grid_of(p.nTT * p.nDT);
       const int nCTw = (int)kd_ceil_div(clen, TC::BM);
       const int gdw = grid_of(nCTw * p.nDT);
-      hipLaunchKernelGGL(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, dzT, WT, hT, T, d, p.Tp, p.Cp, c0, clen,
+      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, dzT, WT, hT, T, d, p.Tp, p.Cp, c0, clen,
                          kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, dh, dW);
       KD_LAUNCH_CHECK();
     }
@@ -800,15 +800,15 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
     int32_t* fillc = at<int32_t>(ws, p.o_fill);
     int32_t* ent_t = at<int32_t>(ws, p.o_entt);
     float* ent_r = at<float>(ws, p.o_entr);
-    hipLaunchKernelGGL(k_sparse_dh, dim3((unsigned)T), dim3(256), 0, s, (const bf16_t*)W, d, (int)K, sidx, coef, tok, dh);
+    KD_LAUNCH(k_sparse_dh, dim3((unsigned)T), dim3(256), 0, s, (const bf16_t*)W, d, (int)K, sidx, coef, tok, dh);
     KD_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_fill_i32, dim3(512), dim3(256), 0, s, cnt, V + 1, 0);
-    hipLaunchKernelGGL(k_fill_i32, dim3(512), dim3(256), 0, s, fillc, V + 1, 0);
+    KD_LAUNCH(k_fill_i32, dim3(512), dim3(256), 0, s, cnt, V + 1, 0);
+    KD_LAUNCH(k_fill_i32, dim3(512), dim3(256), 0, s, fillc, V + 1, 0);
     const unsigned ge = (unsigned)kd_ceil_div(T * K, 256);
-    hipLaunchKernelGGL(k_csr_count, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, tok, cnt);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cnt, V, off);
-    hipLaunchKernelGGL(k_csr_fill, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, coef, tok, off, fillc, ent_t, ent_r);
-    hipLaunchKernelGGL(k_sparse_dw, dim3((unsigned)V), dim3(256), 0, s, (const bf16_t*)h, d, off, ent_t, ent_r, dW);
+    KD_LAUNCH(k_csr_count, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, tok, cnt);
+    KD_LAUNCH(k_scan, dim3(1), dim3(1024), 0, s, cnt, V, off);
+    KD_LAUNCH(k_csr_fill, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, coef, tok, off, fillc, ent_t, ent_r);
+    KD_LAUNCH(k_sparse_dw, dim3((unsigned)V), dim3(256), 0, s, (const bf16_t*)h, d, off, ent_t, ent_r, dW);
     KD_LAUNCH_CHECK();
   }
   return KD_OK;
