@@ -27,7 +27,7 @@
 
 namespace {
 
-using CC = TileCfg<256, 256, 64, 2, 2>;
+using CC = PipeCfg<256, 256, 2, 2>;
 constexpr int RT = 1024;      // threads of the row kernel
 constexpr int NB = 2048;      // radix bins per digit (11 bits)
 constexpr int CAP = 4096;     // candidate capacity (LDS)
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256, 1) void k_cache_gemm(const bf16_t* __restrict_
   if (!tile_of(blockIdx.x, gridDim.x, nTT, nVT, 4, tt, vt)) return;
   const int64_t m0 = (int64_t)tt * CC::BM, n0 = (int64_t)vt * CC::BN;
   Acc<CC> acc;
-  gemm_tile<CC>(g, d, m0, Tb, U, d, n0, V, (int)d, lds, acc);
+  gemm_tile_pipe<CC>(g, d, m0, Tb, U, d, n0, V, (int)d, lds, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / CC::WN, wn = wave % CC::WN;
 #pragma unroll

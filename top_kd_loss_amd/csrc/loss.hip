@@ -31,7 +31,7 @@
 
 namespace {
 
-using TC = TileCfg<256, 256, 64, 2, 2>;
+using TC = PipeCfg<256, 256, 2, 2>;
 constexpr int VT = TC::BM;        // vocabulary rows per tile (M of the z^T tile)
 constexpr int TT = TC::BN;        // tokens per tile
 constexpr int KMAX = 1024;
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, 
   }
 
   Acc<TC> acc;
-  gemm_tile<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
+  gemm_tile_pipe<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
 
   float* red = (float*)lds;  // [WM][TT][2] after the main loop
   const int vw0 = (int)m0 + wm * TC::TM;
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
   }
 
   Acc<TC> acc;
-  gemm_tile<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
+  gemm_tile_pipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
 
   const int vw0 = (int)m0 + wm * TC::TM;
 #pragma unroll
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
     int ti, dj;
     if (!tile_of(blockIdx.x, grid_dh, nTT, nDT, 4, ti, dj)) return;
     const int64_t m0 = (int64_t)ti * TC::BM, n0 = (int64_t)dj * TC::BN;
-    gemm_tile<TC>(dz, Cp, m0, Tp, WT, Cp, n0, d, kdh, lds, acc);
+    gemm_tile_pipe<TC>(dz, Cp, m0, Tp, WT, Cp, n0, d, kdh, lds, acc);
 #pragma unroll
     for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
     int ci, dj;
     if (!tile_of(blockIdx.x - grid_dh, gridDim.x - grid_dh, nCT, nDT, 4, ci, dj)) return;
     const int64_t m0 = (int64_t)ci * TC::BM, n0 = (int64_t)dj * TC::BN;
-    gemm_tile<TC>(dzT, Tp, m0, clen, hT, Tp, n0, d, (int)Tp, lds, acc);
+    gemm_tile_pipe<TC>(dzT, Tp, m0, clen, hT, Tp, n0, d, (int)Tp, lds, acc);
 #pragma unroll
     for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
