@@ -22,6 +22,7 @@ result does not depend on how many worker processes produced it.
 """
 from __future__ import annotations
 
+import multiprocessing
 import os
 from concurrent.futures import ProcessPoolExecutor
 
@@ -77,7 +78,8 @@ def _map_blocks(fn, jobs):
     nw = _workers(len(jobs))
     if nw == 1:
         return [fn(j) for j in jobs]
-    with ProcessPoolExecutor(max_workers=nw) as ex:
+    # spawned workers: they never inherit a parent's GPU runtime state
+    with ProcessPoolExecutor(max_workers=nw, mp_context=multiprocessing.get_context("spawn")) as ex:
         return list(ex.map(fn, jobs))
 
 
