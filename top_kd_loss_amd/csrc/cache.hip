@@ -8,16 +8,18 @@
 // >= rho} ("Sparse Teacher Support Cuts LLM Distillation Cost Without
 // Losing Accuracy").
 //
-// Row pass, one workgroup per row (HBM bound, the row is streamed a few
-// times and stays in the last-level cache between passes):
-//   A  row max and an 11-bit radix histogram of order-preserving keys
-//   B  sum of exp(z - max); per-bin fixed-point mass; candidates of the
-//      top-K (every key in bins above the K-th one plus that bin), refined
-//      by further radix digits only when that bin is too large
+// Row pass, one workgroup per row (HBM bound; the row is streamed two or
+// three times and stays in the last-level cache between passes):
+//   1  an 11-bit radix histogram of order-preserving keys with, per bin, the
+//      count and the sum of exp(z - upper edge of the bin) in 2^-31 fixed
+//      point (exact 64-bit integer sums: independent of atomic order);
+//      logsumexp follows from the bin masses
+//   2  candidates of the top-K (every key in bins above the K-th one plus
+//      that bin; extra digit passes only when that bin is too large), and the
+//      next 11-bit digit of the bins where the cumulative mass crosses rho
+//   3  the last 10-bit digit of those bins: the crossing key is exact
 //   sort the candidates by (key desc, index asc) in LDS: ties go to the
 //      lower index, -0.0 ties with +0.0
-//   C, D  two more radix digits of the mass histogram, only around the bin
-//      where the cumulative mass crosses rho, to get k_rho exactly
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -81,31 +83,48 @@ __device__ __forceinline__ uint32_t fkey(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int RHO_GROUP = 2;  // k_rho targets refined together in one pass
+
+constexpr int NCOPY = 4;       // level-0 histogram copies in pass 1 (by lane % 4): fewer same-address atomics
+
 struct RowShared {
-  unsigned long long cand[CAP];   // ((~key) << 32) | index, sorted ascending
-  int hist[NB];
-  unsigned long long mass[NB];
+  // Pass 1 uses `copies`; afterwards the same bytes hold the top-K candidates
+  // and the refinement histograms.
+  union {
+    struct {
+      int cnt[NCOPY][NB];
+      unsigned long long mass[NCOPY][NB];
+    } copies;
+    struct {
+      unsigned long long cand[CAP];             // ((~key) << 32) | index
+      int cntR[RHO_GROUP][NB];                  // refinement digits (top-K uses cntR[0])
+      unsigned long long massR[RHO_GROUP][NB];
+    } late;
+  } u;
+  float ref0[NB];                               // upper edge of each level-0 bin
+  int cnt0[NB];                                 // level-0 counts
+  unsigned long long mass0[NB];                 // level-0 fixed-point masses, each vs its bin's upper edge
   int scan_i[RT / 64];
-  float red_f[RT / 64];
   double red_d[RT / 64];
-  int ncand;
-  int sel_bin;
-  int sel_above;
-  int sel_eq;
-  unsigned long long rho_target, rho_cum;
-  int rho_cnt, rho_done, rho_bin;
-  uint32_t rho_pre;
+  int ncand, sel_bin, sel_above, sel_eq;
+  double scan_w[RT / 64];
+  int scan_wi[RT / 64];
+  int f_bin, f_cnt_above;
+  double f_above, f_total;
+  // k_rho state per target of the current group
+  double r_target[RHO_GROUP], r_cum[RHO_GROUP];
+  int r_cnt[RHO_GROUP], r_done[RHO_GROUP];
+  uint32_t r_pre[RHO_GROUP];
+  double lse;
 };
 
-__device__ __forceinline__ float block_max(float v, RowShared& S) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) S.red_f[w] = v;
-  __syncthreads();
-  float r = S.red_f[0];
-  for (int i = 1; i < RT / 64; ++i) r = fmaxf(r, S.red_f[i]);
-  __syncthreads();
-  return r;
+// Largest float whose key has prefix `p` in its top `bits` bits: the upper
+// edge of a histogram bin.  Clamped to FLT_MAX for bins above the finite range.
+__device__ __forceinline__ float bin_upper(uint32_t p, int bits) {
+  const uint32_t k = (bits == 32) ? p : ((p << (32 - bits)) | ((1u << (32 - bits)) - 1u));
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  const float f = __uint_as_float(u);
+  return (f != f || f > 3.4028234663852886e38f) ? 3.4028234663852886e38f : f;
 }
 
 __device__ __forceinline__ double block_sum_d(double v, RowShared& S) {
@@ -119,55 +138,157 @@ __device__ __forceinline__ double block_sum_d(double v, RowShared& S) {
   return r;
 }
 
-// From the histogram of a digit, find the bin holding the `need`-th largest
-// element (1-based, counting from the top): returns the bin, the count
-// strictly above it, and its own count.  Thread 0 scans; result in S.
-__device__ void find_kth_bin(RowShared& S, int need) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int cum = 0, b = NB - 1;
-    for (; b > 0; --b) {
-      if (cum + S.hist[b] >= need) break;
-      cum += S.hist[b];
+// Block-wide inclusive scan of (double, int) pairs in thread order; also
+// returns the exclusive values, taken as the previous thread's inclusive ones
+// so that consecutive threads agree exactly.
+__device__ __forceinline__ void block_scan2(double v, int c, RowShared& S, double& incl, double& excl, int& cincl,
+                                            int& cexcl) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double x = v;
+  int y = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double tx = __shfl_up(x, o, 64);
+    const int ty = __shfl_up(y, o, 64);
+    if (lane >= o) {
+      x += tx;
+      y += ty;
     }
-    S.sel_bin = b;
-    S.sel_above = cum;
-    S.sel_eq = S.hist[b];
+  }
+  if (lane == 63) {
+    S.scan_w[w] = x;
+    S.scan_wi[w] = y;
+  }
+  __syncthreads();
+  double off = 0.0;
+  int offi = 0;
+  for (int i = 0; i < w; ++i) {
+    off += S.scan_w[i];
+    offi += S.scan_wi[i];
+  }
+  __syncthreads();
+  const double px = __shfl_up(x, 1, 64);
+  const int py = __shfl_up(y, 1, 64);
+  incl = off + x;
+  cincl = offi + y;
+  excl = lane == 0 ? off : off + px;
+  cexcl = lane == 0 ? offi : offi + py;
+}
+
+// Walk bins nb-1 .. 0 (descending key) accumulating mass(b) and count(b);
+// find the bin where the running mass first reaches `target`.  Returns the
+// bin (-1 when the total stays below), the mass and the count strictly above
+// it.  Thread t owns the descending positions 2t and 2t+1 (nb <= 2 * RT).
+// With mass = count and an integer target this is the K-th element search.
+template <class FM, class FC>
+__device__ void find_from_top(RowShared& S, int nb, double target, FM&& mass, FC&& count, int* bin,
+                              double* above, int* cnt_above) {
+  const int t = threadIdx.x;
+  const int b0 = nb - 1 - 2 * t, b1 = b0 - 1;
+  const double v0 = b0 >= 0 ? mass(b0) : 0.0, v1 = b1 >= 0 ? mass(b1) : 0.0;
+  const int c0 = b0 >= 0 ? count(b0) : 0, c1 = b1 >= 0 ? count(b1) : 0;
+  double incl, excl;
+  int cincl, cexcl;
+  if (t == 0) S.f_bin = -1;
+  block_scan2(v0 + v1, c0 + c1, S, incl, excl, cincl, cexcl);
+  // a target beyond the level's total (rounding of per-bin references) is
+  // met at the last non-empty bin
+  if (t == RT - 1) S.f_total = incl;
+  __syncthreads();
+  const double tg = target < S.f_total ? target : S.f_total;
+  if (b0 >= 0 && excl < tg && incl >= tg) {
+    if (excl + v0 >= tg || b1 < 0) {
+      S.f_bin = b0;
+      S.f_above = excl;
+      S.f_cnt_above = cexcl;
+    } else {
+      S.f_bin = b1;
+      S.f_above = excl + v0;
+      S.f_cnt_above = cexcl + c0;
+    }
+  }
+  __syncthreads();
+  *bin = S.f_bin;
+  *above = S.f_above;
+  *cnt_above = S.f_cnt_above;
+  __syncthreads();
+}
+
+// Bin of a count histogram holding the need-th largest element (1-based):
+// the bin, the count strictly above it, its own count (in S.sel_*).
+__device__ void find_kth_bin(RowShared& S, const int* hist, int nbins, int need) {
+  __syncthreads();
+  int bin, ca;
+  double ma;
+  find_from_top(S, nbins, (double)need, [&](int b) { return (double)hist[b]; }, [&](int b) { return hist[b]; },
+                &bin, &ma, &ca);
+  if (bin < 0) {  // cannot happen for need <= total; keep the lowest bin
+    bin = 0;
+  }
+  if (threadIdx.x == 0) {
+    S.sel_bin = bin;
+    S.sel_above = (int)ma;
+    S.sel_eq = hist[bin];
   }
   __syncthreads();
 }
 
-__device__ void clear_hist(RowShared& S, bool with_mass) {
-  for (int i = threadIdx.x; i < NB; i += RT) {
-    S.hist[i] = 0;
-    if (with_mass) S.mass[i] = 0ull;
+// Sort S.u.late.cand[0..n) ascending, keeping at least the K smallest at the
+// front.  Candidates are distinct 64-bit keys, so each one's rank is the
+// number of smaller ones (broadcast LDS reads, no network of barriers); the
+// K smallest are written by rank to [CAP-K, CAP) (disjoint from [0, n) since
+// n <= 2*RT <= CAP-K) and moved to the front.  Larger n: bitonic network.
+__device__ void sort_cand(RowShared& S, int n, int K) {
+  constexpr int PER = 2;  // candidates ranked per thread
+  static_assert(RT * PER + KMAX <= CAP, "rank-sort staging must not overlap the candidates");
+  if (n <= RT * PER) {
+    unsigned long long mine[PER];
+    int rank[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = threadIdx.x + q * RT;
+      mine[q] = i < n ? S.u.late.cand[i] : ~0ull;
+      rank[q] = 0;
+    }
+    for (int j = 0; j < n; ++j) {
+      const unsigned long long c = S.u.late.cand[j];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) rank[q] += (c < mine[q]) ? 1 : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = threadIdx.x + q * RT;
+      if (i < n && rank[q] < K) S.u.late.cand[CAP - K + rank[q]] = mine[q];
+    }
+    __syncthreads();
+    unsigned long long v = 0ull;
+    if ((int)threadIdx.x < K) v = S.u.late.cand[CAP - K + threadIdx.x];  // K <= KMAX <= RT
+    __syncthreads();
+    if ((int)threadIdx.x < K) S.u.late.cand[threadIdx.x] = v;
+    __syncthreads();
+    return;
   }
-  __syncthreads();
-}
-
-// Bitonic sort of S.cand[0..n) ascending, padded to a power of two with ~0.
-__device__ void sort_cand(RowShared& S, int n) {
   int np = 1;
   while (np < n) np <<= 1;
-  for (int i = n + threadIdx.x; i < np; i += RT) S.cand[i] = ~0ull;
+  for (int i = n + threadIdx.x; i < np; i += RT) S.u.late.cand[i] = ~0ull;
   __syncthreads();
   for (int size = 2; size <= np; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = threadIdx.x; i < np / 2; i += RT) {
         const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
         const bool up = (lo & size) == 0;
-        const unsigned long long a = S.cand[lo], c = S.cand[hi];
+        const unsigned long long a = S.u.late.cand[lo], c = S.u.late.cand[hi];
         if ((a > c) == up) {
-          S.cand[lo] = c;
-          S.cand[hi] = a;
+          S.u.late.cand[lo] = c;
+          S.u.late.cand[hi] = a;
         }
       }
       __syncthreads();
     }
 }
 
-// Block-wide exclusive prefix count of `flag` in thread order; returns this
-// thread's rank and writes the total to *total.
+// Block-wide exclusive prefix count of `flag` in thread order.
 __device__ int block_rank(bool flag, RowShared& S, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const unsigned long long bal = __ballot(flag);
@@ -184,6 +305,74 @@ __device__ int block_rank(bool flag, RowShared& S, int* total) {
   return off + before;
 }
 
+// Visit every element of the row: f(index, value).  16-byte loads when the
+// row is 16-byte aligned and V is a multiple of 4; each thread keeps ROW_U
+// loads in flight before it processes them.
+constexpr int ROW_U = 4;
+template <class F>
+__device__ __forceinline__ void row_loop(const float* zr, int64_t V, bool vec, F&& f) {
+  if (vec) {
+    const float4* z4 = (const float4*)zr;
+    const int64_t n4 = V >> 2;
+    for (int64_t base = threadIdx.x; base < n4; base += (int64_t)RT * ROW_U) {
+      float4 v[ROW_U];
+#pragma unroll
+      for (int u = 0; u < ROW_U; ++u) {
+        const int64_t i = base + (int64_t)u * RT;
+        v[u] = i < n4 ? z4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < ROW_U; ++u) {
+        const int64_t i = base + (int64_t)u * RT;
+        if (i < n4) {
+          f(4 * i, v[u].x);
+          f(4 * i + 1, v[u].y);
+          f(4 * i + 2, v[u].z);
+          f(4 * i + 3, v[u].w);
+        }
+      }
+    }
+  } else {
+    for (int64_t base = threadIdx.x; base < V; base += (int64_t)RT * ROW_U) {
+      float v[ROW_U];
+#pragma unroll
+      for (int u = 0; u < ROW_U; ++u) {
+        const int64_t i = base + (int64_t)u * RT;
+        v[u] = i < V ? zr[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < ROW_U; ++u) {
+        const int64_t i = base + (int64_t)u * RT;
+        if (i < V) f(i, v[u]);
+      }
+    }
+  }
+}
+
+// Per-thread run merging of histogram updates: consecutive elements of one
+// thread that fall into the same bin are added once.
+struct HistRun {
+  int bin = -1, cnt = 0;
+  unsigned long long mass = 0;
+  __device__ __forceinline__ void add(int b, unsigned long long m, int* cnt_h, unsigned long long* mass_h) {
+    if (b != bin) {
+      flush(cnt_h, mass_h);
+      bin = b;
+    }
+    ++cnt;
+    mass += m;
+  }
+  __device__ __forceinline__ void flush(int* cnt_h, unsigned long long* mass_h) {
+    if (bin >= 0) {
+      atomicAdd(&cnt_h[bin], cnt);
+      if (mass_h) atomicAdd(&mass_h[bin], mass);
+    }
+    bin = -1;
+    cnt = 0;
+    mass = 0;
+  }
+};
+
 __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
                                                   int n_rho, float rho0, float rho1, float rho2, float rho3,
                                                   float rho4, float rho5, float rho6, float rho7,
@@ -194,59 +383,195 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, i
   const int64_t row = blockIdx.x;
   const float* zr = z + row * ldz;
   const int tid = threadIdx.x;
+  const bool vec = ((V & 3) == 0) && ((((uintptr_t)zr) & 15) == 0);
+  // fixed point: a mass term exp(z - edge) <= 1 is stored as round(term * 2^31)
+  // (32 bits); sums over a bin are exact 64-bit integers for V < 2^32
+  const float fxs = 2147483648.0f;
+  const double fxs_inv = 1.0 / 2147483648.0;
 
-  // ---- pass A: max and the first-digit histogram
-  clear_hist(S, true);
-  float mx = -KD_INF;
-  for (int64_t i = tid; i < V; i += RT) {
-    const float x = zr[i];
-    mx = fmaxf(mx, x);
-    atomicAdd(&S.hist[fkey(x) >> 21], 1);
+  for (int i = tid; i < NB * NCOPY; i += RT) {
+    (&S.u.copies.cnt[0][0])[i] = 0;
+    (&S.u.copies.mass[0][0])[i] = 0ull;
   }
-  const float M = block_max(mx, S);
-  find_kth_bin(S, K);
+  for (int i = tid; i < NB; i += RT) S.ref0[i] = bin_upper((uint32_t)i, 11);
+  __syncthreads();
 
-  // ---- candidate selection, refining the digit while the bin is too big
-  uint32_t pre = (uint32_t)S.sel_bin;  // key prefix of the K-th element
-  int pbits = 11;                      // bits of the key fixed by `pre`
-  int above = S.sel_above;             // elements with key prefix > pre
+  // ---- pass 1: counts and masses of the first 11-bit digit; masses are
+  // exp(z - upper edge of the element's bin), so no row maximum is needed.
+  {
+    const int cp = tid & (NCOPY - 1);
+    HistRun run;
+    row_loop(zr, V, vec, [&](int64_t, float x) {
+      const int b = (int)(fkey(x) >> 21);
+      const float ex = __expf(x - S.ref0[b]);
+      run.add(b, (unsigned long long)(uint32_t)fmaf(ex, fxs, 0.5f), S.u.copies.cnt[cp], S.u.copies.mass[cp]);
+    });
+    run.flush(S.u.copies.cnt[cp], S.u.copies.mass[cp]);
+  }
+  __syncthreads();
+  for (int i = tid; i < NB; i += RT) {
+    int c = 0;
+    unsigned long long m = 0ull;
+#pragma unroll
+    for (int k = 0; k < NCOPY; ++k) {
+      c += S.u.copies.cnt[k][i];
+      m += S.u.copies.mass[k][i];
+    }
+    S.cnt0[i] = c;
+    S.mass0[i] = m;
+  }
+  __syncthreads();
+  // logsumexp from the bin masses (fixed reduction order: deterministic)
+  {
+    float top = -KD_INF;
+    for (int bb = tid; bb < NB; bb += RT)
+      if (S.mass0[bb] > 0) top = fmaxf(top, S.ref0[bb]);
+    top = wave_max(top);
+    if ((tid & 63) == 0) S.scan_w[tid >> 6] = (double)top;
+    __syncthreads();
+    double tmax = S.scan_w[0];
+    for (int i = 1; i < RT / 64; ++i) tmax = fmax(tmax, S.scan_w[i]);
+    __syncthreads();
+    double acc = 0.0;
+    for (int bb = tid; bb < NB; bb += RT)
+      if (S.mass0[bb] > 0) acc += (double)S.mass0[bb] * fxs_inv * exp((double)S.ref0[bb] - tmax);
+    acc = block_sum_d(acc, S);
+    if (tid == 0) S.lse = tmax + log(acc);
+  }
+  find_kth_bin(S, S.cnt0, NB, K);
+  const double lse = S.lse;
+
+  // ---- top-K: refine the digit while the K-th element's bin is too big
+  uint32_t pre = (uint32_t)S.sel_bin;
+  int pbits = 11;
+  int above = S.sel_above;
   int eq = S.sel_eq;
   while (above + eq > CAP && pbits < 32) {
     const int dbits = (pbits == 11) ? 11 : 10;
     const int sh = 32 - pbits - dbits;
-    clear_hist(S, false);
-    for (int64_t i = tid; i < V; i += RT) {
-      const uint32_t k = fkey(zr[i]);
-      if ((k >> (32 - pbits)) == pre) atomicAdd(&S.hist[(k >> sh) & ((1u << dbits) - 1u)], 1);
-    }
-    find_kth_bin(S, K - above);
+    for (int i = tid; i < NB; i += RT) S.u.late.cntR[0][i] = 0;
+    __syncthreads();
+    HistRun run;
+    row_loop(zr, V, vec, [&](int64_t, float x) {
+      const uint32_t k = fkey(x);
+      if ((k >> (32 - pbits)) == pre) run.add((int)((k >> sh) & ((1u << dbits) - 1u)), 0ull, S.u.late.cntR[0], nullptr);
+    });
+    run.flush(S.u.late.cntR[0], nullptr);
+    find_kth_bin(S, S.u.late.cntR[0], 1 << dbits, K - above);
     pre = (pre << dbits) | (uint32_t)S.sel_bin;
     pbits += dbits;
     above += S.sel_above;
     eq = S.sel_eq;
   }
+  const bool exact_tail = (above + eq > CAP);  // all 32 key bits tie
 
-  // ---- pass B: exp-sum and candidate collection
-  if (tid == 0) S.ncand = 0;
-  const int vbits = 64 - __clzll((unsigned long long)V);  // V < 2^vbits
-  const double fx_scale = ldexp(1.0, 62 - vbits);          // exp(x - M) <= 1 per element
-  __syncthreads();
-  float se = 0.f;
-  const bool exact_tail = (above + eq > CAP);  // only when all 32 key bits tie
-  for (int64_t i = tid; i < V; i += RT) {
-    const float x = zr[i];
-    const float ex = __expf(x - M);
-    se += ex;
-    const uint32_t k = fkey(x);
-    const uint32_t kp = k >> (32 - pbits);
-    if (kp > pre || (!exact_tail && kp == pre)) {
-      const int slot = atomicAdd(&S.ncand, 1);
-      S.cand[slot] = ((unsigned long long)(~k) << 32) | (unsigned long long)i;
-    }
+  // ---- k_rho: crossing bins of the first digit, from the top
+  const float rhos[RHO_MAX] = {rho0, rho1, rho2, rho3, rho4, rho5, rho6, rho7};
+  auto mass0_of = [&](int b) {
+    return S.mass0[b] > 0 ? (double)S.mass0[b] * fxs_inv * exp((double)S.ref0[b] - lse) : 0.0;
+  };
+  double total = 0.0;
+  if (n_rho > 0) {
+    double part = 0.0;
+    for (int bb = tid; bb < NB; bb += RT) part += mass0_of(bb);
+    total = block_sum_d(part, S);
   }
-  const double sum_e = block_sum_d((double)se, S);
-  const double lse = (double)M + log(sum_e);
-  __syncthreads();
+
+  for (int g0 = 0; g0 < (n_rho > 0 ? n_rho : 1); g0 += RHO_GROUP) {
+    const int ng = (n_rho - g0) < RHO_GROUP ? (n_rho - g0) : RHO_GROUP;
+    for (int j = 0; j < ng; ++j) {
+      const double target = (double)rhos[g0 + j] * total;
+      int bin, ca;
+      double ma;
+      find_from_top(S, NB, target, mass0_of, [&](int b) { return S.cnt0[b]; }, &bin, &ma, &ca);
+      if (tid == 0) {
+        S.r_target[j] = target;
+        S.r_cum[j] = ma;
+        S.r_cnt[j] = bin < 0 ? (int)V : ca;
+        S.r_done[j] = bin < 0 ? 1 : 0;
+        S.r_pre[j] = (uint32_t)(bin < 0 ? 0 : bin);
+      }
+      __syncthreads();
+    }
+    // refinement levels: 11 more bits, then the last 10
+    for (int pb = 11; pb < 32;) {
+      const int dbits = (pb == 11) ? 11 : 10;
+      const int sh = 32 - pb - dbits;
+      for (int i = tid; i < NB; i += RT)
+        for (int j = 0; j < RHO_GROUP; ++j) {
+          S.u.late.cntR[j][i] = 0;
+          S.u.late.massR[j][i] = 0ull;
+        }
+      if (tid == 0 && g0 == 0 && pb == 11) S.ncand = 0;
+      __syncthreads();
+      uint32_t pj[RHO_GROUP];
+      bool act[RHO_GROUP];
+      for (int j = 0; j < RHO_GROUP; ++j) {
+        act[j] = j < ng && !S.r_done[j];
+        pj[j] = S.r_pre[j];
+      }
+      const bool collect = (g0 == 0 && pb == 11);  // top-K candidates ride on the first refinement pass
+      HistRun run[RHO_GROUP];
+      row_loop(zr, V, vec, [&](int64_t i, float x) {
+        const uint32_t k = fkey(x);
+        if (collect) {
+          const uint32_t kp = k >> (32 - pbits);
+          if (kp > pre || (!exact_tail && kp == pre)) {
+            const int slot = atomicAdd(&S.ncand, 1);
+            S.u.late.cand[slot] = ((unsigned long long)(~k) << 32) | (unsigned long long)i;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < RHO_GROUP; ++j) {
+          if (act[j] && (k >> (32 - pb)) == pj[j]) {
+            const int dg = (int)((k >> sh) & ((1u << dbits) - 1u));
+            const float ex = __expf(x - bin_upper((pj[j] << dbits) | (uint32_t)dg, pb + dbits));
+            run[j].add(dg, (unsigned long long)(uint32_t)fmaf(ex, fxs, 0.5f), S.u.late.cntR[j], S.u.late.massR[j]);
+          }
+        }
+      });
+      for (int j = 0; j < RHO_GROUP; ++j) run[j].flush(S.u.late.cntR[j], S.u.late.massR[j]);
+      __syncthreads();
+      for (int j = 0; j < ng; ++j) {
+        if (S.r_done[j]) continue;  // uniform: written by thread 0 before a barrier
+        const uint32_t p = S.r_pre[j];
+        auto massj = [&](int b) {
+          return S.u.late.massR[j][b] > 0 ? (double)S.u.late.massR[j][b] * fxs_inv *
+                                         exp((double)bin_upper((p << dbits) | (uint32_t)b, pb + dbits) - lse) : 0.0;
+        };
+        int bin, ca;
+        double ma;
+        find_from_top(S, 1 << dbits, S.r_target[j] - S.r_cum[j], massj, [&](int b) { return S.u.late.cntR[j][b]; }, &bin,
+                      &ma, &ca);
+        if (bin < 0) bin = 0;  // rounding: the crossing is in this bin's lowest digit
+        if (tid == 0) {
+          const double cum = S.r_cum[j] + ma;
+          const int cnt = S.r_cnt[j] + ca;
+          if (pb + dbits == 32) {
+            // all elements of the final bin share one key, hence one mass
+            const int nbin = S.u.late.cntR[j][bin];
+            const double each = exp((double)bin_upper((p << dbits) | (uint32_t)bin, 32) - lse);
+            long long jn = each > 0.0 ? (long long)ceil((S.r_target[j] - cum) / each) : (long long)nbin;
+            if (jn < 1) jn = 1;
+            if (jn > nbin) jn = nbin;
+            S.r_cnt[j] = cnt + (int)jn;
+            S.r_done[j] = 1;
+          } else {
+            S.r_cum[j] = cum;
+            S.r_cnt[j] = cnt;
+            S.r_pre[j] = (p << dbits) | (uint32_t)bin;
+          }
+        }
+        __syncthreads();
+      }
+      pb += dbits;
+      if (n_rho == 0) break;  // the pass only collected the top-K candidates
+    }
+    if (tid == 0)
+      for (int j = 0; j < ng; ++j) krho_out[row * n_rho + g0 + j] = S.r_cnt[j];
+    __syncthreads();
+  }
+
   int nc = S.ncand;
   if (exact_tail) {
     // all remaining ties share one key: take the lowest indices, in order
@@ -256,19 +581,18 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, i
       const bool f = (i < V) && (fkey(zr[i]) == pre);
       int tot;
       const int r = block_rank(f, S, &tot);
-      if (f && r < need) S.cand[nc + r] = ((unsigned long long)(~pre) << 32) | (unsigned long long)i;
+      if (f && r < need) S.u.late.cand[nc + r] = ((unsigned long long)(~pre) << 32) | (unsigned long long)i;
       const int took = tot < need ? tot : need;
       nc += took;
       need -= took;
       __syncthreads();
     }
   }
-  sort_cand(S, nc);
+  sort_cand(S, nc, K);
 
-  // ---- outputs of the top-K
   double kept = 0.0;
   for (int k = tid; k < K; k += RT) {
-    const int64_t i = (int64_t)(S.cand[k] & 0xffffffffull);
+    const int64_t i = (int64_t)(S.u.late.cand[k] & 0xffffffffull);
     const float x = zr[i];
     idx_out[row * K + k] = (int32_t)i;
     val_out[row * K + k] = x;
@@ -278,88 +602,6 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, i
   if (tid == 0) {
     lse_out[row] = (float)lse;
     mq_out[row] = (float)(1.0 - kept);
-  }
-  if (n_rho == 0) return;
-
-  // ---- k_rho: cumulative mass from the top, refined digit by digit around
-  // the crossing.  Masses are fixed point (exact integer sums), so the
-  // result does not depend on the order of the atomics.
-  const float rhos[RHO_MAX] = {rho0, rho1, rho2, rho3, rho4, rho5, rho6, rho7};
-  for (int j = 0; j < n_rho; ++j) {
-    clear_hist(S, true);
-    for (int64_t i = tid; i < V; i += RT) {
-      const float x = zr[i];
-      const uint32_t k = fkey(x);
-      atomicAdd(&S.hist[k >> 21], 1);
-      atomicAdd(&S.mass[k >> 21], (unsigned long long)llrint((double)__expf(x - M) * fx_scale));
-    }
-    __syncthreads();
-    if (tid == 0) {
-      unsigned long long tot = 0;
-      for (int bb = 0; bb < NB; ++bb) tot += S.mass[bb];
-      unsigned long long target = (unsigned long long)ceil((double)rhos[j] * (double)tot);
-      if (target == 0) target = 1;
-      unsigned long long cum = 0;
-      int cnt = 0, bb = NB - 1;
-      for (; bb >= 0; --bb) {
-        if (cum + S.mass[bb] >= target) break;
-        cum += S.mass[bb];
-        cnt += S.hist[bb];
-      }
-      S.rho_target = target;
-      S.rho_cum = cum;
-      S.rho_cnt = bb < 0 ? (int)V : cnt;
-      S.rho_done = bb < 0 ? 1 : 0;  // rounding kept the total below rho
-      S.rho_pre = (uint32_t)(bb < 0 ? 0 : bb);
-      S.rho_bin = bb < 0 ? 0 : bb;
-    }
-    __syncthreads();
-    for (int pb = 11; pb < 32 && !S.rho_done;) {
-      const int dbits = (pb == 11) ? 11 : 10;
-      const int sh = 32 - pb - dbits;
-      const uint32_t pfx = S.rho_pre;
-      clear_hist(S, true);
-      for (int64_t i = tid; i < V; i += RT) {
-        const float x = zr[i];
-        const uint32_t k = fkey(x);
-        if ((k >> (32 - pb)) == pfx) {
-          const int dg = (int)((k >> sh) & ((1u << dbits) - 1u));
-          atomicAdd(&S.hist[dg], 1);
-          atomicAdd(&S.mass[dg], (unsigned long long)llrint((double)__expf(x - M) * fx_scale));
-        }
-      }
-      __syncthreads();
-      if (tid == 0) {
-        unsigned long long cum = S.rho_cum;
-        int cnt = S.rho_cnt, bb = (1 << dbits) - 1;
-        for (; bb > 0; --bb) {
-          if (cum + S.mass[bb] >= S.rho_target) break;
-          cum += S.mass[bb];
-          cnt += S.hist[bb];
-        }
-        S.rho_cum = cum;
-        S.rho_cnt = cnt;
-        S.rho_pre = (pfx << dbits) | (uint32_t)bb;
-        S.rho_bin = bb;
-      }
-      __syncthreads();
-      pb += dbits;
-    }
-    if (tid == 0) {
-      int cnt = S.rho_cnt;
-      if (!S.rho_done) {
-        // every element of the final bin has one key, hence one mass
-        const int nb = S.hist[S.rho_bin];
-        const unsigned long long each = nb > 0 ? S.mass[S.rho_bin] / (unsigned long long)nb : 0ull;
-        const unsigned long long gap = S.rho_target - S.rho_cum;
-        long long jn = each > 0 ? (long long)((gap + each - 1) / each) : (long long)nb;
-        if (jn < 1) jn = 1;
-        if (jn > nb) jn = nb;
-        cnt += (int)jn;
-      }
-      krho_out[row * n_rho + j] = cnt;
-    }
-    __syncthreads();
   }
 }
 
