@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the RENORM line and the cache-build line")
     ap.add_argument("--memscan", action="store_true", help="peak memory vs T at d=2560, K=64 (4K..32K)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 4 device copies of 1 GiB (fp32) for HBM counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); multi-GPU runs are not part of this build",
@@ -162,6 +164,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of fp32 read and 1 GiB written per copy
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "copies": 4}), flush=True)
+        return
     T, d, V, K, chunk = CFG["T"], CFG["d"], CFG["V"], CFG["K"], CFG["chunk"]
     mode = kd.MODE_BY_NAME[args.mode]
     t0 = time.time()

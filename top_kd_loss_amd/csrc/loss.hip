@@ -472,9 +472,12 @@ __global__ __launch_bounds__(256) void k_transpose(const bf16_t* __restrict__ in
 }
 
 // ---------------------------------------------------------------------------
-// dh / dW GEMMs of one chunk in a single launch.
-//   dh tiles: dh[t][j] (+)= sum_v dz[t][v] * WT[j][v]     (K = chunk rows)
-//   dW tiles: dW[c0+v][j] = sum_t dzT[v][t] * hT[j][t]    (K = Tp)
+// dh / dW GEMMs of one chunk in a single launch.  Both are computed as
+// transposed tiles (rows = feature j, columns = token t or vocabulary row v)
+// so that each lane's accumulator group e = 4g..4g+3 holds four consecutive
+// features of one output row: the epilogue moves float4s.
+//   dh tiles: dh[t][j] (+)= sum_v WT[j][v] * dz[t][v]     (K = chunk rows)
+//   dW tiles: dW[c0+v][j] = sum_t hT[j][t] * dzT[v][t]    (K = Tp)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, const bf16_t* __restrict__ dzT,
                                                  const bf16_t* __restrict__ WT, const bf16_t* __restrict__ hT,
@@ -486,36 +489,50 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   Acc<TC> acc;
   if ((int)blockIdx.x < grid_dh) {
-    int ti, dj;
-    if (!tile_of(blockIdx.x, grid_dh, nTT, nDT, 4, ti, dj)) return;
-    const int64_t m0 = (int64_t)ti * TC::BM, n0 = (int64_t)dj * TC::BN;
-    gemm_tile_pipe<TC>(dz, Cp, m0, Tp, WT, Cp, n0, d, kdh, lds, acc);
+    int dj, ti;
+    if (!tile_of(blockIdx.x, grid_dh, nDT, nTT, 4, dj, ti)) return;
+    const int64_t m0 = (int64_t)dj * TC::BM, n0 = (int64_t)ti * TC::BN;
+    gemm_tile_pipe<TC>(WT, Cp, m0, d, dz, Cp, n0, Tp, kdh, lds, acc);
 #pragma unroll
-    for (int fm = 0; fm < TC::FM; ++fm)
+    for (int fn = 0; fn < TC::FN; ++fn) {
+      const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
+      f32x4 x[TC::FM][4];
 #pragma unroll
-      for (int fn = 0; fn < TC::FN; ++fn)
+      for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t t = m0 + acc_row<TC>(wm, fm, e, lane), j = n0 + acc_col<TC>(wn, fn, lane);
-          if (t < T && j < d) {
-            float* p = dh + t * d + j;
-            *p = first_chunk ? acc.v[fm][fn][e] : (*p + acc.v[fm][fn][e]);
-          }
+        for (int g = 0; g < 4; ++g) {
+          const int64_t j = m0 + acc_row<TC>(wm, fm, 4 * g, lane);
+          x[fm][g] = f32x4{acc.v[fm][fn][4 * g], acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2],
+                           acc.v[fm][fn][4 * g + 3]};
+          if (!first_chunk && t < T && j < d) x[fm][g] += *(const f32x4*)(dh + t * d + j);
         }
+#pragma unroll
+      for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t j = m0 + acc_row<TC>(wm, fm, 4 * g, lane);
+          if (t < T && j < d) *(f32x4*)(dh + t * d + j) = x[fm][g];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   } else {
-    int ci, dj;
-    if (!tile_of(blockIdx.x - grid_dh, gridDim.x - grid_dh, nCT, nDT, 4, ci, dj)) return;
-    const int64_t m0 = (int64_t)ci * TC::BM, n0 = (int64_t)dj * TC::BN;
-    gemm_tile_pipe<TC>(dzT, Tp, m0, clen, hT, Tp, n0, d, (int)Tp, lds, acc);
+    int dj, ci;
+    if (!tile_of(blockIdx.x - grid_dh, gridDim.x - grid_dh, nDT, nCT, 4, dj, ci)) return;
+    const int64_t m0 = (int64_t)dj * TC::BM, n0 = (int64_t)ci * TC::BN;
+    gemm_tile_pipe<TC>(hT, Tp, m0, d, dzT, Tp, n0, clen, (int)Tp, lds, acc);
 #pragma unroll
-    for (int fm = 0; fm < TC::FM; ++fm)
+    for (int fn = 0; fn < TC::FN; ++fn) {
+      const int64_t v = n0 + acc_col<TC>(wn, fn, lane);
 #pragma unroll
-      for (int fn = 0; fn < TC::FN; ++fn)
+      for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t v = m0 + acc_row<TC>(wm, fm, e, lane), j = n0 + acc_col<TC>(wn, fn, lane);
-          if (v < clen && j < d) dW[(c0 + v) * d + j] = acc.v[fm][fn][e];
+        for (int g = 0; g < 4; ++g) {
+          const int64_t j = m0 + acc_row<TC>(wm, fm, 4 * g, lane);
+          if (v < clen && j < d)
+            *(f32x4*)(dW + (c0 + v) * d + j) = f32x4{acc.v[fm][fn][4 * g], acc.v[fm][fn][4 * g + 1],
+                                                     acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]};
         }
+    }
   }
 }
 
@@ -788,7 +805,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
       KD_LAUNCH_CHECK();
       const int kdh = (int)kd_round_up(clen, 64);
       const int gdh = grid_of(p.nTT * p.nDT);
-      const int nCTw = (int)kd_ceil_div(clen, TC::BM);
+      const int nCTw = (int)kd_ceil_div(clen, TC::BN);
       const int gdw = grid_of(nCTw * p.nDT);
       KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, dzT, WT, hT, T, d, p.Tp, p.Cp, c0, clen,
                          kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, dh, dW);
