@@ -24,9 +24,14 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
+
+#define KD_LOG2E 1.4426950408889634f
 
 // D = A(32x16) * B(16x32) + C on the matrix cores, bf16 in, fp32 accumulate.
 // Lane l holds A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; the

@@ -62,25 +62,6 @@ __device__ __forceinline__ bool tile_of(int bid, int nblocks, int nM, int nN, in
 
 static inline int grid_of(int tiles) { return (int)kd_round_up(tiles, 8); }
 
-// Select accumulator element `sel` (0 .. FM*16-1) of token column fn.
-__device__ __forceinline__ float acc_pick(const Acc<TC>& acc, int fn, int sel) {
-  float v = 0.f;
-#pragma unroll
-  for (int fm = 0; fm < TC::FM; ++fm)
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (fm * 16 + e == sel) v = acc.v[fm][fn][e];
-  return v;
-}
-
-// Does this lane hold vocabulary row offset `off` (0 .. TM-1 within its
-// wavefront's rows)?  If so, returns the accumulator element index.
-__device__ __forceinline__ int acc_slot(int off, int lane) {
-  const int fm = off >> 5, w = off & 31;
-  if (((w >> 2) & 1) != (lane >> 5)) return -1;
-  return fm * 16 + (w >> 3) * 4 + (w & 3);
-}
-
 // ---------------------------------------------------------------------------
 // prep: one 64-lane workgroup per token.  Sort (idx, tlp) ascending by idx
 // with a bitonic network in LDS; padding slots (idx < 0) and indices >= V
@@ -167,7 +148,46 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
 
 // ---------------------------------------------------------------------------
 // pass 1: z^T tile (vocab x tokens) with the logsumexp / gather epilogue.
+// Per token column: (max, sum exp(z - max)) over the tile's vocabulary rows,
+// in-lane over the 64 accumulators plus one xor-32 exchange, merged across
+// the WM wavefront rows in LDS.  z at retained indices is gathered from an
+// fp32 copy of the tile staged in LDS, 128 vocabulary rows at a time, by
+// one thread per token walking its sorted index list.
 // ---------------------------------------------------------------------------
+constexpr int P1_RED = TC::WM * TT * 2 * 4;           // (max, sum) per wavefront row and token
+constexpr int P1_Z = TT * TC::TM * 4;                 // fp32 z of 128 vocabulary rows x TT tokens
+constexpr int P1_LDS = P1_RED + P1_Z;
+
+// Row reductions of one wavefront's accumulators; MASK drops tile rows >= vlim.
+template <bool MASK>
+__device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, float* red, int vlim, int wm, int wn, int lane) {
+  const int rbase = wm * TC::TM + 4 * (lane >> 5);
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    float mx = -KD_INF;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!MASK || rbase + fm * 32 + 8 * (e >> 2) + (e & 3) < vlim) mx = fmaxf(mx, acc.v[fm][fn][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float nm = (mx == -KD_INF) ? 0.f : -mx * KD_LOG2E;
+    float s = 0.f;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!MASK || rbase + fm * 32 + 8 * (e >> 2) + (e & 3) < vlim)
+          s += __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][e], KD_LOG2E, nm));
+    s += __shfl_xor(s, 32, 64);
+    const int col = acc_col<TC>(wn, fn, lane);
+    if (lane < 32) {
+      red[(wm * TT + col) * 2 + 0] = mx;
+      red[(wm * TT + col) * 2 + 1] = s;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                   int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
                                                   int64_t Tp, const int32_t* __restrict__ sidx,
@@ -179,65 +199,58 @@ __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, 
   const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
+  const int tid = threadIdx.x;
 
-  int cur[TC::FN], nxt[TC::FN];
-#pragma unroll
-  for (int fn = 0; fn < TC::FN; ++fn) {
-    const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
-    cur[fn] = K;
-    nxt[fn] = SENT;
-    if (t < T) {
-      cur[fn] = starts[(int64_t)vt * Tp + t];
-      nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
-    }
+  // thread tid owns token n0 + tid for the gather: first retained index >= m0
+  const int64_t ts = n0 + tid;
+  int kcur = K, vnext = SENT;
+  if (ts < T) {
+    kcur = starts[(int64_t)vt * Tp + ts];
+    vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
   }
 
   Acc<TC> acc;
   gemm_tile_pipe<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
+  __syncthreads();  // every wavefront is done with the operand stages
 
-  float* red = (float*)lds;  // [WM][TT][2] after the main loop
-  const int vw0 = (int)m0 + wm * TC::TM;
+  float* red = (float*)lds;
+  char* Z = (char*)lds + P1_RED;
+  const int vlim = (int)((V - m0) < VT ? (V - m0) : VT);
+  if (vlim == VT) pass1_reduce<false>(acc, red, VT, wm, wn, lane);
+  else pass1_reduce<true>(acc, red, vlim, wm, wn, lane);
+
+  // gather, one half of the tile's vocabulary rows at a time
+  const int rb = 4 * (lane >> 5);
 #pragma unroll
-  for (int fn = 0; fn < TC::FN; ++fn) {
-    float mx = -KD_INF;
+  for (int half = 0; half < TC::WM; ++half) {
+    if (wm == half) {
 #pragma unroll
-    for (int fm = 0; fm < TC::FM; ++fm)
+      for (int fn = 0; fn < TC::FN; ++fn) {
+        const int tl = acc_col<TC>(wn, fn, lane);
+        char* row = Z + tl * (TC::TM * 4);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = (int)m0 + acc_row<TC>(wm, fm, e, lane);
-        if (v < V) mx = fmaxf(mx, acc.v[fm][fn][e]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float s = 0.f;
+        for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-    for (int fm = 0; fm < TC::FM; ++fm)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = (int)m0 + acc_row<TC>(wm, fm, e, lane);
-        if (v < V) s += __expf(acc.v[fm][fn][e] - mx);
-      }
-    s += __shfl_xor(s, 32, 64);
-    const int col = acc_col<TC>(wn, fn, lane);
-    if (lane < 32) {
-      red[(wm * TT + col) * 2 + 0] = mx;
-      red[(wm * TT + col) * 2 + 1] = s;
-    }
-    // gather z at retained indices inside this wavefront's rows
-    const int64_t t = n0 + col;
-    if (t < T) {
-      const int vw1 = vw0 + TC::TM;
-      while (nxt[fn] < vw1) {
-        const int v = nxt[fn];
-        if (v >= vw0) {
-          const int slot = acc_slot(v - vw0, lane);
-          if (slot >= 0) zS[t * K + cur[fn]] = acc_pick(acc, fn, slot);
-        }
-        ++cur[fn];
-        nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
+          for (int g = 0; g < 4; ++g) {
+            const int vr = fm * 32 + 8 * g + rb;  // multiple of 4
+            *(f32x4*)(row + (((vr >> 2) ^ (tl & 31)) << 4)) =
+                f32x4{acc.v[fm][fn][4 * g], acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]};
+          }
       }
     }
+    __syncthreads();
+    const int vh1 = (int)m0 + (half + 1) * TC::TM;
+    if (vnext < vh1) {
+      const char* row = Z + tid * (TC::TM * 4);
+      while (vnext < vh1) {
+        const int vr = vnext - (int)m0 - half * TC::TM;
+        zS[ts * K + kcur] = *(const float*)(row + (((vr >> 2) ^ (tid & 31)) << 4) + (vr & 3) * 4);
+        ++kcur;
+        vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // merge the WM wavefront rows of the tile and write one partial per token
   for (int col = threadIdx.x; col < TT; col += TC::NT) {
     float m = -KD_INF, s = 0.f;
@@ -370,13 +383,63 @@ __global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const
 // pass 2 (dense modes): recompute the z^T tile of one vocabulary chunk and
 // write dz = alpha * exp(z - lse) (+ r on S) as bf16 in both layouts:
 // dz [Tp][Cp] (token rows) and dzT [Cp][Tp] (vocabulary rows).
+//
+// The bf16 tile is staged in LDS as E[t][v] (512-byte token rows, 16-byte
+// chunks XOR-swizzled by zdz_swz(t)) and leaves in 16-byte stores: token
+// rows straight from E, vocabulary rows through transposing LDS reads
+// (ds_read_b64_tr_b16: within each 16-lane group, lane j names 4 elements
+// of row t0 + j/4 at columns vb + 4*(j%4); lane i receives column vb + i of
+// rows t0 .. t0+3).
 // ---------------------------------------------------------------------------
+constexpr int ZDZ_LDS = VT * TT * 2;  // 128 KB bf16 tile
+
+// Bijection on 0..31: 32 consecutive rows hit 32 distinct chunk positions
+// (conflict-free stores), 4 consecutive rows fall into different aligned
+// groups of 8 chunks (transposing reads).
+__device__ __forceinline__ int zdz_swz(int t) { return ((t & 3) << 3) | ((t >> 2) & 7); }
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// Dense part of dz for one tile into E: alpha * exp(z - lse) as bf16, zero
+// for padding tokens and (MASK) for tile rows at or past vlim.
+template <bool MASK>
+__device__ __forceinline__ void zdz_dense(const Acc<TC>& acc, char* E, int64_t n0, int64_t T,
+                                          const float (&lse_t)[TC::FN], const float (&al_t)[TC::FN], int vlim,
+                                          int wm, int wn, int lane) {
+  const int rbase = wm * TC::TM + 4 * (lane >> 5);
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int tl = acc_col<TC>(wn, fn, lane);  // token row of E
+    const float nl = (n0 + tl < T) ? -lse_t[fn] * KD_LOG2E : -KD_INF;
+    const float a = al_t[fn];
+    char* row = E + tl * (VT * 2);
+    const int sw = zdz_swz(tl);
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = a * __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][g * 4 + r], KD_LOG2E, nl));
+          if (MASK && rbase + fm * 32 + 8 * g + r >= vlim) x[r] = 0.f;
+        }
+        const int vl = rbase + fm * 32 + 8 * g;  // multiple of 4
+        uint2 pk;
+        pk.x = pack_bf16x2(x[0], x[1]);
+        pk.y = pack_bf16x2(x[2], x[3]);
+        *(uint2*)(row + (((vl >> 3) ^ sw) << 4) + (vl & 7) * 2) = pk;
+      }
+  }
+}
 __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                 int64_t T, int64_t d, int64_t V, int K, int64_t Tp, int64_t Cp,
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
                                                 const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
-                                                const float* __restrict__ tok, const float* __restrict__ coef,
-                                                bf16_t* __restrict__ dz, bf16_t* __restrict__ dzT) {
+                                                const float* __restrict__ tok, const float* __restrict__ zS,
+                                                const float* __restrict__ coef, bf16_t* __restrict__ dz,
+                                                bf16_t* __restrict__ dzT) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 2, ct, tt)) return;
@@ -386,68 +449,82 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
   const int wm = wave / TC::WN, wn = wave % TC::WN;
 
   float lse_t[TC::FN], al_t[TC::FN];
-  int cur[TC::FN], nxt[TC::FN];
 #pragma unroll
   for (int fn = 0; fn < TC::FN; ++fn) {
     const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
     lse_t[fn] = 0.f;
     al_t[fn] = 0.f;
-    cur[fn] = K;
-    nxt[fn] = SENT;
     if (t < T) {
       lse_t[fn] = tok[t * TOKF + TK_LSE];
       al_t[fn] = tok[t * TOKF + TK_ALPHA];
-      cur[fn] = starts[(int64_t)vt * Tp + t];
-      nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
     }
+  }
+  // thread tid owns token row n0 + tid of the tile for the sparse term
+  const int tid = threadIdx.x;
+  const int64_t ts = n0 + tid;
+  const int64_t vend = (m0 + VT < c1) ? m0 + VT : c1;
+  int kcur = K, vnext = SENT;
+  if (ts < T) {
+    kcur = starts[(int64_t)vt * Tp + ts];
+    vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
   }
 
   Acc<TC> acc;
   gemm_tile_pipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
+  __syncthreads();  // every wavefront is done with the operand stages
 
-  const int vw0 = (int)m0 + wm * TC::TM;
-#pragma unroll
-  for (int fn = 0; fn < TC::FN; ++fn) {
-    const int col = acc_col<TC>(wn, fn, lane);
-    const int64_t t = n0 + col;
-    const bool tok_ok = t < T;
-#pragma unroll
-    for (int fm = 0; fm < TC::FM; ++fm)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = g * 4 + r;
-          const int64_t v = m0 + acc_row<TC>(wm, fm, e, lane);
-          x[r] = (tok_ok && v < c1) ? al_t[fn] * __expf(acc.v[fm][fn][e] - lse_t[fn]) : 0.f;
-          dzT[(v - c0) * Tp + t] = f32_to_bf16(x[r]);
-        }
-        const int64_t vl = m0 - c0 + acc_row<TC>(wm, fm, g * 4, lane);
-        uint2 pk;
-        pk.x = pack_bf16x2(x[0], x[1]);
-        pk.y = pack_bf16x2(x[2], x[3]);
-        *(uint2*)(dz + t * Cp + vl) = pk;
-      }
-    // sparse term on S: the owning lane rewrites its element
-    if (tok_ok) {
-      const int vw1 = vw0 + TC::TM;
-      while (nxt[fn] < vw1) {
-        const int v = nxt[fn];
-        if (v >= vw0 && v < c1) {
-          const int slot = acc_slot(v - vw0, lane);
-          if (slot >= 0) {
-            const float z = acc_pick(acc, fn, slot);
-            const float val = al_t[fn] * __expf(z - lse_t[fn]) + coef[t * K + cur[fn]];
-            const bf16_t b = f32_to_bf16(val);
-            dzT[(v - c0) * Tp + t] = b;
-            dz[t * Cp + (v - c0)] = b;
-          }
-        }
-        ++cur[fn];
-        nxt[fn] = cur[fn] < K ? sidx[t * K + cur[fn]] : SENT;
-      }
+  char* E = (char*)lds;
+  const int vlim = (int)((c1 - m0) < VT ? (c1 - m0) : VT);  // tile rows inside the chunk
+  if (vlim == VT) zdz_dense<false>(acc, E, n0, T, lse_t, al_t, VT, wm, wn, lane);
+  else zdz_dense<true>(acc, E, n0, T, lse_t, al_t, vlim, wm, wn, lane);
+  __syncthreads();
+  // sparse term on S: dz = alpha * exp(z - lse) + r with z gathered in pass 1
+  if (vnext < vend) {
+    const float al = tok[ts * TOKF + TK_ALPHA], ls = tok[ts * TOKF + TK_LSE];
+    char* row = E + tid * (VT * 2);
+    const int sw = zdz_swz(tid);
+    while (vnext < vend) {
+      const int vl = vnext - (int)m0;
+      const float val = al * __expf(zS[ts * K + kcur] - ls) + coef[ts * K + kcur];
+      *(bf16_t*)(row + (((vl >> 3) ^ sw) << 4) + (vl & 7) * 2) = f32_to_bf16(val);
+      ++kcur;
+      vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
     }
+  }
+  __syncthreads();
+
+  // token rows: 32 threads per 512-byte row
+  const int64_t vo = m0 - c0;
+#pragma unroll 4
+  for (int it = 0; it < TT / 8; ++it) {
+    const int tl = it * 8 + (tid >> 5), c = tid & 31;
+    const u32x4 q = *(const u32x4*)(E + tl * (VT * 2) + ((c ^ zdz_swz(tl)) << 4));
+    *(u32x4*)(dz + (n0 + tl) * Cp + vo + c * 8) = q;
+  }
+  // vocabulary rows: per step a wavefront covers 16 vocabulary rows x 32
+  // tokens; its four 16-lane groups take consecutive 8-token pieces, so each
+  // store instruction writes 64 contiguous bytes of 16 rows
+  const int gi = lane >> 4, li = lane & 15;
+  const int rsel = li >> 2, csel = li & 3;
+#pragma unroll 2
+  for (int it = 0; it < (VT / 16) * (TT / 32) / 4; ++it) {
+    const int job = it * 4 + wave;                // 0 .. (VT/16)*(TT/32)-1
+    const int vb = (job / (TT / 32)) * 16;
+    const int t0 = (job % (TT / 32)) * 32 + gi * 8;
+    const int va = vb + 4 * csel;                 // this lane's source columns va .. va+3
+    bf16x4_t lo, hi;
+    {
+      const int tr = t0 + rsel;
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4_t*)(E + tr * (VT * 2) + (((va >> 3) ^ zdz_swz(tr)) << 4) + (va & 7) * 2));
+    }
+    {
+      const int tr = t0 + 4 + rsel;
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4_t*)(E + tr * (VT * 2) + (((va >> 3) ^ zdz_swz(tr)) << 4) + (va & 7) * 2));
+    }
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    *(u32x4*)(dzT + (vo + vb + li) * Tp + n0 + t0) = u32x4{a.x, a.y, b.x, b.y};
   }
 }
 
@@ -774,7 +851,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   // zero the gathered logits so padding slots read as finite values
   KD_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
   const int g1 = grid_of(p.nVT * p.nTT);
-  KD_LAUNCH(k_pass1, dim3(g1), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
+  KD_LAUNCH(k_pass1, dim3(g1), dim3(TC::NT), P1_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
                      p.nVT, p.nTT, p.Tp, sidx, starts, zS, part);
   KD_LAUNCH_CHECK();
   KD_LAUNCH(k_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, (int)K, p.nVT, p.Tp, (int)mode,
@@ -797,8 +874,8 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
       const int64_t clen = c1 - c0;
       const int nCT = (int)kd_ceil_div(clen, VT);
       const int gz = grid_of(nCT * p.nTT);
-      KD_LAUNCH(k_zdz, dim3(gz), dim3(TC::NT), lds, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
-                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, coef, dz, dzT);
+      KD_LAUNCH(k_zdz, dim3(gz), dim3(TC::NT), ZDZ_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
+                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, dz, dzT);
       KD_LAUNCH_CHECK();
       KD_LAUNCH(k_transpose, dim3((unsigned)kd_ceil_div(p.Cp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256),
                          0, s, (const bf16_t*)W + c0 * d, d, clen, d, WT, p.Cp);
