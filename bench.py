@@ -40,24 +40,35 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_hash() -> str:
+# Source files each kernel family is built from (a change elsewhere leaves
+# its recorded HBM traffic valid).
+KERNEL_SOURCES = {
+    "loss": ["loss.hip", "gemm.h", "kd_common.h", "kd_internal.h"],
+    "cache": ["cache.hip", "gemm.h", "kd_common.h", "kd_internal.h"],
+}
+
+
+def kernel_family(kernel: str) -> str:
+    return "cache" if kernel in ("k_cache_gemm", "k_topk_rows") else "loss"
+
+
+def kernel_sources_hash(family: str = "loss") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "top_kd_loss_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES[family]:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
+    it was taken on the current sources of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path)).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("sources") != kernel_sources_hash():
+    if not rec or rec.get("sources") != kernel_sources_hash(kernel_family(kernel)):
         return None
     return rec.get("bytes_per_launch")
 

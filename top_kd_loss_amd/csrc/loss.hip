@@ -158,27 +158,36 @@ constexpr int P1_RED = TC::WM * TT * 2 * 4;           // (max, sum) per wavefron
 constexpr int P1_Z = TT * TC::TM * 4;                 // fp32 z of 128 vocabulary rows x TT tokens
 constexpr int P1_LDS = P1_RED + P1_Z;
 
-// Row reductions of one wavefront's accumulators; MASK drops tile rows >= vlim.
-template <bool MASK>
-__device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, float* red, int vlim, int wm, int wn, int lane) {
+// Tile rows at or past vlim (the vocabulary's end) are set to -inf in the
+// accumulators, so the epilogues below need no per-element row test: they
+// drop out of maxima and exp() of them is 0.
+__device__ __forceinline__ void mask_rows(Acc<TC>& acc, int vlim, int wm, int lane) {
   const int rbase = wm * TC::TM + 4 * (lane >> 5);
+#pragma unroll
+  for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < TC::FN; ++fn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (rbase + fm * 32 + 8 * (e >> 2) + (e & 3) >= vlim) acc.v[fm][fn][e] = -KD_INF;
+}
+
+// Row reductions of one wavefront's accumulators per token column.
+__device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, float* red, int wm, int wn, int lane) {
 #pragma unroll
   for (int fn = 0; fn < TC::FN; ++fn) {
     float mx = -KD_INF;
 #pragma unroll
     for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (!MASK || rbase + fm * 32 + 8 * (e >> 2) + (e & 3) < vlim) mx = fmaxf(mx, acc.v[fm][fn][e]);
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc.v[fm][fn][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float nm = (mx == -KD_INF) ? 0.f : -mx * KD_LOG2E;
     float s = 0.f;
 #pragma unroll
     for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (!MASK || rbase + fm * 32 + 8 * (e >> 2) + (e & 3) < vlim)
-          s += __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][e], KD_LOG2E, nm));
+      for (int e = 0; e < 16; ++e) s += __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][e], KD_LOG2E, nm));
     s += __shfl_xor(s, 32, 64);
     const int col = acc_col<TC>(wn, fn, lane);
     if (lane < 32) {
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, 
                                                   float2* __restrict__ part) {
   extern __shared__ __align__(16) bf16_t lds[];
   int vt, tt;
-  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 2, vt, tt)) return;
+  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 8, vt, tt)) return;
   const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
@@ -216,8 +225,8 @@ __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, 
   float* red = (float*)lds;
   char* Z = (char*)lds + P1_RED;
   const int vlim = (int)((V - m0) < VT ? (V - m0) : VT);
-  if (vlim == VT) pass1_reduce<false>(acc, red, VT, wm, wn, lane);
-  else pass1_reduce<true>(acc, red, vlim, wm, wn, lane);
+  if (vlim < VT) mask_rows(acc, vlim, wm, lane);
+  pass1_reduce(acc, red, wm, wn, lane);
 
   // gather, one half of the tile's vocabulary rows at a time
   const int rb = 4 * (lane >> 5);
@@ -402,11 +411,10 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 // Dense part of dz for one tile into E: alpha * exp(z - lse) as bf16, zero
-// for padding tokens and (MASK) for tile rows at or past vlim.
-template <bool MASK>
+// for padding tokens (nl = -inf) and for rows masked to -inf.
 __device__ __forceinline__ void zdz_dense(const Acc<TC>& acc, char* E, int64_t n0, int64_t T,
-                                          const float (&lse_t)[TC::FN], const float (&al_t)[TC::FN], int vlim,
-                                          int wm, int wn, int lane) {
+                                          const float (&lse_t)[TC::FN], const float (&al_t)[TC::FN], int wm, int wn,
+                                          int lane) {
   const int rbase = wm * TC::TM + 4 * (lane >> 5);
 #pragma unroll
   for (int fn = 0; fn < TC::FN; ++fn) {
@@ -421,10 +429,7 @@ __device__ __forceinline__ void zdz_dense(const Acc<TC>& acc, char* E, int64_t n
       for (int g = 0; g < 4; ++g) {
         float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = a * __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][g * 4 + r], KD_LOG2E, nl));
-          if (MASK && rbase + fm * 32 + 8 * g + r >= vlim) x[r] = 0.f;
-        }
+        for (int r = 0; r < 4; ++r) x[r] = a * __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][g * 4 + r], KD_LOG2E, nl));
         const int vl = rbase + fm * 32 + 8 * g;  // multiple of 4
         uint2 pk;
         pk.x = pack_bf16x2(x[0], x[1]);
@@ -433,6 +438,7 @@ __device__ __forceinline__ void zdz_dense(const Acc<TC>& acc, char* E, int64_t n
       }
   }
 }
+
 __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                 int64_t T, int64_t d, int64_t V, int K, int64_t Tp, int64_t Cp,
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
                                                 bf16_t* __restrict__ dzT) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
-  if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 2, ct, tt)) return;
+  if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
   const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
   const int vt = (int)(m0 / VT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -475,8 +481,8 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
 
   char* E = (char*)lds;
   const int vlim = (int)((c1 - m0) < VT ? (c1 - m0) : VT);  // tile rows inside the chunk
-  if (vlim == VT) zdz_dense<false>(acc, E, n0, T, lse_t, al_t, VT, wm, wn, lane);
-  else zdz_dense<true>(acc, E, n0, T, lse_t, al_t, vlim, wm, wn, lane);
+  if (vlim < VT) mask_rows(acc, vlim, wm, lane);
+  zdz_dense(acc, E, n0, T, lse_t, al_t, wm, wn, lane);
   __syncthreads();
   // sparse term on S: dz = alpha * exp(z - lse) + r with z gathered in pass 1
   if (vnext < vend) {
