@@ -559,11 +559,12 @@ __global__ __launch_bounds__(256) void k_transpose(const bf16_t* __restrict__ in
 // transposed tiles (rows = feature j, columns = token t or vocabulary row v)
 // so that each lane's accumulator group e = 4g..4g+3 holds four consecutive
 // features of one output row: the epilogue moves float4s.
-//   dh tiles: dh[t][j] (+)= sum_v WT[j][v] * dz[t][v]     (K = chunk rows)
+//   dh tiles: dh[t][j] (+)= sum_v W[c0+v][j] * dz[t][v]   (K = chunk rows;
+//             W is read as an MN-major operand straight from its rows)
 //   dW tiles: dW[c0+v][j] = sum_t hT[j][t] * dzT[v][t]    (K = Tp)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, const bf16_t* __restrict__ dzT,
-                                                 const bf16_t* __restrict__ WT, const bf16_t* __restrict__ hT,
+                                                 const bf16_t* __restrict__ W, const bf16_t* __restrict__ hT,
                                                  int64_t T, int64_t d, int64_t Tp, int64_t Cp, int64_t c0,
                                                  int64_t clen, int kdh, int first_chunk, int nTT, int nDT, int nCT,
                                                  int grid_dh, float* __restrict__ dh, float* __restrict__ dW) {
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
     int dj, ti;
     if (!tile_of(blockIdx.x, grid_dh, nDT, nTT, 4, dj, ti)) return;
     const int64_t m0 = (int64_t)dj * TC::BM, n0 = (int64_t)ti * TC::BN;
-    gemm_tile_pipe<TC>(WT, Cp, m0, d, dz, Cp, n0, Tp, kdh, lds, acc);
+    gemm_tile_pipe<TC, true, false>(W + c0 * d, d, m0, d, dz, Cp, n0, Tp, kdh, lds, acc, (int)clen);
 #pragma unroll
     for (int fn = 0; fn < TC::FN; ++fn) {
       const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
@@ -745,7 +746,7 @@ struct LossPlan {
   int64_t T, d, V, Tp, Cp, C;
   int K, Kp2, mode, nVT, nTT, nDT, nchunks;
   size_t o_sidx, o_stlp, o_zS, o_coef, o_tok, o_starts, o_part, o_err;
-  size_t o_hT, o_dz, o_dzT, o_WT;                    // dense modes
+  size_t o_hT, o_dz, o_dzT;                          // dense modes
   size_t o_cnt, o_off, o_fill, o_entt, o_entr;       // sparse modes
   size_t total;
 };
@@ -767,6 +768,8 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.C = kd_round_up(chunk, VT);
   if (p.C > kd_round_up(V, VT)) p.C = kd_round_up(V, VT);
   p.Cp = p.C;
+  // 32-bit byte offsets inside one chunk of W (MN-major operand of the dh GEMM)
+  if ((uint64_t)p.C * (uint64_t)d * 2u >= ((uint64_t)1 << 32)) return false;
   p.nVT = (int)kd_ceil_div(V, VT);
   p.nTT = (int)(p.Tp / TT);
   p.nDT = (int)kd_ceil_div(d, TC::BN);
@@ -781,13 +784,12 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.o_starts = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
   p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_err = o; o = align_up(o + 4);
-  p.o_hT = p.o_dz = p.o_dzT = p.o_WT = 0;
+  p.o_hT = p.o_dz = p.o_dzT = 0;
   p.o_cnt = p.o_off = p.o_fill = p.o_entt = p.o_entr = 0;
   if (mode == KD_TAIL || mode == KD_FULL) {
     p.o_hT = o; o = align_up(o + (size_t)d * p.Tp * 2);
     p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
     p.o_dzT = o; o = align_up(o + (size_t)p.Cp * p.Tp * 2);
-    p.o_WT = o; o = align_up(o + (size_t)d * p.Cp * 2);
   } else {
     p.o_cnt = o; o = align_up(o + (size_t)(V + 1) * 4);
     p.o_off = o; o = align_up(o + (size_t)(V + 1) * 4);
@@ -824,7 +826,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   LossPlan p;
   if (mode < KD_RENORM || mode > KD_REVERSE) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
   if (!plan_loss(T, d, V, K, mode, chunk, p))
-    return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0)",
+    return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0, chunk*d*2 < 4 GiB)",
                    (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
   if (!loss || !dW || !W) return kd_fail(KD_EINVAL, "null required pointer (loss, W, dW)");
   if (T > 0 && (!h || !idx || !teacher_logp || !dh)) return kd_fail(KD_EINVAL, "null required pointer (h, idx, teacher_logp, dh)");
@@ -870,7 +872,6 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
     bf16_t* hT = at<bf16_t>(ws, p.o_hT);
     bf16_t* dz = at<bf16_t>(ws, p.o_dz);
     bf16_t* dzT = at<bf16_t>(ws, p.o_dzT);
-    bf16_t* WT = at<bf16_t>(ws, p.o_WT);
     KD_LAUNCH(k_transpose, dim3((unsigned)kd_ceil_div(p.Tp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256), 0,
                        s, (const bf16_t*)h, d, T, d, hT, p.Tp);
     KD_LAUNCH_CHECK();
@@ -883,14 +884,11 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
       KD_LAUNCH(k_zdz, dim3(gz), dim3(TC::NT), ZDZ_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
                          p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, dz, dzT);
       KD_LAUNCH_CHECK();
-      KD_LAUNCH(k_transpose, dim3((unsigned)kd_ceil_div(p.Cp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256),
-                         0, s, (const bf16_t*)W + c0 * d, d, clen, d, WT, p.Cp);
-      KD_LAUNCH_CHECK();
       const int kdh = (int)kd_round_up(clen, 64);
       const int gdh = grid_of(p.nTT * p.nDT);
       const int nCTw = (int)kd_ceil_div(clen, TC::BN);
       const int gdw = grid_of(nCTw * p.nDT);
-      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, dzT, WT, hT, T, d, p.Tp, p.Cp, c0, clen,
+      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, dzT, (const bf16_t*)W, hT, T, d, p.Tp, p.Cp, c0, clen,
                          kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, dh, dW);
       KD_LAUNCH_CHECK();
     }
