@@ -661,27 +661,59 @@ __global__ void k_csr_count(int64_t T, int K, const int32_t* __restrict__ sidx, 
   if (k < (int)tok[t * TOKF + TK_NV]) atomicAdd(&cnt[sidx[i]], 1);
 }
 
-// Exclusive scan of cnt[0..n) into off[0..n]; one workgroup.
-__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ cnt, int64_t n, int32_t* __restrict__ off) {
-  __shared__ int32_t part[1024];
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t b = threadIdx.x * per, e = min(n, b + per);
+// Exclusive scan of cnt[0..n) into off[0..n] in segments of SCAN_SEG:
+// k_seg_sum sums each segment, k_seg_scan scans it after adding the sums of
+// the segments before it (few: n / SCAN_SEG).
+constexpr int SCAN_SEG = 4096;  // 256 threads x 16 elements
+
+__global__ __launch_bounds__(256) void k_seg_sum(const int32_t* __restrict__ cnt, int64_t n,
+                                                 int32_t* __restrict__ segsum) {
+  __shared__ int32_t red[4];
+  const int64_t b = (int64_t)blockIdx.x * SCAN_SEG;
   int32_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += cnt[i];
-  part[threadIdx.x] = s;
+  for (int i = threadIdx.x; i < SCAN_SEG; i += 256) s += (b + i < n) ? cnt[b + i] : 0;
+  s = wave_sum_i32(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int32_t x = ((int)threadIdx.x >= o) ? part[threadIdx.x - o] : 0;
-    __syncthreads();
-    part[threadIdx.x] += x;
-    __syncthreads();
+  if (threadIdx.x == 0) segsum[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(256) void k_seg_scan(const int32_t* __restrict__ cnt, int64_t n,
+                                                  const int32_t* __restrict__ segsum, int nseg,
+                                                  int32_t* __restrict__ off) {
+  __shared__ int32_t wsum[4];
+  __shared__ int32_t base_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (w == 0) {
+    int32_t p = 0;
+    for (int i = lane; i < (int)blockIdx.x; i += 64) p += segsum[i];
+    p = wave_sum_i32(p);
+    if (lane == 0) base_s = p;
   }
-  int32_t run = part[threadIdx.x] - s;
-  for (int64_t i = b; i < e; ++i) {
-    off[i] = run;
-    run += cnt[i];
+  const int64_t b = (int64_t)blockIdx.x * SCAN_SEG + tid * 16;
+  int32_t v[16], t = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = (b + i < n) ? cnt[b + i] : 0;
+    t += v[i];
   }
-  if (threadIdx.x == 1023) off[n] = part[1023];
+  // inclusive scan of the thread totals: within the wavefront, then across
+  int32_t x = t;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int32_t run = base_s + x - t;
+  for (int i = 0; i < w; ++i) run += wsum[i];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (b + i < n) off[b + i] = run;
+    run += v[i];
+  }
+  if ((int)blockIdx.x == nseg - 1 && tid == 255) off[n] = run;
 }
 
 // Scatter entries (token, coefficient) into their vocabulary row's bucket.
@@ -747,7 +779,7 @@ struct LossPlan {
   int K, Kp2, mode, nVT, nTT, nDT, nchunks;
   size_t o_sidx, o_stlp, o_zS, o_coef, o_tok, o_starts, o_part, o_err;
   size_t o_hT, o_dz, o_dzT;                          // dense modes
-  size_t o_cnt, o_off, o_fill, o_entt, o_entr;       // sparse modes
+  size_t o_cnt, o_off, o_fill, o_entt, o_entr, o_seg; // sparse modes
   size_t total;
 };
 
@@ -785,7 +817,7 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_err = o; o = align_up(o + 4);
   p.o_hT = p.o_dz = p.o_dzT = 0;
-  p.o_cnt = p.o_off = p.o_fill = p.o_entt = p.o_entr = 0;
+  p.o_cnt = p.o_off = p.o_fill = p.o_entt = p.o_entr = p.o_seg = 0;
   if (mode == KD_TAIL || mode == KD_FULL) {
     p.o_hT = o; o = align_up(o + (size_t)d * p.Tp * 2);
     p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
@@ -796,6 +828,7 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
     p.o_fill = o; o = align_up(o + (size_t)(V + 1) * 4);
     p.o_entt = o; o = align_up(o + TK * 4);
     p.o_entr = o; o = align_up(o + TK * 4);
+    p.o_seg = o; o = align_up(o + (size_t)kd_ceil_div(V, SCAN_SEG) * 4);
   }
   p.total = o;
   return true;
@@ -904,7 +937,10 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
     KD_LAUNCH(k_fill_i32, dim3(512), dim3(256), 0, s, fillc, V + 1, 0);
     const unsigned ge = (unsigned)kd_ceil_div(T * K, 256);
     KD_LAUNCH(k_csr_count, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, tok, cnt);
-    KD_LAUNCH(k_scan, dim3(1), dim3(1024), 0, s, cnt, V, off);
+    const int nseg = (int)kd_ceil_div(V, SCAN_SEG);
+    int32_t* segsum = at<int32_t>(ws, p.o_seg);
+    KD_LAUNCH(k_seg_sum, dim3(nseg), dim3(256), 0, s, cnt, V, segsum);
+    KD_LAUNCH(k_seg_scan, dim3(nseg), dim3(256), 0, s, cnt, V, segsum, nseg, off);
     KD_LAUNCH(k_csr_fill, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, coef, tok, off, fillc, ent_t, ent_r);
     KD_LAUNCH(k_sparse_dw, dim3((unsigned)V), dim3(256), 0, s, (const bf16_t*)h, d, off, ent_t, ent_r, dW);
     KD_LAUNCH_CHECK();
