@@ -51,28 +51,72 @@ __device__ __forceinline__ bool tile_of(int bid, int nblocks, int nM, int nN, in
 }
 
 // z[t][v] = sum_j g[t][j] U[v][j] + b[v] for the token block [t0, t0+Tb).
+// The tile is computed as z^T (rows = vocabulary, columns = tokens), so each
+// lane holds 4 consecutive vocabulary entries of one token.  The epilogue
+// stages half of the tile's tokens at a time in LDS (fp32, 1 KB token rows,
+// 16-byte chunks XOR-swizzled by token) and stores whole token rows with the
+// bias added: 1 KB of contiguous z per wavefront store.
+constexpr int CG_LDS = (CC::BN / 2) * CC::BM * 4;  // 128 tokens x 256 vocabulary fp32
+static_assert(CG_LDS >= CC::LDS_BYTES, "epilogue staging reuses the operand stages");
+
+__device__ __forceinline__ int cg_swz(int tl) { return (tl & 31) << 1; }
+
 __global__ __launch_bounds__(256, 1) void k_cache_gemm(const bf16_t* __restrict__ g, const bf16_t* __restrict__ U,
                                                        const float* __restrict__ b, int64_t Tb, int64_t d,
                                                        int64_t V, int nTT, int nVT, float* __restrict__ z) {
   extern __shared__ __align__(16) bf16_t lds[];
-  int tt, vt;
-  if (!tile_of(blockIdx.x, gridDim.x, nTT, nVT, 4, tt, vt)) return;
-  const int64_t m0 = (int64_t)tt * CC::BM, n0 = (int64_t)vt * CC::BN;
+  int vt, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 4, vt, tt)) return;
+  const int64_t m0 = (int64_t)vt * CC::BM, n0 = (int64_t)tt * CC::BN;
   Acc<CC> acc;
-  gemm_tile_pipe<CC>(g, d, m0, Tb, U, d, n0, V, (int)d, lds, acc);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  gemm_tile_pipe<CC>(U, d, m0, V, g, d, n0, Tb, (int)d, lds, acc);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / CC::WN, wn = wave % CC::WN;
+  float* E = (float*)lds;
+  // readout: thread -> 16-byte chunk c of the token rows wave, wave+4, ...
+  const int c = tid & 63;
+  const int64_t v = m0 + 4 * c;
+  float bv[4];
 #pragma unroll
-  for (int fn = 0; fn < CC::FN; ++fn) {
-    const int64_t v = n0 + acc_col<CC>(wn, fn, lane);
-    const float bv = (b != nullptr && v < V) ? b[v] : 0.f;
+  for (int e = 0; e < 4; ++e) bv[e] = (b != nullptr && v + e < V) ? b[v + e] : 0.f;
+  const bool vec = ((V & 3) == 0) && (v + 3 < V);
+  __syncthreads();  // every wavefront is done with the operand stages
 #pragma unroll
-    for (int fm = 0; fm < CC::FM; ++fm)
+  for (int half = 0; half < 2; ++half) {
+    if (wn == half) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t t = m0 + acc_row<CC>(wm, fm, e, lane);
-        if (t < Tb && v < V) z[t * V + v] = acc.v[fm][fn][e] + bv;
+      for (int fn = 0; fn < CC::FN; ++fn) {
+        const int tl = fn * 32 + (lane & 31);
+        float* row = E + tl * CC::BM;
+#pragma unroll
+        for (int fm = 0; fm < CC::FM; ++fm)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cv = (wm * CC::TM + fm * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+            *(f32x4*)(row + ((cv ^ cg_swz(tl)) << 2)) =
+                f32x4{acc.v[fm][fn][4 * q], acc.v[fm][fn][4 * q + 1], acc.v[fm][fn][4 * q + 2], acc.v[fm][fn][4 * q + 3]};
+          }
       }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < CC::BN / 2 / 4; ++i) {
+      const int tl = wave + 4 * i;
+      const int64_t t = n0 + half * (CC::BN / 2) + tl;
+      f32x4 x = *(const f32x4*)(E + tl * CC::BM + ((c ^ cg_swz(tl)) << 2));
+      x += f32x4{bv[0], bv[1], bv[2], bv[3]};
+      if (t < Tb) {
+        float* dst = z + t * V + v;
+        if (vec) {
+          *(f32x4*)dst = x;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (v + e < V) dst[e] = x[e];
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -667,7 +711,7 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
     const int64_t tb = (T - t0 < p.Tb) ? T - t0 : p.Tb;
     const int nTT = (int)kd_ceil_div(tb, CC::BM), nVT = (int)kd_ceil_div(V, CC::BN);
     const int grid = (int)kd_round_up((int64_t)nTT * nVT, 8);
-    KD_LAUNCH(k_cache_gemm, dim3(grid), dim3(CC::NT), CC::LDS_BYTES, s, (const bf16_t*)g + t0 * d,
+    KD_LAUNCH(k_cache_gemm, dim3(grid), dim3(CC::NT), CG_LDS, s, (const bf16_t*)g + t0 * d,
                        (const bf16_t*)U, b, tb, d, V, nTT, nVT, z);
     launch_rows(z, V, tb, V, K, rho_host, n_rho, idx + t0 * K, val + t0 * K, lse + t0, m_q + t0,
                 n_rho ? k_rho + t0 * n_rho : nullptr, s);
