@@ -74,6 +74,10 @@ __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 2)) & 3; }
 // the same 4 rows + 8); the XOR puts those 4 rows on disjoint bank quarters.
 __device__ __forceinline__ int mswz(int k) { return (k & 3) << 2; }
 
+#ifndef PIPE_BARRIER_LGKM
+#define PIPE_BARRIER_LGKM 1
+#endif
+
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
@@ -214,19 +218,23 @@ __device__ __forceinline__ void pipe_fread(PipeState<C, AT, BT>& P, int stage, i
   for (int i = 1; i < C::FM; ++i) P.fa[BUF][i] = P.a.fread(i, stage, ks);
 }
 
-template <class C, bool AT, bool BT, int BUF>
+template <class C, bool AT, bool BT, int BUF, int I0 = 0, int I1 = C::FM>
 __device__ __forceinline__ void pipe_mfma(PipeState<C, AT, BT>& P, Acc<C>& acc) {
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int i = I0; i < I1; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc.v[i][j] = mfma32x32x16(P.fa[BUF][i], P.fb[BUF][j], acc.v[i][j]);
 }
 
-// Interleave of one slice for the scheduler: the global loads and the second
-// substep's fragment reads among the first substep's MFMAs; the LDS stores
-// and the next slice's first fragment reads among the second substep's.
+// Interleave of one slice for the scheduler, in two regions separated by a
+// scheduling barrier.  Region 1: the first substep's MFMAs with the global
+// loads and the second substep's fragment reads among them, then the first
+// half of the second substep's MFMAs with the LDS stores.  Region 2: the
+// rest of the second substep's MFMAs with the next slice's first fragment
+// reads.  Every LDS store thus precedes those reads, which the barrier
+// below relies on.
 template <class C, int NFR>
-__device__ __forceinline__ void pipe_schedule() {
+__device__ __forceinline__ void pipe_schedule1() {
   constexpr int NMF = C::FM * C::FN;
   static_assert(NFR <= NMF, "fragment reads per substep");
 #pragma unroll
@@ -236,10 +244,39 @@ __device__ __forceinline__ void pipe_schedule() {
     if (m < C::NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 #pragma unroll
-  for (int m = 0; m < NMF; ++m) {
+  for (int m = 0; m < NMF / 2; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (m < C::NLD) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    if (m >= NMF - NFR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  static_assert(C::NLD <= NMF / 2, "LDS stores per half substep");
+}
+template <class C, int NFR>
+__device__ __forceinline__ void pipe_schedule2() {
+  constexpr int NMF = C::FM * C::FN;
+#pragma unroll
+  for (int m = 0; m < NMF / 2; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    // spread NFR reads over NMF/2 slots
+    constexpr int H = NMF / 2;
+    const int r = ((m + 1) * NFR) / H - (m * NFR) / H;
+    if (r == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (r == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  static_assert(NFR <= NMF, "at most two reads per slot");
+}
+
+// End-of-slice barrier.  Every LDS store and every read of the slice just
+// consumed precede the last N reads (the next slice's first fragments, from a
+// stage completed earlier), so waiting until at most N LDS operations are
+// outstanding orders all cross-wavefront hazards while those N reads stay in
+// flight across the barrier.
+template <int N>
+__device__ __forceinline__ void pipe_barrier() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt");
+  if constexpr (PIPE_BARRIER_LGKM) {
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  } else {
+    __syncthreads();
   }
 }
 
@@ -249,11 +286,14 @@ __device__ __forceinline__ void pipe_iter(PipeState<C, AT, BT>& P, int kt, int n
   pipe_gload<C, AT, BT, SET ^ 1>(P, kt + 3 < nk ? kt + 3 : nk - 1);
   pipe_fread<C, AT, BT, 1>(P, kt % 3, 1);
   pipe_mfma<C, AT, BT, 0>(P, acc);
-  pipe_mfma<C, AT, BT, 1>(P, acc);
+  pipe_mfma<C, AT, BT, 1, 0, C::FM / 2>(P, acc);
   pipe_lstore<C, AT, BT, SET>(P, (kt + 2) % 3);
+  pipe_schedule1<C, NFR>();
+  __builtin_amdgcn_sched_barrier(0);
+  pipe_mfma<C, AT, BT, 1, C::FM / 2, C::FM>(P, acc);
   pipe_fread<C, AT, BT, 0>(P, (kt + 1) % 3, 0);
-  pipe_schedule<C, NFR>();
-  __syncthreads();
+  pipe_schedule2<C, NFR>();
+  pipe_barrier<(NFR < 15 ? NFR : 15)>();
 }
 
 // One BM x BN tile over K (a multiple of 32).  `lds` holds C::LDS_BYTES.
