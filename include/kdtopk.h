@@ -88,7 +88,8 @@ size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_
  *                                 for the other modes)
  *      mode         kd_mode
  *      chunk        vocabulary rows per chunk of the backward (> 0; e.g. 8192;
- *                   rounded up to 256, and chunk * d * 2 must stay below 4 GiB).
+ *                   rounded up to 256).  chunk x d, T x d and T x chunk bf16
+ *                   arrays must each stay below 4 GiB.
  *                   Vocabulary-sized scratch is bounded by chunk rows.
  *      scale        loss = scale * sum_t L_t (e.g. 1/T for the token mean)
  * Out: loss         [1]    fp32   the scalar loss

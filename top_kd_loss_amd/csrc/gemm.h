@@ -9,8 +9,10 @@
 //   K-major  (MN = false): element (r, k) at P[r * ld + k]; the tile's rows
 //            [r0, r_end) are read, clamped to r_end - 1.
 //   MN-major (MN = true):  element (r, k) at P[k * ld + r]; the tile's
-//            columns [r0, r_end) are read (8 at a time, clamped to start at
-//            r_end - 8 or below) from rows k < k_end (clamped to k_end - 1).
+//            columns [r0, r_end) are read in aligned groups of 8, chunks
+//            past the one holding column r_end - 1 clamped to it (each row
+//            must hold r_end rounded up to 8 elements), from rows k < k_end
+//            (clamped to k_end - 1).
 // K-major slices sit in LDS as 64-byte rows (one per M/N index); MN-major
 // slices as BM- (or BN-) wide rows (one per k) that reach the matrix cores
 // through transposing LDS reads (ds_read_b64_tr_b16), so no operand is ever
@@ -152,7 +154,7 @@ struct PipeOperand<C, ROWS, TW, NF, LDN, true> {
     kr = tid / CPK;
     kend = k_end;
     ld2 = (uint32_t)(ld * 2);
-    const int cmax = (int)(r_end - r0) - 8;
+    const int cmax = (((int)(r_end - r0) - 1) >> 3) << 3;  // chunk holding the last column
     col = (uint32_t)((mc * 8 < cmax ? mc * 8 : cmax) * 2);
     // rows kr + i*KSTEP share kr's swizzle (KSTEP is a multiple of 4)
     st = lds_op + kr * ROWS + ((mc ^ mswz(kr)) << 3);

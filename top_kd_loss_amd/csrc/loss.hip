@@ -390,15 +390,11 @@ __global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const
 
 // ---------------------------------------------------------------------------
 // pass 2 (dense modes): recompute the z^T tile of one vocabulary chunk and
-// write dz = alpha * exp(z - lse) (+ r on S) as bf16 in both layouts:
-// dz [Tp][Cp] (token rows) and dzT [Cp][Tp] (vocabulary rows).
-//
-// The bf16 tile is staged in LDS as E[t][v] (512-byte token rows, 16-byte
-// chunks XOR-swizzled by zdz_swz(t)) and leaves in 16-byte stores: token
-// rows straight from E, vocabulary rows through transposing LDS reads
-// (ds_read_b64_tr_b16: within each 16-lane group, lane j names 4 elements
-// of row t0 + j/4 at columns vb + 4*(j%4); lane i receives column vb + i of
-// rows t0 .. t0+3).
+// write dz = alpha * exp(z - lse) (+ r on S) as bf16 token rows,
+// dz [Tp][Cp].  The tile is staged in LDS as E[t][v] (512-byte token rows,
+// 16-byte chunks XOR-swizzled by zdz_swz(t)) and leaves in 16-byte stores,
+// 32 threads per row.  Both backward GEMMs read dz in this one layout (the
+// dW GEMM as an MN-major operand).
 // ---------------------------------------------------------------------------
 constexpr int ZDZ_LDS = VT * TT * 2;  // 128 KB bf16 tile
 
@@ -407,8 +403,6 @@ constexpr int ZDZ_LDS = VT * TT * 2;  // 128 KB bf16 tile
 // groups of 8 chunks (transposing reads).
 __device__ __forceinline__ int zdz_swz(int t) { return ((t & 3) << 3) | ((t >> 2) & 7); }
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 // Dense part of dz for one tile into E: alpha * exp(z - lse) as bf16, zero
 // for padding tokens (nl = -inf) and for rows masked to -inf.
@@ -444,8 +438,7 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
                                                 const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
-                                                const float* __restrict__ coef, bf16_t* __restrict__ dz,
-                                                bf16_t* __restrict__ dzT) {
+                                                const float* __restrict__ coef, bf16_t* __restrict__ dz) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
@@ -507,51 +500,6 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
     const u32x4 q = *(const u32x4*)(E + tl * (VT * 2) + ((c ^ zdz_swz(tl)) << 4));
     *(u32x4*)(dz + (n0 + tl) * Cp + vo + c * 8) = q;
   }
-  // vocabulary rows: per step a wavefront covers 16 vocabulary rows x 32
-  // tokens; its four 16-lane groups take consecutive 8-token pieces, so each
-  // store instruction writes 64 contiguous bytes of 16 rows
-  const int gi = lane >> 4, li = lane & 15;
-  const int rsel = li >> 2, csel = li & 3;
-#pragma unroll 2
-  for (int it = 0; it < (VT / 16) * (TT / 32) / 4; ++it) {
-    const int job = it * 4 + wave;                // 0 .. (VT/16)*(TT/32)-1
-    const int vb = (job / (TT / 32)) * 16;
-    const int t0 = (job % (TT / 32)) * 32 + gi * 8;
-    const int va = vb + 4 * csel;                 // this lane's source columns va .. va+3
-    bf16x4_t lo, hi;
-    {
-      const int tr = t0 + rsel;
-      lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4_t*)(E + tr * (VT * 2) + (((va >> 3) ^ zdz_swz(tr)) << 4) + (va & 7) * 2));
-    }
-    {
-      const int tr = t0 + 4 + rsel;
-      hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4_t*)(E + tr * (VT * 2) + (((va >> 3) ^ zdz_swz(tr)) << 4) + (va & 7) * 2));
-    }
-    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
-    *(u32x4*)(dzT + (vo + vb + li) * Tp + n0 + t0) = u32x4{a.x, a.y, b.x, b.y};
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Transpose with zero padding: out[c][r] = in[r][c] for r < R, 0 for
-// R <= r < Rp.  in is [R][C] (row pitch ldi), out is [C][Rp].
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_transpose(const bf16_t* __restrict__ in, int64_t ldi, int64_t R, int64_t C,
-                                                   bf16_t* __restrict__ out, int64_t Rp) {
-  __shared__ bf16_t tile[64][66];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? in[r * ldi + c] : (bf16_t)0;
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < Rp) out[c * Rp + r] = tile[tx][i];
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -561,10 +509,11 @@ __global__ __launch_bounds__(256) void k_transpose(const bf16_t* __restrict__ in
 // features of one output row: the epilogue moves float4s.
 //   dh tiles: dh[t][j] (+)= sum_v W[c0+v][j] * dz[t][v]   (K = chunk rows;
 //             W is read as an MN-major operand straight from its rows)
-//   dW tiles: dW[c0+v][j] = sum_t hT[j][t] * dzT[v][t]    (K = Tp)
+//   dW tiles: dW[c0+v][j] = sum_t h[t][j] * dz[t][v]      (K = Tp; both read
+//             as MN-major operands: h's and dz's rows are token rows)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, const bf16_t* __restrict__ dzT,
-                                                 const bf16_t* __restrict__ W, const bf16_t* __restrict__ hT,
+__global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, const bf16_t* __restrict__ W,
+                                                 const bf16_t* __restrict__ h,
                                                  int64_t T, int64_t d, int64_t Tp, int64_t Cp, int64_t c0,
                                                  int64_t clen, int kdh, int first_chunk, int nTT, int nDT, int nCT,
                                                  int grid_dh, float* __restrict__ dh, float* __restrict__ dW) {
@@ -603,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
     int dj, ci;
     if (!tile_of(blockIdx.x - grid_dh, gridDim.x - grid_dh, nDT, nCT, 4, dj, ci)) return;
     const int64_t m0 = (int64_t)dj * TC::BM, n0 = (int64_t)ci * TC::BN;
-    gemm_tile_pipe<TC>(hT, Tp, m0, d, dzT, Tp, n0, clen, (int)Tp, lds, acc);
+    gemm_tile_pipe<TC, true, true>(h, d, m0, d, dz, Cp, n0, clen, (int)Tp, lds, acc, (int)T, (int)Tp);
 #pragma unroll
     for (int fn = 0; fn < TC::FN; ++fn) {
       const int64_t v = n0 + acc_col<TC>(wn, fn, lane);
@@ -778,7 +727,7 @@ struct LossPlan {
   int64_t T, d, V, Tp, Cp, C;
   int K, Kp2, mode, nVT, nTT, nDT, nchunks;
   size_t o_sidx, o_stlp, o_zS, o_coef, o_tok, o_starts, o_part, o_err;
-  size_t o_hT, o_dz, o_dzT;                          // dense modes
+  size_t o_dz;                                       // dense modes
   size_t o_cnt, o_off, o_fill, o_entt, o_entr, o_seg; // sparse modes
   size_t total;
 };
@@ -800,8 +749,11 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.C = kd_round_up(chunk, VT);
   if (p.C > kd_round_up(V, VT)) p.C = kd_round_up(V, VT);
   p.Cp = p.C;
-  // 32-bit byte offsets inside one chunk of W (MN-major operand of the dh GEMM)
-  if ((uint64_t)p.C * (uint64_t)d * 2u >= ((uint64_t)1 << 32)) return false;
+  // the GEMMs address MN-major operands (a chunk of W, h, dz) with 32-bit byte offsets
+  const uint64_t lim = (uint64_t)1 << 32;
+  const uint64_t Tp64 = (uint64_t)kd_round_up(T > 0 ? T : 1, TT);
+  if ((uint64_t)p.C * (uint64_t)d * 2u >= lim || Tp64 * (uint64_t)d * 2u >= lim || Tp64 * (uint64_t)p.C * 2u >= lim)
+    return false;
   p.nVT = (int)kd_ceil_div(V, VT);
   p.nTT = (int)(p.Tp / TT);
   p.nDT = (int)kd_ceil_div(d, TC::BN);
@@ -816,12 +768,10 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.o_starts = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
   p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_err = o; o = align_up(o + 4);
-  p.o_hT = p.o_dz = p.o_dzT = 0;
+  p.o_dz = 0;
   p.o_cnt = p.o_off = p.o_fill = p.o_entt = p.o_entr = p.o_seg = 0;
   if (mode == KD_TAIL || mode == KD_FULL) {
-    p.o_hT = o; o = align_up(o + (size_t)d * p.Tp * 2);
     p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
-    p.o_dzT = o; o = align_up(o + (size_t)p.Cp * p.Tp * 2);
   } else {
     p.o_cnt = o; o = align_up(o + (size_t)(V + 1) * 4);
     p.o_off = o; o = align_up(o + (size_t)(V + 1) * 4);
@@ -859,7 +809,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   LossPlan p;
   if (mode < KD_RENORM || mode > KD_REVERSE) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
   if (!plan_loss(T, d, V, K, mode, chunk, p))
-    return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0, chunk*d*2 < 4 GiB)",
+    return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0, and chunk*d, T*d, T*chunk bf16 each < 4 GiB)",
                    (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
   if (!loss || !dW || !W) return kd_fail(KD_EINVAL, "null required pointer (loss, W, dW)");
   if (T > 0 && (!h || !idx || !teacher_logp || !dh)) return kd_fail(KD_EINVAL, "null required pointer (h, idx, teacher_logp, dh)");
@@ -902,12 +852,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   KD_LAUNCH_CHECK();
 
   if (mode == KD_TAIL || mode == KD_FULL) {
-    bf16_t* hT = at<bf16_t>(ws, p.o_hT);
     bf16_t* dz = at<bf16_t>(ws, p.o_dz);
-    bf16_t* dzT = at<bf16_t>(ws, p.o_dzT);
-    KD_LAUNCH(k_transpose, dim3((unsigned)kd_ceil_div(p.Tp, 64), (unsigned)kd_ceil_div(d, 64)), dim3(256), 0,
-                       s, (const bf16_t*)h, d, T, d, hT, p.Tp);
-    KD_LAUNCH_CHECK();
     for (int c = 0; c < p.nchunks; ++c) {
       const int64_t c0 = (int64_t)c * p.C;
       const int64_t c1 = (c0 + p.C < V) ? c0 + p.C : V;
@@ -915,13 +860,13 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
       const int nCT = (int)kd_ceil_div(clen, VT);
       const int gz = grid_of(nCT * p.nTT);
       KD_LAUNCH(k_zdz, dim3(gz), dim3(TC::NT), ZDZ_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
-                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, dz, dzT);
+                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, dz);
       KD_LAUNCH_CHECK();
       const int kdh = (int)kd_round_up(clen, 64);
       const int gdh = grid_of(p.nTT * p.nDT);
       const int nCTw = (int)kd_ceil_div(clen, TC::BN);
       const int gdw = grid_of(nCTw * p.nDT);
-      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, dzT, (const bf16_t*)W, hT, T, d, p.Tp, p.Cp, c0, clen,
+      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0, clen,
                          kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, dh, dW);
       KD_LAUNCH_CHECK();
     }
