@@ -157,6 +157,7 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
 constexpr int P1_RED = TC::WM * TT * 2 * 4;           // (max, sum) per wavefront row and token
 constexpr int P1_Z = TT * TC::TM * 4;                 // fp32 z of 128 vocabulary rows x TT tokens
 constexpr int P1_LDS = P1_RED + P1_Z;
+static_assert(TC::LDS_BYTES + 2 * TC::NT * 4 <= P1_LDS, "pass-1 parking space");
 
 // Tile rows at or past vlim (the vocabulary's end) are set to -inf in the
 // accumulators, so the epilogues below need no per-element row test: they
@@ -194,38 +195,52 @@ __device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, float* red, int
       red[(wm * TT + col) * 2 + 0] = mx;
       red[(wm * TT + col) * 2 + 1] = s;
     }
+    __builtin_amdgcn_sched_barrier(0);  // one token column's values live at a time
   }
 }
 
-__global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+// One pass-1 tile; MASK: the tile runs past the vocabulary end (own code
+// path, so the common one carries no masking registers).
+template <bool MASK>
+__device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                   int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
                                                   int64_t Tp, const int32_t* __restrict__ sidx,
                                                   const int32_t* __restrict__ starts, float* __restrict__ zS,
-                                                  float2* __restrict__ part) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  int vt, tt;
-  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 8, vt, tt)) return;
+                                                  float2* __restrict__ part, int vt, int tt, bf16_t* lds) {
   const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   const int tid = threadIdx.x;
 
-  // thread tid owns token n0 + tid for the gather: first retained index >= m0
+  // thread tid owns token n0 + tid for the gather: first retained index >= m0,
+  // fetched before the main loop and parked in LDS past the operand stages
+  // (nothing stays live in registers across the loop)
   const int64_t ts = n0 + tid;
-  int kcur = K, vnext = SENT;
-  if (ts < T) {
-    kcur = starts[(int64_t)vt * Tp + ts];
-    vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
+  {
+    int kc = K, vn = SENT;
+    if (ts < T) {
+      kc = starts[(int64_t)vt * Tp + ts];
+      vn = kc < K ? sidx[ts * K + kc] : SENT;
+    }
+    int* park = (int*)((char*)lds + TC::LDS_BYTES);
+    park[tid] = kc;
+    park[TC::NT + tid] = vn;
   }
 
   Acc<TC> acc;
   gemm_tile_pipe<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
   __syncthreads();  // every wavefront is done with the operand stages
+  int kcur, vnext;
+  {
+    const int* park = (const int*)((const char*)lds + TC::LDS_BYTES);
+    kcur = park[tid];
+    vnext = park[TC::NT + tid];
+  }
+  __syncthreads();  // parked values read before the epilogue reuses that LDS
 
   float* red = (float*)lds;
   char* Z = (char*)lds + P1_RED;
-  const int vlim = (int)((V - m0) < VT ? (V - m0) : VT);
-  if (vlim < VT) mask_rows(acc, vlim, wm, lane);
+  if (MASK) mask_rows(acc, (int)(V - m0), wm, lane);
   pass1_reduce(acc, red, wm, wn, lane);
 
   // gather, one half of the tile's vocabulary rows at a time
@@ -273,6 +288,20 @@ __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, 
     const int64_t t = n0 + col;
     if (t < T) part[(int64_t)vt * Tp + t] = make_float2(m, s);
   }
+}
+
+__global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+                                                  int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
+                                                  int64_t Tp, const int32_t* __restrict__ sidx,
+                                                  const int32_t* __restrict__ starts, float* __restrict__ zS,
+                                                  float2* __restrict__ part) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int vt, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 8, vt, tt)) return;
+  if ((int64_t)(vt + 1) * VT > V)
+    pass1_tile<true>(W, h, T, d, V, K, nVT, nTT, Tp, sidx, starts, zS, part, vt, tt, lds);
+  else
+    pass1_tile<false>(W, h, T, d, V, K, nVT, nTT, Tp, sidx, starts, zS, part, vt, tt, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -397,6 +426,7 @@ __global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const
 // dW GEMM as an MN-major operand).
 // ---------------------------------------------------------------------------
 constexpr int ZDZ_LDS = VT * TT * 2;  // 128 KB bf16 tile
+static_assert(TC::LDS_BYTES + (2 * TC::FN + 2) * TC::NT * 4 <= ZDZ_LDS, "pass-2 parking space");
 
 // Bijection on 0..31: 32 consecutive rows hit 32 distinct chunk positions
 // (conflict-free stores), 4 consecutive rows fall into different aligned
@@ -433,48 +463,63 @@ __device__ __forceinline__ void zdz_dense(const Acc<TC>& acc, char* E, int64_t n
   }
 }
 
-__global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+// One pass-2 tile; MASK: the tile runs past the chunk end.
+template <bool MASK>
+__device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                 int64_t T, int64_t d, int64_t V, int K, int64_t Tp, int64_t Cp,
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
                                                 const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
-                                                const float* __restrict__ coef, bf16_t* __restrict__ dz) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  int ct, tt;
-  if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
+                                                const float* __restrict__ coef, bf16_t* __restrict__ dz, int ct, int tt, bf16_t* lds) {
   const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
   const int vt = (int)(m0 / VT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
 
-  float lse_t[TC::FN], al_t[TC::FN];
-#pragma unroll
-  for (int fn = 0; fn < TC::FN; ++fn) {
-    const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
-    lse_t[fn] = 0.f;
-    al_t[fn] = 0.f;
-    if (t < T) {
-      lse_t[fn] = tok[t * TOKF + TK_LSE];
-      al_t[fn] = tok[t * TOKF + TK_ALPHA];
-    }
-  }
-  // thread tid owns token row n0 + tid of the tile for the sparse term
+  // per-token values fetched before the main loop and parked in LDS past the
+  // operand stages (nothing stays live in registers across the loop): the
+  // lanes' (lse, alpha) of their 4 token columns, and for thread tid, owner
+  // of token row n0 + tid, its first retained index >= m0
   const int tid = threadIdx.x;
   const int64_t ts = n0 + tid;
   const int64_t vend = (m0 + VT < c1) ? m0 + VT : c1;
-  int kcur = K, vnext = SENT;
-  if (ts < T) {
-    kcur = starts[(int64_t)vt * Tp + ts];
-    vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
+  {
+    float* park = (float*)((char*)lds + TC::LDS_BYTES);
+#pragma unroll
+    for (int fn = 0; fn < TC::FN; ++fn) {
+      const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
+      const bool ok = t < T;
+      park[(2 * fn) * TC::NT + tid] = ok ? tok[t * TOKF + TK_LSE] : 0.f;
+      park[(2 * fn + 1) * TC::NT + tid] = ok ? tok[t * TOKF + TK_ALPHA] : 0.f;
+    }
+    int kc = K, vn = SENT;
+    if (ts < T) {
+      kc = starts[(int64_t)vt * Tp + ts];
+      vn = kc < K ? sidx[ts * K + kc] : SENT;
+    }
+    ((int*)park)[(2 * TC::FN) * TC::NT + tid] = kc;
+    ((int*)park)[(2 * TC::FN + 1) * TC::NT + tid] = vn;
   }
 
   Acc<TC> acc;
   gemm_tile_pipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
   __syncthreads();  // every wavefront is done with the operand stages
+  float lse_t[TC::FN], al_t[TC::FN];
+  int kcur, vnext;
+  {
+    const float* park = (const float*)((const char*)lds + TC::LDS_BYTES);
+#pragma unroll
+    for (int fn = 0; fn < TC::FN; ++fn) {
+      lse_t[fn] = park[(2 * fn) * TC::NT + tid];
+      al_t[fn] = park[(2 * fn + 1) * TC::NT + tid];
+    }
+    kcur = ((const int*)park)[(2 * TC::FN) * TC::NT + tid];
+    vnext = ((const int*)park)[(2 * TC::FN + 1) * TC::NT + tid];
+  }
+  __syncthreads();  // parked values read before the epilogue reuses that LDS
 
   char* E = (char*)lds;
-  const int vlim = (int)((c1 - m0) < VT ? (c1 - m0) : VT);  // tile rows inside the chunk
-  if (vlim < VT) mask_rows(acc, vlim, wm, lane);
+  if (MASK) mask_rows(acc, (int)(c1 - m0), wm, lane);  // tile rows inside the chunk
   zdz_dense(acc, E, n0, T, lse_t, al_t, wm, wn, lane);
   __syncthreads();
   // sparse term on S: dz = alpha * exp(z - lse) + r with z gathered in pass 1
@@ -500,6 +545,21 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
     const u32x4 q = *(const u32x4*)(E + tl * (VT * 2) + ((c ^ zdz_swz(tl)) << 4));
     *(u32x4*)(dz + (n0 + tl) * Cp + vo + c * 8) = q;
   }
+}
+
+__global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+                                                int64_t T, int64_t d, int64_t V, int K, int64_t Tp, int64_t Cp,
+                                                int64_t c0, int64_t c1, int nCT, int nTT,
+                                                const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
+                                                const float* __restrict__ tok, const float* __restrict__ zS,
+                                                const float* __restrict__ coef, bf16_t* __restrict__ dz) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int ct, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
+  if (c0 + (int64_t)(ct + 1) * VT > c1)
+    zdz_tile<true>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, dz, ct, tt, lds);
+  else
+    zdz_tile<false>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, dz, ct, tt, lds);
 }
 
 // ---------------------------------------------------------------------------
