@@ -393,28 +393,14 @@ __device__ __forceinline__ void row_loop(const float* zr, int64_t V, bool vec, F
   }
 }
 
-// Per-thread run merging of histogram updates: consecutive elements of one
-// thread that fall into the same bin are added once.
+// Histogram update: one LDS atomic per element and counter (merging runs of
+// equal bins per thread cost more in divergent control flow than it saved).
 struct HistRun {
-  int bin = -1, cnt = 0;
-  unsigned long long mass = 0;
   __device__ __forceinline__ void add(int b, unsigned long long m, int* cnt_h, unsigned long long* mass_h) {
-    if (b != bin) {
-      flush(cnt_h, mass_h);
-      bin = b;
-    }
-    ++cnt;
-    mass += m;
+    atomicAdd(&cnt_h[b], 1);
+    if (mass_h) atomicAdd(&mass_h[b], m);
   }
-  __device__ __forceinline__ void flush(int* cnt_h, unsigned long long* mass_h) {
-    if (bin >= 0) {
-      atomicAdd(&cnt_h[bin], cnt);
-      if (mass_h) atomicAdd(&mass_h[bin], mass);
-    }
-    bin = -1;
-    cnt = 0;
-    mass = 0;
-  }
+  __device__ __forceinline__ void flush(int*, unsigned long long*) {}
 };
 
 __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
