@@ -137,7 +137,8 @@ kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, const float* b
                               int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
                               void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of device workspace kd_topk_rows needs. */
+/* Bytes of device workspace kd_topk_rows needs (4 bytes per row, rounded up
+ * to 256; 0 for invalid sizes). */
 size_t kd_topk_rows_workspace(int64_t T, int64_t V, int32_t K, int32_t n_rho);
 
 /* The row pass of the cache build on caller-provided fp32 logits z [T, V]

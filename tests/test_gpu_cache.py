@@ -133,3 +133,22 @@ def test_rows_huge_tie_takes_lowest_indices():
     z[1, :5000] = 0.0
     z[2, 9000:] = 3.0
     _check_rows(z, 1024, rho=(0.5, 0.9))
+
+
+def test_rows_fine_ties_wide_rows():
+    """Many small groups of equal values spread over a wide row: candidate
+    bins hold ties that must resolve to the lower indices."""
+    z = synth.tie_heavy_logits(12, 40000, seed=7, step=1.0 / 64.0, span=3.0)
+    for K in (5, 256, 1000):
+        _check_rows(z, K, rho=(0.3, 0.9, 0.95))
+
+
+def test_rows_bitwise_deterministic():
+    r = np.random.default_rng(11)
+    z = torch.from_numpy((r.standard_normal((64, 151936)) * 1.05).astype(np.float32)).to(DEV)
+    a = kd.topk_rows(z, 256, RHO)
+    b = kd.topk_rows(z, 256, RHO)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x,
+                           y.view(torch.int32) if y.dtype == torch.float32 else y)

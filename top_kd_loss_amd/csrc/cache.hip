@@ -8,8 +8,16 @@
 // >= rho} ("Sparse Teacher Support Cuts LLM Distillation Cost Without
 // Losing Accuracy").
 //
-// Row pass, one workgroup per row (HBM bound; the row is streamed two or
-// three times and stays in the last-level cache between passes):
+// Row pass, one workgroup per row, in two kernels:
+//   k_topk_rows (fast)  value bins of width 1/128 below the row maximum (the
+//      maximum comes from the GEMM epilogue's per-tile maxima, or from a
+//      first streaming read); one streaming read builds packed
+//      (count, fixed-point mass) bins, whose exact integer prefix sums give
+//      logsumexp, the bin of the K-th largest value and each rho's crossing
+//      bin; a second read collects the elements of those bins, which are
+//      ordered exactly in LDS.  Rows it cannot finish are flagged.
+//   k_topk_rows_exact  for the flagged rows (or every row when V >= 2^18):
+//      radix digits of order-preserving keys, refined until exact:
 //   1  an 11-bit radix histogram of order-preserving keys with, per bin, the
 //      count and the sum of exp(z - upper edge of the bin) in 2^-31 fixed
 //      point (exact 64-bit integer sums: independent of atomic order);
@@ -55,15 +63,32 @@ __device__ __forceinline__ bool tile_of(int bid, int nblocks, int nM, int nN, in
 // lane holds 4 consecutive vocabulary entries of one token.  The epilogue
 // stages half of the tile's tokens at a time in LDS (fp32, 1 KB token rows,
 // 16-byte chunks XOR-swizzled by token) and stores whole token rows with the
-// bias added: 1 KB of contiguous z per wavefront store.
+// bias added: 1 KB of contiguous z per wavefront store.  The maximum of each
+// token row of the tile goes to tmax[t][vt] (the row pass starts from it).
 constexpr int CG_LDS = (CC::BN / 2) * CC::BM * 4;  // 128 tokens x 256 vocabulary fp32
 static_assert(CG_LDS >= CC::LDS_BYTES, "epilogue staging reuses the operand stages");
 
 __device__ __forceinline__ int cg_swz(int tl) { return (tl & 31) << 1; }
 
+// Maximum over the wavefront without LDS traffic: rotations within each
+// 16-lane row (DPP row_ror 1, 2, 4, 8), then the four row results read as
+// scalars.  Every lane returns the maximum.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __global__ __launch_bounds__(256, 1) void k_cache_gemm(const bf16_t* __restrict__ g, const bf16_t* __restrict__ U,
                                                        const float* __restrict__ b, int64_t Tb, int64_t d,
-                                                       int64_t V, int nTT, int nVT, float* __restrict__ z) {
+                                                       int64_t V, int nTT, int nVT, float* __restrict__ z,
+                                                       float* __restrict__ tmax) {
   extern __shared__ __align__(16) bf16_t lds[];
   int vt, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 4, vt, tt)) return;
@@ -105,6 +130,12 @@ __global__ __launch_bounds__(256, 1) void k_cache_gemm(const bf16_t* __restrict_
       const int64_t t = n0 + half * (CC::BN / 2) + tl;
       f32x4 x = *(const f32x4*)(E + tl * CC::BM + ((c ^ cg_swz(tl)) << 2));
       x += f32x4{bv[0], bv[1], bv[2], bv[3]};
+      float m = -KD_INF;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v + e < V) m = fmaxf(m, x[e]);
+      m = wave_max_dpp(m);  // the wavefront holds the token row's 256 values
+      if (t < Tb && lane == 0) tmax[t * nVT + vt] = m;
       if (t < Tb) {
         float* dst = z + t * V + v;
         if (vec) {
@@ -349,25 +380,25 @@ __device__ int block_rank(bool flag, RowShared& S, int* total) {
   return off + before;
 }
 
-// Visit every element of the row: f(index, value).  16-byte loads when the
-// row is 16-byte aligned and V is a multiple of 4; each thread keeps ROW_U
-// loads in flight before it processes them.
+// Visit every element of the row with NT threads: f(index, value).  16-byte
+// loads when the row is 16-byte aligned and V is a multiple of 4; each thread
+// keeps ROW_U loads in flight before it processes them.
 constexpr int ROW_U = 4;
-template <class F>
+template <int NT, class F>
 __device__ __forceinline__ void row_loop(const float* zr, int64_t V, bool vec, F&& f) {
   if (vec) {
     const float4* z4 = (const float4*)zr;
     const int64_t n4 = V >> 2;
-    for (int64_t base = threadIdx.x; base < n4; base += (int64_t)RT * ROW_U) {
+    for (int64_t base = threadIdx.x; base < n4; base += (int64_t)NT * ROW_U) {
       float4 v[ROW_U];
 #pragma unroll
       for (int u = 0; u < ROW_U; ++u) {
-        const int64_t i = base + (int64_t)u * RT;
+        const int64_t i = base + (int64_t)u * NT;
         v[u] = i < n4 ? z4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < ROW_U; ++u) {
-        const int64_t i = base + (int64_t)u * RT;
+        const int64_t i = base + (int64_t)u * NT;
         if (i < n4) {
           f(4 * i, v[u].x);
           f(4 * i + 1, v[u].y);
@@ -377,18 +408,90 @@ __device__ __forceinline__ void row_loop(const float* zr, int64_t V, bool vec, F
       }
     }
   } else {
-    for (int64_t base = threadIdx.x; base < V; base += (int64_t)RT * ROW_U) {
+    for (int64_t base = threadIdx.x; base < V; base += (int64_t)NT * ROW_U) {
       float v[ROW_U];
 #pragma unroll
       for (int u = 0; u < ROW_U; ++u) {
-        const int64_t i = base + (int64_t)u * RT;
+        const int64_t i = base + (int64_t)u * NT;
         v[u] = i < V ? zr[i] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < ROW_U; ++u) {
-        const int64_t i = base + (int64_t)u * RT;
+        const int64_t i = base + (int64_t)u * NT;
         if (i < V) f(i, v[u]);
       }
+    }
+  }
+}
+
+// Software-pipelined variant for the fast row pass: batch b + 1 (ROW_U
+// 16-byte loads per thread, indices clamped into the row so every load is
+// issued unconditionally) is in flight while batch b is processed.
+// f(index, value, e) sees each valid element, e = its slot 0..4*ROW_U-1 in
+// the thread's batch; g(base, vec) runs after each batch, where the element
+// of slot e has index 4*(base + (e/4)*NT) + e%4 (vec) or base + e*NT.
+template <int NT, class F, class G>
+__device__ __forceinline__ void row_loop_pipe(const float* zr, int64_t V, bool vec, F&& f, G&& g) {
+  if (vec) {
+    const float4* z4 = (const float4*)zr;
+    const int64_t n4 = V >> 2, last = n4 - 1;
+    const int64_t step = (int64_t)NT * ROW_U;
+    const int64_t iters = (n4 + step - 1) / step;
+    float4 cur[ROW_U];
+#pragma unroll
+    for (int u = 0; u < ROW_U; ++u) {
+      const int64_t i = threadIdx.x + (int64_t)u * NT;
+      cur[u] = z4[i < last ? i : last];
+    }
+    for (int64_t it = 0; it < iters; ++it) {
+      const int64_t base = threadIdx.x + it * step;
+      float4 nxt[ROW_U];
+#pragma unroll
+      for (int u = 0; u < ROW_U; ++u) {
+        const int64_t i = base + step + (int64_t)u * NT;
+        nxt[u] = z4[i < last ? i : last];
+      }
+#pragma unroll
+      for (int u = 0; u < ROW_U; ++u) {
+        const int64_t i = base + (int64_t)u * NT;
+        if (i < n4) {
+          f(4 * i, cur[u].x, 4 * u);
+          f(4 * i + 1, cur[u].y, 4 * u + 1);
+          f(4 * i + 2, cur[u].z, 4 * u + 2);
+          f(4 * i + 3, cur[u].w, 4 * u + 3);
+        }
+      }
+      g(base, true);
+#pragma unroll
+      for (int u = 0; u < ROW_U; ++u) cur[u] = nxt[u];
+    }
+  } else {
+    constexpr int U = 4 * ROW_U;
+    const int64_t last = V - 1;
+    const int64_t step = (int64_t)NT * U;
+    const int64_t iters = (V + step - 1) / step;
+    float cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = threadIdx.x + (int64_t)u * NT;
+      cur[u] = zr[i < last ? i : last];
+    }
+    for (int64_t it = 0; it < iters; ++it) {
+      const int64_t base = threadIdx.x + it * step;
+      float nxt[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + step + (int64_t)u * NT;
+        nxt[u] = zr[i < last ? i : last];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * NT;
+        if (i < V) f(i, cur[u], u);
+      }
+      g(base, false);
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
   }
 }
@@ -403,14 +506,18 @@ struct HistRun {
   __device__ __forceinline__ void flush(int*, unsigned long long*) {}
 };
 
-__global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
-                                                  int n_rho, float rho0, float rho1, float rho2, float rho3,
-                                                  float rho4, float rho5, float rho6, float rho7,
-                                                  int32_t* __restrict__ idx_out, float* __restrict__ val_out,
-                                                  float* __restrict__ lse_out, float* __restrict__ mq_out,
-                                                  int32_t* __restrict__ krho_out) {
+// Exact row pass for the rows the fast pass flagged (flags[row] != 0), or
+// for every row when flags is NULL.
+__global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
+                                                        int n_rho, float rho0, float rho1, float rho2, float rho3,
+                                                        float rho4, float rho5, float rho6, float rho7,
+                                                        const int32_t* __restrict__ flags,
+                                                        int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+                                                        float* __restrict__ lse_out, float* __restrict__ mq_out,
+                                                        int32_t* __restrict__ krho_out) {
   __shared__ RowShared S;
   const int64_t row = blockIdx.x;
+  if (flags != nullptr && flags[row] == 0) return;
   const float* zr = z + row * ldz;
   const int tid = threadIdx.x;
   const bool vec = ((V & 3) == 0) && ((((uintptr_t)zr) & 15) == 0);
@@ -431,7 +538,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, i
   {
     const int cp = tid & (NCOPY - 1);
     HistRun run;
-    row_loop(zr, V, vec, [&](int64_t, float x) {
+    row_loop<RT>(zr, V, vec, [&](int64_t, float x) {
       const int b = (int)(fkey(x) >> 21);
       const float ex = __expf(x - S.ref0[b]);
       run.add(b, (unsigned long long)(uint32_t)fmaf(ex, fxs, 0.5f), S.u.copies.cnt[cp], S.u.copies.mass[cp]);
@@ -482,7 +589,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, i
     for (int i = tid; i < NB; i += RT) S.u.late.cntR[0][i] = 0;
     __syncthreads();
     HistRun run;
-    row_loop(zr, V, vec, [&](int64_t, float x) {
+    row_loop<RT>(zr, V, vec, [&](int64_t, float x) {
       const uint32_t k = fkey(x);
       if ((k >> (32 - pbits)) == pre) run.add((int)((k >> sh) & ((1u << dbits) - 1u)), 0ull, S.u.late.cntR[0], nullptr);
     });
@@ -542,7 +649,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, i
       }
       const bool collect = (g0 == 0 && pb == 11);  // top-K candidates ride on the first refinement pass
       HistRun run[RHO_GROUP];
-      row_loop(zr, V, vec, [&](int64_t i, float x) {
+      row_loop<RT>(zr, V, vec, [&](int64_t i, float x) {
         const uint32_t k = fkey(x);
         if (collect) {
           const uint32_t kp = k >> (32 - pbits);
@@ -635,9 +742,385 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ z, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast row pass: one workgroup of RF threads per row, three streaming reads
+// of the row (the second and third are served by the last-level cache).
+//   A  the row maximum zmax;
+//   B  a histogram over NBL value bins below zmax, bin b holding the values
+//      with floor(128 (zmax - z)) = b (the last bin also everything lower).
+//      A bin packs its count (bits 46..63) and the sum of
+//      round(2^23 exp(z - e_b)), e_b = zmax - b/128 its upper edge, into one
+//      64-bit word: one LDS atomic per element, integer sums independent of
+//      the atomic order.  The bin masses, rescaled to a common 2^-44 fixed
+//      point relative to exp(zmax), give logsumexp, the bin of the K-th
+//      largest value and, per rho, the bin where the mass accumulated from
+//      the top reaches rho of the total (exact integer prefix sums);
+//   C  collect the elements of the bins down to the K-th one (the top-K
+//      candidates) and those of the crossing bins, then order them in LDS by
+//      (value desc, index asc): the top-K and each k_rho follow exactly.
+// The bin of a value is a monotone function of it, so equal values share a
+// bin and every bin above another holds only larger values.  Rows this path
+// cannot finish (non-finite maximum, too many candidates, a crossing in the
+// lowest bin) are flagged for k_topk_rows_exact.
+// ---------------------------------------------------------------------------
+constexpr int RF = 512;                        // threads of the fast row kernel
+constexpr int NBL = 4096;                      // value bins
+constexpr int BPT = NBL / RF;                  // bins per thread in the scans
+constexpr float BIN_INVW = 128.f;              // bins per unit of logit
+constexpr float BIN_W = 1.f / 128.f;
+constexpr int CAPK = 2048;                     // top-K candidates
+constexpr int CAPR = 2048;                     // crossing-bin candidates, all targets
+constexpr int CNT_SHIFT = 46;
+constexpr unsigned long long MASS_MASK = (1ull << CNT_SHIFT) - 1ull;
+constexpr int64_t VFAST_MAX = ((int64_t)1 << 18) - 1;  // bin counts fit 18 bits
+
+struct FastShared {
+  union {
+    unsigned long long hist[NBL];  // pass B and the scans
+    double m[CAPR];                // candidate masses by rank (after pass C)
+  } u;
+  unsigned long long poolK[CAPK];  // ((~key) << 32) | index
+  unsigned long long poolR[CAPR];
+  unsigned long long scan_m[RF / 64];
+  int scan_c[RF / 64];
+  double red_d[RF / 64];
+  float red_f[RF / 64];
+  int red_i[RF / 64];
+  unsigned long long total_q;
+  int bK, aboveK, nbK, fillK;
+  int bR[RHO_MAX], cntAboveR[RHO_MAX], nR[RHO_MAX], fillR[RHO_MAX], segR[RHO_MAX];
+  unsigned long long massAboveR[RHO_MAX];
+  float rho[RHO_MAX];
+};
+
+// Value bin of x below the row maximum: monotone non-increasing in x
+// (rounded subtraction, exact scaling by 128); -inf goes to the last bin.
+__device__ __forceinline__ int vbin(float x, float zmax) {
+  return (int)fminf(fmaxf((zmax - x) * BIN_INVW, 0.f), (float)(NBL - 1));  // in [0, NBL) for any input
+}
+// Upper edge of bin b, rounded once (b / 128 is exact).
+__device__ __forceinline__ float vedge(int b, float zmax) { return fmaf(-(float)b, BIN_W, zmax); }
+
+__device__ __forceinline__ float fast_block_max(float v, FastShared& S) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) S.red_f[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = S.red_f[0];
+  for (int i = 1; i < RF / 64; ++i) r = fmaxf(r, S.red_f[i]);
+  __syncthreads();
+  return r;
+}
+
+// Sum in a fixed order (per thread, then the wavefront tree, then the waves
+// in order): deterministic for a fixed assignment of terms to threads.
+__device__ __forceinline__ double fast_block_sum(double v, FastShared& S) {
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) S.red_d[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = 0.0;
+  for (int i = 0; i < RF / 64; ++i) r += S.red_d[i];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int fast_block_min(int v, FastShared& S) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) S.red_i[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = S.red_i[0];
+  for (int i = 1; i < RF / 64; ++i) r = min(r, S.red_i[i]);
+  __syncthreads();
+  return r;
+}
+
+// Exclusive prefix over threads (thread order) of (m, c); integer sums, so
+// the result does not depend on the order of the additions.
+__device__ __forceinline__ void fast_excl_scan(unsigned long long m, int c, FastShared& S, unsigned long long& em,
+                                               int& ec, unsigned long long& tm, int& tc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  unsigned long long x = m;
+  int y = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long tx = __shfl_up(x, o, 64);
+    const int ty = __shfl_up(y, o, 64);
+    if (lane >= o) {
+      x += tx;
+      y += ty;
+    }
+  }
+  if (lane == 63) {
+    S.scan_m[w] = x;
+    S.scan_c[w] = y;
+  }
+  __syncthreads();
+  unsigned long long om = 0ull, all_m = 0ull;
+  int oc = 0, all_c = 0;
+  for (int i = 0; i < RF / 64; ++i) {
+    if (i < w) {
+      om += S.scan_m[i];
+      oc += S.scan_c[i];
+    }
+    all_m += S.scan_m[i];
+    all_c += S.scan_c[i];
+  }
+  __syncthreads();
+  em = om + x - m;
+  ec = oc + y - c;
+  tm = all_m;
+  tc = all_c;
+}
+
+// Sort key: ascending order = value descending, then index ascending.
+__device__ __forceinline__ unsigned long long cand_key(float x, int64_t i) {
+  return ((unsigned long long)(~fkey(x)) << 32) | (unsigned long long)i;
+}
+__device__ __forceinline__ float cand_value(unsigned long long c) {
+  const uint32_t k = ~(uint32_t)(c >> 32);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
+                                                  int n_rho, float rho0, float rho1, float rho2, float rho3,
+                                                  float rho4, float rho5, float rho6, float rho7,
+                                                  const float* __restrict__ tmax, int n_tmax,
+                                                  int32_t* __restrict__ flags, int32_t* __restrict__ idx_out,
+                                                  float* __restrict__ val_out, float* __restrict__ lse_out,
+                                                  float* __restrict__ mq_out, int32_t* __restrict__ krho_out) {
+  __shared__ FastShared S;
+  const int64_t row = blockIdx.x;
+  const float* zr = z + row * ldz;
+  const int tid = threadIdx.x;
+  const bool vec = ((V & 3) == 0) && ((((uintptr_t)zr) & 15) == 0);
+  const float rhos[RHO_MAX] = {rho0, rho1, rho2, rho3, rho4, rho5, rho6, rho7};
+
+  // ---- A: the row maximum (from the producer's per-tile maxima when given)
+  float mx = -KD_INF;
+  if (tmax != nullptr) {
+    for (int p = tid; p < n_tmax; p += RF) mx = fmaxf(mx, tmax[row * n_tmax + p]);
+  } else {
+    row_loop_pipe<RF>(zr, V, vec, [&](int64_t, float x, int) { mx = fmaxf(mx, x); }, [](int64_t, bool) {});
+  }
+  const float zmax = fast_block_max(mx, S);
+  if (!(fabsf(zmax) <= 3.4028234663852886e38f)) {  // all -inf, +inf present, or NaN only
+    if (tid == 0) flags[row] = 1;
+    return;
+  }
+
+  // ---- B: packed (count, fixed-point mass) histogram of the value bins
+  for (int i = tid; i < NBL; i += RF) S.u.hist[i] = 0ull;
+  __syncthreads();
+  row_loop_pipe<RF>(
+      zr, V, vec,
+      [&](int64_t, float x, int) {
+        const int b = vbin(x, zmax);
+        const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
+        const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
+        atomicAdd(&S.u.hist[b], w);
+      },
+      [](int64_t, bool) {});
+  __syncthreads();
+
+  // bins [tid*BPT, tid*BPT + BPT) per thread: masses in 2^-44 units of exp(zmax)
+  unsigned long long bm[BPT];
+  int bc[BPT];
+  unsigned long long tm = 0ull;
+  int tc = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const int b = tid * BPT + i;
+    const unsigned long long w = S.u.hist[b];
+    const unsigned long long fix = w & MASS_MASK;
+    bc[i] = (int)(w >> CNT_SHIFT);
+    bm[i] = fix ? (unsigned long long)__double2ll_rn((double)fix * 2097152.0 *
+                                                      exp((double)vedge(b, zmax) - (double)zmax))
+                : 0ull;
+    tm += bm[i];
+    tc += bc[i];
+  }
+  unsigned long long em, total;
+  int ec, ctot;
+  fast_excl_scan(tm, tc, S, em, ec, total, ctot);
+  const double lse = (double)zmax + log((double)total * 5.684341886080802e-14);  // 2^-44
+  unsigned long long tq[RHO_MAX];
+#pragma unroll
+  for (int j = 0; j < RHO_MAX; ++j) {
+    double t = ceil((double)rhos[j] * (double)total);
+    unsigned long long q = (unsigned long long)t;
+    tq[j] = (j < n_rho) ? (q < total ? (q > 0ull ? q : 1ull) : total) : ~0ull;
+  }
+  if (tid == 0) {
+    S.bK = -1;
+#pragma unroll
+    for (int j = 0; j < RHO_MAX; ++j) {
+      S.bR[j] = -1;
+      S.rho[j] = rhos[j];
+    }
+  }
+  __syncthreads();
+  {
+    unsigned long long cm = em;
+    int cc = ec;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int b = tid * BPT + i;
+      const unsigned long long nm = cm + bm[i];
+      const int nc = cc + bc[i];
+      if (cc < K && nc >= K) {
+        S.bK = b;
+        S.aboveK = cc;
+        S.nbK = bc[i];
+      }
+#pragma unroll
+      for (int j = 0; j < RHO_MAX; ++j)
+        if (j < n_rho && cm < tq[j] && nm >= tq[j]) {
+          S.bR[j] = b;
+          S.cntAboveR[j] = cc;
+          S.massAboveR[j] = cm;
+          S.nR[j] = bc[i];
+        }
+      cm = nm;
+      cc = nc;
+    }
+  }
+  __syncthreads();
+  // candidate segments: one per distinct crossing bin; fall back when the
+  // candidates do not fit or a crossing lies in the last (unbounded) bin
+  const int bK = S.bK;
+  const int nKc = S.aboveK + S.nbK;
+  int bR[RHO_MAX], seg[RHO_MAX];
+  bool own[RHO_MAX];
+  int used = 0;
+  bool fail = (bK < 0) || (nKc > CAPK);
+#pragma unroll
+  for (int j = 0; j < RHO_MAX; ++j) {
+    bR[j] = -1;
+    seg[j] = 0;
+    own[j] = false;
+    if (j < n_rho) {
+      bR[j] = S.bR[j];
+      if (bR[j] < 0 || bR[j] == NBL - 1) fail = true;
+      int first = j;
+      for (int q = 0; q < j; ++q)
+        if (bR[q] == bR[j] && first == j) first = q;
+      own[j] = (first == j);
+      seg[j] = own[j] ? used : seg[first];
+      if (own[j]) used += S.nR[j];
+    }
+  }
+  if (used > CAPR) fail = true;
+  if (fail) {
+    if (tid == 0) flags[row] = 1;
+    return;
+  }
+  if (tid == 0) {
+    flags[row] = 0;
+    S.fillK = 0;
+#pragma unroll
+    for (int j = 0; j < RHO_MAX; ++j) {
+      S.fillR[j] = 0;
+      S.segR[j] = seg[j];
+    }
+  }
+  __syncthreads();
+
+  // ---- C: collect the candidates (rare: the LDS slot atomics run only for
+  // the lanes holding one)
+  row_loop_pipe<RF>(
+      zr, V, vec,
+      [&](int64_t i, float x, int) {
+        const int b = vbin(x, zmax);
+        // the bins are recomputed exactly as in pass B, so the counts match;
+        // the bounds tests only keep LDS writes inside the pools regardless
+        if (b <= bK) {
+          const int slot = atomicAdd(&S.fillK, 1);
+          if (slot < CAPK) S.poolK[slot] = cand_key(x, i);
+        }
+        int jr = -1;  // the first target with this crossing bin owns its segment
+#pragma unroll
+        for (int j = RHO_MAX - 1; j >= 0; --j) jr = (b == bR[j]) ? j : jr;  // bR[j] = -1 past n_rho
+        if (jr >= 0) {
+          const int slot = S.segR[jr] + atomicAdd(&S.fillR[jr], 1);
+          if (slot < CAPR) S.poolR[slot] = cand_key(x, i);
+        }
+      },
+      [](int64_t, bool) {});
+  __syncthreads();
+
+  // top-K: rank of each candidate among all of them (distinct keys)
+  for (int p = tid; p < nKc; p += RF) {
+    const unsigned long long mine = S.poolK[p];
+    int r = 0;
+#pragma unroll 8
+    for (int q = 0; q < nKc; ++q) r += (S.poolK[q] < mine) ? 1 : 0;
+    if (r < K) {
+      const int64_t i = (int64_t)(mine & 0xffffffffull);
+      const float x = zr[i];  // the stored value keeps its bits (-0.0)
+      idx_out[row * K + r] = (int32_t)i;
+      val_out[row * K + r] = x;
+      S.u.m[r] = exp((double)x - lse);
+    }
+  }
+  __syncthreads();
+  double kept = 0.0;
+  for (int r = tid; r < K; r += RF) kept += S.u.m[r];
+  kept = fast_block_sum(kept, S);
+  if (tid == 0) {
+    lse_out[row] = (float)lse;
+    mq_out[row] = (float)(1.0 - kept);
+  }
+
+  // k_rho: masses of the crossing bin's elements in rank order, then the
+  // first rank where the mass from the top reaches rho
+  const double inv_total = 1.0 / (double)total;
+  for (int j = 0; j < n_rho; ++j) {
+    const int s0 = S.segR[j], n = S.nR[j];
+    for (int p = tid; p < n; p += RF) {
+      const unsigned long long mine = S.poolR[s0 + p];
+      int r = 0;
+#pragma unroll 8
+      for (int q = 0; q < n; ++q) r += (S.poolR[s0 + q] < mine) ? 1 : 0;
+      S.u.m[r] = exp((double)cand_value(mine) - lse);
+    }
+    __syncthreads();
+    // thread tid scans ranks [tid*per, tid*per + per) after the masses of
+    // the ranks before them (their thread totals, in thread order)
+    const int per = (n + RF - 1) / RF;
+    const int r0 = tid * per, r1 = min(n, r0 + per);
+    double own_sum = 0.0;
+    for (int r = r0; r < r1; ++r) own_sum += S.u.m[r];
+    double x = own_sum;
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double t = __shfl_up(x, o, 64);
+      if (lane >= o) x += t;
+    }
+    if (lane == 63) S.red_d[w] = x;
+    __syncthreads();
+    double base = (double)S.massAboveR[j] * inv_total + (x - own_sum);
+    for (int i = 0; i < w; ++i) base += S.red_d[i];
+    __syncthreads();
+    int hit = n;
+    const double target = (double)S.rho[j];
+    for (int r = r0; r < r1; ++r) {
+      base += S.u.m[r];
+      if (base >= target) {
+        hit = r;
+        break;
+      }
+    }
+    hit = fast_block_min(hit, S);
+    if (tid == 0) krho_out[row * n_rho + j] = S.cntAboveR[j] + (hit < n ? hit + 1 : n);
+    __syncthreads();
+  }
+}
+
 struct CachePlan {
   int64_t Tb;
-  size_t zbytes, total;
+  int nVT;
+  size_t zbytes, o_flags, o_tmax, total;
 };
 
 static bool plan_cache(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho, CachePlan& p) {
@@ -649,8 +1132,12 @@ static bool plan_cache(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho
   if (tb < CC::BM) tb = CC::BM;
   if (tb > kd_round_up(T > 0 ? T : 1, CC::BM)) tb = kd_round_up(T > 0 ? T : 1, CC::BM);
   p.Tb = tb;
+  p.nVT = (int)kd_ceil_div(V, CC::BM);
+  // logit block, per-row fallback flags, per-(row, vocabulary tile) maxima
   p.zbytes = (size_t)tb * V * 4;
-  p.total = p.zbytes + 256;
+  p.o_flags = p.zbytes;
+  p.o_tmax = p.o_flags + (size_t)kd_round_up(tb * 4, 256);
+  p.total = p.o_tmax + (size_t)kd_round_up(tb * p.nVT * 4, 256);
   return true;
 }
 
@@ -661,12 +1148,20 @@ static kd_status check_rho(const float* rho_host, int32_t n_rho) {
   return KD_OK;
 }
 
+// Fast pass over all rows, then the exact pass over the rows it flagged
+// (every row when V is beyond the fast pass's packed counts).  `flags` holds
+// `rows` int32; tmax (optional) the rows' maxima in n_tmax parts each.
 static void launch_rows(const float* z, int64_t ldz, int64_t rows, int64_t V, int K, const float* rho, int n_rho,
-                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho, hipStream_t s) {
+                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho, int32_t* flags,
+                        const float* tmax, int n_tmax, hipStream_t s) {
   float r[RHO_MAX] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < n_rho; ++j) r[j] = rho[j];
-  KD_LAUNCH(k_topk_rows, dim3((unsigned)rows), dim3(RT), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
-                     r[4], r[5], r[6], r[7], idx, val, lse, m_q, k_rho);
+  const bool fast = V <= VFAST_MAX;
+  if (fast)
+    KD_LAUNCH(k_topk_rows, dim3((unsigned)rows), dim3(RF), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
+                       r[4], r[5], r[6], r[7], tmax, n_tmax, flags, idx, val, lse, m_q, k_rho);
+  KD_LAUNCH(k_topk_rows_exact, dim3((unsigned)rows), dim3(RT), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
+                     r[4], r[5], r[6], r[7], fast ? (const int32_t*)flags : nullptr, idx, val, lse, m_q, k_rho);
 }
 
 }  // namespace
@@ -695,12 +1190,13 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
   float* z = (float*)ws;
   for (int64_t t0 = 0; t0 < T; t0 += p.Tb) {
     const int64_t tb = (T - t0 < p.Tb) ? T - t0 : p.Tb;
-    const int nTT = (int)kd_ceil_div(tb, CC::BM), nVT = (int)kd_ceil_div(V, CC::BN);
+    const int nTT = (int)kd_ceil_div(tb, CC::BN), nVT = p.nVT;
     const int grid = (int)kd_round_up((int64_t)nTT * nVT, 8);
+    float* tmax = (float*)((char*)ws + p.o_tmax);
     KD_LAUNCH(k_cache_gemm, dim3(grid), dim3(CC::NT), CG_LDS, s, (const bf16_t*)g + t0 * d,
-                       (const bf16_t*)U, b, tb, d, V, nTT, nVT, z);
+                       (const bf16_t*)U, b, tb, d, V, nTT, nVT, z, tmax);
     launch_rows(z, V, tb, V, K, rho_host, n_rho, idx + t0 * K, val + t0 * K, lse + t0, m_q + t0,
-                n_rho ? k_rho + t0 * n_rho : nullptr, s);
+                n_rho ? k_rho + t0 * n_rho : nullptr, (int32_t*)((char*)ws + p.o_flags), tmax, nVT, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
   }
@@ -709,7 +1205,7 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
 
 extern "C" size_t kd_topk_rows_workspace(int64_t T, int64_t V, int32_t K, int32_t n_rho) {
   if (T < 0 || V <= 0 || K < 1 || K > KMAX || K > V || n_rho < 0 || n_rho > RHO_MAX) return 0;
-  return 256;
+  return (size_t)kd_round_up((T > 0 ? T : 1) * 4, 256);  // per-row fallback flags
 }
 
 extern "C" kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K, const float* rho_host,
@@ -721,9 +1217,10 @@ extern "C" kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t 
   if (st != KD_OK) return st;
   if (T == 0) return KD_OK;
   if (!z || !idx || !val || !lse || !m_q || (n_rho > 0 && !k_rho)) return kd_fail(KD_EINVAL, "null required pointer");
-  (void)ws;
-  (void)ws_bytes;
-  launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, (hipStream_t)stream);
+  const size_t need = (size_t)kd_round_up(T * 4, 256);
+  if (!ws || ws_bytes < need) return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+  launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, (int32_t*)ws, nullptr, 0,
+              (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
   return KD_OK;
