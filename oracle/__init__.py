@@ -27,6 +27,9 @@ Sources (cited by title and section, figure or equation):
 * "Sparse Teacher Support Cuts LLM Distillation Cost Without Losing
   Accuracy", definition of k_rho: the smallest k whose top-k teacher mass
   reaches rho.
+* The hard-label cross-entropy term that "The Gradient That Top-k
+  Distillation Never Computes" (abstract) trains with or without, added
+  with a weight to any of the four distillation losses.
 
 Every function is pinned by a CPU test (tests/test_oracle.py) against
 printed values, closed forms, library routines, finite differences or

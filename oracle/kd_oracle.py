@@ -110,8 +110,28 @@ def _support(idx_row: np.ndarray, tlp_row: np.ndarray):
     return np.asarray(idx_row)[keep].astype(np.int64), np.asarray(tlp_row, np.float64)[keep]
 
 
-def loss_rows_from_logits(z, idx, tlp, m_q, mode):
-    """Per-token (L, dz, lse, m_p) for logits z [T, V].  Returns arrays."""
+def _label_term(z: np.ndarray, y: int, lse: float, ce_weight: float):
+    """Hard-label cross-entropy term added to a distillation loss:
+    ce_weight * (lse - z_y), gradient ce_weight * (softmax(z) - e_y).
+
+    "The Gradient That Top-k Distillation Never Computes" (abstract) trains
+    the top-k student with and without the cross-entropy term on the data
+    token; the weight is not printed, so it is an argument here.  A label
+    y < 0 means the token has no label (no term).
+    """
+    if y < 0 or ce_weight == 0.0:
+        return 0.0, None
+    p = np.exp(z - lse)
+    g = ce_weight * p
+    g[y] -= ce_weight
+    return ce_weight * (lse - float(z[y])), g
+
+
+def loss_rows_from_logits(z, idx, tlp, m_q, mode, labels=None, ce_weight=0.0):
+    """Per-token (L, dz, lse, m_p) for logits z [T, V].  Returns arrays.
+
+    With labels [T] (int, -1 = none) and ce_weight, each labelled token also
+    carries the hard-label cross-entropy term of _label_term."""
     z = np.asarray(z, np.float64)
     T, V = z.shape
     L = np.zeros(T)
@@ -122,15 +142,21 @@ def loss_rows_from_logits(z, idx, tlp, m_q, mode):
     for t in range(T):
         S, tl = _support(idx[t], tlp[t])
         L[t], dz[t], lse[t], m_p[t] = _loss_row(z[t], S, tl, float(mq[t]), mode)
+        if labels is not None:
+            Lc, gc = _label_term(z[t], int(labels[t]), lse[t], float(ce_weight))
+            if gc is not None:
+                L[t] += Lc
+                dz[t] += gc
     return L, dz, lse, m_p
 
 
-def loss_fwd_bwd(h, W, idx, tlp, m_q, mode, scale=None, block=256):
+def loss_fwd_bwd(h, W, idx, tlp, m_q, mode, scale=None, block=256, labels=None, ce_weight=0.0):
     """Fused LM head + top-K KD loss, forward and backward, as dense math.
 
     loss = scale * sum_t L_t; dh = scale * dz W; dW = scale * dz^T h,
     with z = h W^T in float64.  The mean over tokens (scale = 1/T) is the
-    default reduction; the pages only define per-token losses.
+    default reduction; the pages only define per-token losses.  labels and
+    ce_weight add the hard-label cross-entropy term (_label_term).
 
     Returns a dict with loss, loss_tok [T], lse [T], m_p [T], dh [T, d],
     dW [V, d].
@@ -153,7 +179,8 @@ def loss_fwd_bwd(h, W, idx, tlp, m_q, mode, scale=None, block=256):
         t1 = min(T, t0 + block)
         z = h[t0:t1] @ W.T
         Lb, dz, lb, mb = loss_rows_from_logits(
-            z, idx[t0:t1], tlp[t0:t1], None if mq is None else mq[t0:t1], mode)
+            z, idx[t0:t1], tlp[t0:t1], None if mq is None else mq[t0:t1], mode,
+            None if labels is None else labels[t0:t1], ce_weight)
         L[t0:t1], lse[t0:t1], m_p[t0:t1] = Lb, lb, mb
         dh[t0:t1] = scale * (dz @ W)
         dW += scale * (dz.T @ h[t0:t1])

@@ -389,3 +389,75 @@ def test_cache_build_matches_head_reconstruction():
     np.testing.assert_allclose(lse, scipy.special.logsumexp(z, axis=1), atol=1e-12)
     tl = oracle.teacher_logp(val, lse)
     np.testing.assert_allclose(np.exp(tl).sum(axis=1) + m_q, 1.0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Hard-label cross-entropy term ("The Gradient That Top-k Distillation Never
+# Computes", abstract: training with and without the CE term)
+# --------------------------------------------------------------------------
+
+def _labels(T, V, seed):
+    r = np.random.default_rng(seed)
+    y = r.integers(0, V, size=T)
+    y[::3] = -1  # unlabelled tokens
+    return y
+
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_label_term_against_torch_cross_entropy(mode):
+    """The added term and its gradient equal torch's cross_entropy on the
+    logits (fp64 autograd), on top of the distillation loss of the mode."""
+    h, W, idx, tlp, m_q = _problem(31 + mode, T=6, d=5, V=30, K=6)
+    y = _labels(6, 30, 7 + mode)
+    y[1] = idx[1, 0]  # a label inside the retained set
+    lam = 0.37
+    z = oracle.student_logits(h, W)
+    L0, dz0, _, _ = oracle.loss_rows_from_logits(z, idx, tlp, m_q, mode)
+    L1, dz1, _, _ = oracle.loss_rows_from_logits(z, idx, tlp, m_q, mode, labels=y, ce_weight=lam)
+    for t in range(6):
+        zt = torch.tensor(z[t], dtype=torch.float64, requires_grad=True)
+        if y[t] >= 0:
+            ce = torch.nn.functional.cross_entropy(zt[None], torch.tensor([int(y[t])]))
+            (lam * ce).backward()
+            extra, g = float(lam * ce.detach()), zt.grad.numpy()
+        else:
+            extra, g = 0.0, np.zeros(30)
+        assert abs((L1[t] - L0[t]) - extra) < 1e-12
+        np.testing.assert_allclose(dz1[t] - dz0[t], g, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", [RENORM, TAIL])
+def test_label_term_finite_differences(mode):
+    h, W, idx, tlp, m_q = _problem(41 + mode, consistent=True)
+    y = _labels(h.shape[0], W.shape[0], 3)
+    r = oracle.loss_fwd_bwd(h, W, idx, tlp, m_q, mode, scale=0.6, labels=y, ce_weight=0.8)
+
+    def f(hh, WW):
+        return oracle.loss_fwd_bwd(hh, WW, idx, tlp, m_q, mode, scale=0.6, labels=y, ce_weight=0.8)["loss"]
+
+    eps = 1e-6
+    for name, X, G in (("h", h, r["dh"]), ("W", W, r["dW"])):
+        num = np.zeros_like(X)
+        for i in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[i] += eps
+            Xm[i] -= eps
+            num[i] = (f(Xp, W) - f(Xm, W)) / (2 * eps) if name == "h" else \
+                     (f(h, Xp) - f(h, Xm)) / (2 * eps)
+        err = np.linalg.norm(num - G) / max(np.linalg.norm(G), 1e-300)
+        assert err < 1e-6, (name, err)
+
+
+def test_label_term_alone_is_cross_entropy():
+    """With every teacher entry padded out (empty support) the full-mode
+    loss is zero and only the label term remains: the mean cross-entropy."""
+    r = np.random.default_rng(5)
+    T, d, V = 7, 4, 25
+    h, W = r.standard_normal((T, d)), r.standard_normal((V, d))
+    idx = np.full((T, 3), -1)
+    tlp = np.zeros((T, 3))
+    y = r.integers(0, V, size=T)
+    out = oracle.loss_fwd_bwd(h, W, idx, tlp, None, FULL, labels=y, ce_weight=1.0)
+    zt = torch.tensor(h @ W.T)
+    ce = float(torch.nn.functional.cross_entropy(zt, torch.tensor(y)))
+    assert abs(out["loss"] - ce) < 1e-12
