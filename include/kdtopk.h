@@ -110,6 +110,31 @@ kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t
                                float* dh, float* dW,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace kd_topk_loss_fwd_bwd_ce needs (0 for invalid
+ * sizes).  A nonzero ce_weight sends every mode through the dense backward. */
+size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk,
+                                 float ce_weight);
+
+/* kd_topk_loss_fwd_bwd plus a hard-label cross-entropy term [TG abstract:
+ * the top-k student trained with and without the cross-entropy term]:
+ *   L_t += ce_weight * (logsumexp(z) - z_y),  dL_t/dz += ce_weight * (p - e_y)
+ * for each token with labels[t] = y >= 0.
+ *
+ * In:  labels    [T] int32  data-token label per token, -1 for none; labels
+ *                           >= V are rejected on the device (NaN loss).  May be
+ *                           NULL when ce_weight == 0.
+ *      ce_weight finite, >= 0; 0 gives exactly kd_topk_loss_fwd_bwd.
+ * All other arguments, outputs and errors as kd_topk_loss_fwd_bwd; loss_tok
+ * includes the term.  The workspace size comes from kd_topk_loss_ce_workspace. */
+kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                  const float* teacher_logp, const float* m_q,
+                                  const int32_t* labels, float ce_weight,
+                                  int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                                  int32_t chunk, float scale,
+                                  float* loss, float* loss_tok, float* lse, float* m_p,
+                                  float* dh, float* dW,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace kd_topk_cache_build needs.  Returns 0 for
  * invalid sizes. */
 size_t kd_topk_cache_build_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho);

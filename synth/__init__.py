@@ -36,6 +36,7 @@ STREAM_G = 4
 STREAM_U = 5
 STREAM_B = 6
 STREAM_TIES = 7
+STREAM_LABELS = 8
 
 # rows per independently seeded block
 BLOCK = 256
@@ -143,3 +144,13 @@ def tie_heavy_logits(rows: int, V: int, seed: int = 0, step: float = 0.25,
     r = _rng(seed, STREAM_TIES, 0)
     x = np.round(r.uniform(-span, span, size=(rows, V)) / step) * step
     return x.astype(np.float32)
+
+
+def token_labels(T: int, V: int, seed: int = 0, unlabelled_every: int = 5) -> np.ndarray:
+    """int32 data-token labels uniform in [0, V); every unlabelled_every-th
+    token has none (-1)."""
+    r = _rng(seed, STREAM_LABELS, 0)
+    y = r.integers(0, V, size=T).astype(np.int32)
+    if unlabelled_every > 0:
+        y[::unlabelled_every] = -1
+    return y

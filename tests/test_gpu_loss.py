@@ -184,3 +184,68 @@ def test_argument_errors():
         kd.loss_fwd_bwd(h[:, :32].contiguous(), W[:, :32].contiguous(), idx, tlp, None, mode=kd.RENORM)
     with pytest.raises(ValueError):
         kd.loss_fwd_bwd(h.cpu(), W, idx, tlp, None, mode=kd.RENORM)
+
+
+# --------------------------------------------------------------------------
+# Hard-label cross-entropy term (kd_topk_loss_fwd_bwd_ce)
+# --------------------------------------------------------------------------
+
+def _run_ce(h, W, idx, tlp, mq, mode, chunk, y, lam):
+    out = kd.loss_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV),
+                          torch.from_numpy(mq).to(DEV) if mq is not None else None, mode=mode, chunk=chunk,
+                          labels=torch.from_numpy(y).to(DEV), ce_weight=lam)
+    torch.cuda.synchronize()
+    return {k: getattr(out, k).cpu().numpy() for k in out._fields}
+
+
+@pytest.mark.parametrize("mode", [kd.RENORM, kd.TAIL, kd.FULL, kd.REVERSE])
+@pytest.mark.parametrize("shape", ["tiny", "ragged"])
+def test_label_term_all_modes(mode, shape):
+    """Distillation loss + 0.5 x cross-entropy on data-token labels: labels
+    outside S, inside S (first cached index) and absent (-1); the sparse modes
+    take the dense backward because of the label term."""
+    if shape == "tiny":
+        T, d, V, K, chunk, seed = 64, 64, 1024, 8, 8192, 0
+    else:
+        T, d, V, K, chunk, seed = 300, 128, 2500, 13, 700, 3
+    h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=seed)
+    y = synth.token_labels(T, V, seed=seed)
+    y[1::7] = idx[1::7, 0]
+    g = _run_ce(h, W, idx, tlp, mq, mode, chunk, y, 0.5)
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode, labels=y, ce_weight=0.5)
+    e = _compare(g, r, f"ce {shape} mode={mode}")
+    print(f"ce {shape} mode={mode} loss={float(g['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
+def test_label_term_zero_weight_is_plain_loss():
+    T, d, V, K = 64, 64, 1024, 8
+    h, W, idx, tlp, mq = _case(T, d, V, K, kd.TAIL, seed=2)
+    y = synth.token_labels(T, V, seed=2)
+    a = _run(h, W, idx, tlp, mq, kd.TAIL, chunk=8192)
+    # the _ce entry point itself with ce_weight = 0 (the binding would take the plain one)
+    L = kd.lib()
+    hd, Wd = h.to(DEV), W.to(DEV)
+    idd, tld, mqd, yd = (torch.from_numpy(x).to(DEV) for x in (idx, tlp, mq, y))
+    f32 = dict(dtype=torch.float32, device=DEV)
+    o = kd.LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
+                   torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
+    nb = L.kd_topk_loss_ce_workspace(T, d, V, K, kd.TAIL, 8192, 0.0)
+    assert nb == L.kd_topk_loss_workspace(T, d, V, K, kd.TAIL, 8192)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    st = L.kd_topk_loss_fwd_bwd_ce(kd._ptr(hd), kd._ptr(Wd), kd._ptr(idd), kd._ptr(tld), kd._ptr(mqd), kd._ptr(yd),
+                                   0.0, T, d, V, K, kd.TAIL, 8192, 1.0 / T, kd._ptr(o.loss), kd._ptr(o.loss_tok),
+                                   kd._ptr(o.lse), kd._ptr(o.m_p), kd._ptr(o.dh), kd._ptr(o.dW), kd._ptr(ws), nb,
+                                   kd._stream(torch.device(DEV)))
+    assert st == 0
+    torch.cuda.synchronize()
+    for k in a:
+        np.testing.assert_array_equal(a[k], getattr(o, k).cpu().numpy(), err_msg=k)
+
+
+def test_label_out_of_range_gives_nan():
+    T, d, V, K = 64, 64, 1024, 8
+    h, W, idx, tlp, mq = _case(T, d, V, K, kd.TAIL, seed=4)
+    y = synth.token_labels(T, V, seed=4)
+    y[5] = V
+    g = _run_ce(h, W, idx, tlp, mq, kd.TAIL, 8192, y, 1.0)
+    assert np.isnan(g["loss"])

@@ -31,6 +31,9 @@ _SIGS = {
     "kd_topk_loss_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
     "kd_topk_loss_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_topk_loss_ce_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _f32]),
+    "kd_topk_loss_fwd_bwd_ce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, _i32, _i32,
+                                               _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -99,15 +102,20 @@ class LossOut(NamedTuple):
     m_p: torch.Tensor       # [T] fp32
 
 
-def loss_workspace_bytes(T: int, d: int, V: int, K: int, mode: int, chunk: int) -> int:
+def loss_workspace_bytes(T: int, d: int, V: int, K: int, mode: int, chunk: int, ce_weight: float = 0.0) -> int:
+    if ce_weight:
+        return int(lib().kd_topk_loss_ce_workspace(T, d, V, K, mode, chunk, ce_weight))
     return int(lib().kd_topk_loss_workspace(T, d, V, K, mode, chunk))
 
 
 def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_logp: torch.Tensor,
                  m_q: Optional[torch.Tensor] = None, mode: int = TAIL, chunk: int = 8192,
                  scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-                 out: Optional[LossOut] = None) -> LossOut:
-    """Fused LM head + top-K KD loss, forward and backward (kd_topk_loss_fwd_bwd)."""
+                 out: Optional[LossOut] = None, labels: Optional[torch.Tensor] = None,
+                 ce_weight: float = 0.0) -> LossOut:
+    """Fused LM head + top-K KD loss, forward and backward (kd_topk_loss_fwd_bwd;
+    with labels [T] int32 (-1 = none) and ce_weight > 0, kd_topk_loss_fwd_bwd_ce
+    adds the weighted hard-label cross-entropy term)."""
     if isinstance(mode, str):
         mode = MODE_BY_NAME[mode]
     dev = h.device
@@ -120,13 +128,17 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
     _need(teacher_logp, "teacher_logp", torch.float32, (T, K), dev)
     if m_q is not None:
         _need(m_q, "m_q", torch.float32, (T,), dev)
+    if labels is not None:
+        _need(labels, "labels", torch.int32, (T,), dev)
+    ce = ce_weight != 0.0
     if scale is None:
         scale = 1.0 / max(T, 1)
     L = lib()
-    ws_bytes = int(L.kd_topk_loss_workspace(T, d, V, K, mode, chunk))
+    ws_bytes = loss_workspace_bytes(T, d, V, K, mode, chunk, ce_weight)
     if ws_bytes == 0:
-        _check(L.kd_topk_loss_fwd_bwd(None, None, None, None, None, T, d, V, K, mode, chunk, scale,
-                                      None, None, None, None, None, None, None, 0, None), "kd_topk_loss_fwd_bwd")
+        _check(L.kd_topk_loss_fwd_bwd_ce(None, None, None, None, None, None, ce_weight, T, d, V, K, mode, chunk,
+                                         scale, None, None, None, None, None, None, None, 0, None),
+               "kd_topk_loss_fwd_bwd_ce")
     with torch.cuda.device(dev):
         if workspace is None or workspace.numel() < ws_bytes:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -134,11 +146,19 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
             f32 = dict(dtype=torch.float32, device=dev)
             out = LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
                           torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
-        st = L.kd_topk_loss_fwd_bwd(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
-                                    T, d, V, K, mode, chunk, scale,
-                                    _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
-                                    _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(), _stream(dev))
-    _check(st, "kd_topk_loss_fwd_bwd")
+        if ce:
+            st = L.kd_topk_loss_fwd_bwd_ce(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
+                                           _ptr(labels), ce_weight, T, d, V, K, mode, chunk, scale,
+                                           _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
+                                           _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
+                                           _stream(dev))
+        else:
+            st = L.kd_topk_loss_fwd_bwd(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
+                                        T, d, V, K, mode, chunk, scale,
+                                        _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
+                                        _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
+                                        _stream(dev))
+    _check(st, "kd_topk_loss_fwd_bwd_ce" if ce else "kd_topk_loss_fwd_bwd")
     return out
 
 

@@ -38,7 +38,7 @@ constexpr int KMAX = 1024;
 constexpr int SENT = 0x7fffffff;  // sorted-index sentinel (padding)
 
 // Per-token scalars kept in the workspace (float, stride TOKF).
-enum { TK_LSE = 0, TK_ALPHA = 1, TK_L = 2, TK_MP = 3, TK_Q = 4, TK_LSEQ = 5, TK_NV = 6, TOKF = 8 };
+enum { TK_LSE = 0, TK_ALPHA = 1, TK_L = 2, TK_MP = 3, TK_Q = 4, TK_LSEQ = 5, TK_NV = 6, TK_ZY = 7, TOKF = 8 };
 
 // ---------------------------------------------------------------------------
 // Tile ordering: workgroup id -> (m tile, n tile).  Workgroups are handed to
@@ -305,14 +305,51 @@ __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, 
 }
 
 // ---------------------------------------------------------------------------
+// Label logit for the hard-label cross-entropy term: z_y = h_t . W_y in fp32
+// (products of bf16 values are exact), one wavefront per token.  Labels >= V
+// raise the error flag; y < 0 means no label.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_label_logit(const bf16_t* __restrict__ h, const bf16_t* __restrict__ W,
+                                                     const int32_t* __restrict__ labels, int64_t T, int64_t d,
+                                                     int64_t V, float* __restrict__ tok, int32_t* __restrict__ err) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int y = labels[t];
+  float acc = 0.f;
+  if (y >= 0 && y < V) {
+    const bf16_t* hr = h + t * d;
+    const bf16_t* wr = W + (int64_t)y * d;
+    for (int64_t j = (int64_t)lane * 8; j < d; j += 64 * 8) {
+      const u32x4 a = *(const u32x4*)(hr + j), b = *(const u32x4*)(wr + j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+        acc = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
+      }
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    tok[t * TOKF + TK_ZY] = acc;
+    if (y >= V) atomicOr(err, 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine: one wavefront per token.  All per-token math in fp64.
 // ---------------------------------------------------------------------------
+// With labels (ce_weight != 0): L += ce_weight (lse - z_y), alpha += ce_weight,
+// r_y -= ce_weight when y is in S; otherwise ylab[t] = y for the pass-2 fixup
+// (-1 when there is none).
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int64_t Tp, int mode, float scale,
                                                  const float2* __restrict__ part, const float* __restrict__ zS,
                                                  const int32_t* __restrict__ sidx, const float* __restrict__ stlp,
-                                                 const float* __restrict__ m_q, float* __restrict__ tok,
-                                                 float* __restrict__ coef, float* __restrict__ loss_tok,
-                                                 float* __restrict__ lse_out, float* __restrict__ mp_out) {
+                                                 const float* __restrict__ m_q, const int32_t* __restrict__ labels,
+                                                 float ce_weight, int64_t V, float* __restrict__ tok,
+                                                 float* __restrict__ coef, int32_t* __restrict__ ylab,
+                                                 float* __restrict__ loss_tok, float* __restrict__ lse_out,
+                                                 float* __restrict__ mp_out) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -368,10 +405,19 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
   L = wave_sum_f64(L);
   if (mode == KD_TAIL && mq > 0.0) L += mq * (log(mq) - log(mps));
   if (mode == KD_FULL) L += Q * lse;
+  const double Lkd = L;  // the distillation term alone (REVERSE's gradient uses it)
 
   double alpha = 0.0;
   if (mode == KD_TAIL) alpha = Q + mq - ratio;
   if (mode == KD_FULL) alpha = Q;
+  const int y = (labels != nullptr && ce_weight != 0.f) ? labels[t] : -1;
+  const bool has_y = y >= 0 && y < V;
+  const double lam = has_y ? (double)ce_weight : 0.0;
+  if (has_y) {
+    L += lam * (lse - (double)tk[TK_ZY]);
+    alpha += lam;
+  }
+  bool y_in_s = false;
   for (int k = lane; k < K; k += 64) {
     double r = 0.0;
     if (k < nv) {
@@ -385,11 +431,17 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
         r = -q;
       } else {
         const double lph = z - lseS, lqh = tl - lseq;
-        r = exp(lph) * (lph - lqh - L);
+        r = exp(lph) * (lph - lqh - Lkd);
+      }
+      if (has_y && sidx[t * K + k] == y) {
+        r -= lam;
+        y_in_s = true;
       }
     }
     coef[t * K + k] = (float)(scale * r);
   }
+  y_in_s = __ballot(y_in_s) != 0ull;
+  if (ylab != nullptr && lane == 0) ylab[t] = (has_y && !y_in_s) ? y : -1;
   if (lane == 0) {
     float* tw = tok + t * TOKF;
     tw[TK_LSE] = (float)lse;
@@ -470,7 +522,8 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
                                                 const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
-                                                const float* __restrict__ coef, bf16_t* __restrict__ dz, int ct, int tt, bf16_t* lds) {
+                                                const float* __restrict__ coef, const int32_t* __restrict__ ylab,
+                                                float lam_s, bf16_t* __restrict__ dz, int ct, int tt, bf16_t* lds) {
   const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
   const int vt = (int)(m0 / VT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -535,6 +588,16 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
       vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
     }
   }
+  // label outside S (cross-entropy term): dz = alpha * exp(z_y - lse) - ce_weight * scale
+  if (ylab != nullptr && ts < T) {
+    const int y = ylab[ts];
+    if (y >= m0 && y < vend) {
+      const float* tk = tok + ts * TOKF;
+      const float val = tk[TK_ALPHA] * __expf(tk[TK_ZY] - tk[TK_LSE]) - lam_s;
+      const int vl = y - (int)m0;
+      *(bf16_t*)(E + tid * (VT * 2) + (((vl >> 3) ^ zdz_swz(tid)) << 4) + (vl & 7) * 2) = f32_to_bf16(val);
+    }
+  }
   __syncthreads();
 
   // token rows: 32 threads per 512-byte row
@@ -552,14 +615,15 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
                                                 const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
-                                                const float* __restrict__ coef, bf16_t* __restrict__ dz) {
+                                                const float* __restrict__ coef, const int32_t* __restrict__ ylab,
+                                                float lam_s, bf16_t* __restrict__ dz) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
   if (c0 + (int64_t)(ct + 1) * VT > c1)
-    zdz_tile<true>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, dz, ct, tt, lds);
+    zdz_tile<true>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, ylab, lam_s, dz, ct, tt, lds);
   else
-    zdz_tile<false>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, dz, ct, tt, lds);
+    zdz_tile<false>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, ylab, lam_s, dz, ct, tt, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -786,7 +850,8 @@ namespace {
 struct LossPlan {
   int64_t T, d, V, Tp, Cp, C;
   int K, Kp2, mode, nVT, nTT, nDT, nchunks;
-  size_t o_sidx, o_stlp, o_zS, o_coef, o_tok, o_starts, o_part, o_err;
+  bool ce, dense;                                    // label term; dense backward
+  size_t o_sidx, o_stlp, o_zS, o_coef, o_tok, o_starts, o_part, o_err, o_ylab;
   size_t o_dz;                                       // dense modes
   size_t o_cnt, o_off, o_fill, o_entt, o_entr, o_seg; // sparse modes
   size_t total;
@@ -794,7 +859,10 @@ struct LossPlan {
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, LossPlan& p) {
+// ce: a hard-label cross-entropy term is present (its dense gradient makes
+// every mode take the dense backward).
+static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, bool ce,
+                      LossPlan& p) {
   if (T < 0 || d <= 0 || V <= 0 || K < 1 || K > KMAX || K > V || d % 64 != 0 || d > 16384 || chunk <= 0) return false;
   if (mode < KD_RENORM || mode > KD_REVERSE) return false;
   if (V > (int64_t)1 << 30 || T > (int64_t)1 << 26) return false;
@@ -803,6 +871,8 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.V = V;
   p.K = K;
   p.mode = mode;
+  p.ce = ce;
+  p.dense = (mode == KD_TAIL || mode == KD_FULL || ce);
   p.Kp2 = 1;
   while (p.Kp2 < K) p.Kp2 <<= 1;
   p.Tp = kd_round_up(T > 0 ? T : 1, TT);
@@ -828,9 +898,13 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.o_starts = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
   p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_err = o; o = align_up(o + 4);
+  p.o_ylab = 0;
+  if (ce) {
+    p.o_ylab = o; o = align_up(o + (size_t)(T > 0 ? T : 1) * 4);
+  }
   p.o_dz = 0;
   p.o_cnt = p.o_off = p.o_fill = p.o_entt = p.o_entr = p.o_seg = 0;
-  if (mode == KD_TAIL || mode == KD_FULL) {
+  if (p.dense) {
     p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
   } else {
     p.o_cnt = o; o = align_up(o + (size_t)(V + 1) * 4);
@@ -851,7 +925,14 @@ static T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
 
 extern "C" size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk) {
   LossPlan p;
-  if (!plan_loss(T, d, V, K, mode, chunk, p)) return 0;
+  if (!plan_loss(T, d, V, K, mode, chunk, false, p)) return 0;
+  return p.total;
+}
+
+extern "C" size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk,
+                                            float ce_weight) {
+  LossPlan p;
+  if (!plan_loss(T, d, V, K, mode, chunk, ce_weight != 0.f, p)) return 0;
   return p.total;
 }
 
@@ -861,14 +942,19 @@ extern "C" size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_
     if (e_ != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e_)); \
   } while (0)
 
-extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
-                                          const float* teacher_logp, const float* m_q, int64_t T, int64_t d,
-                                          int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale,
-                                          float* loss, float* loss_tok, float* lse, float* m_p, float* dh,
-                                          float* dW, void* ws, size_t ws_bytes, void* stream) {
+extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                             const float* teacher_logp, const float* m_q, const int32_t* labels,
+                                             float ce_weight, int64_t T, int64_t d, int64_t V, int32_t K,
+                                             int32_t mode, int32_t chunk, float scale, float* loss,
+                                             float* loss_tok, float* lse, float* m_p, float* dh, float* dW,
+                                             void* ws, size_t ws_bytes, void* stream) {
   LossPlan p;
   if (mode < KD_RENORM || mode > KD_REVERSE) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
-  if (!plan_loss(T, d, V, K, mode, chunk, p))
+  if (!(ce_weight == ce_weight) || ce_weight < 0.f || ce_weight > 3.4e38f)
+    return kd_fail(KD_EINVAL, "ce_weight must be finite and >= 0 (got %g)", (double)ce_weight);
+  const bool ce = ce_weight != 0.f;
+  if (ce && T > 0 && !labels) return kd_fail(KD_EINVAL, "ce_weight != 0 needs labels");
+  if (!plan_loss(T, d, V, K, mode, chunk, ce, p))
     return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0, and chunk*d, T*d, T*chunk bf16 each < 4 GiB)",
                    (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
   if (!loss || !dW || !W) return kd_fail(KD_EINVAL, "null required pointer (loss, W, dW)");
@@ -905,13 +991,20 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   KD_LAUNCH(k_pass1, dim3(g1), dim3(TC::NT), P1_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
                      p.nVT, p.nTT, p.Tp, sidx, starts, zS, part);
   KD_LAUNCH_CHECK();
+  int32_t* ylab = ce ? at<int32_t>(ws, p.o_ylab) : nullptr;
+  if (ce) {
+    KD_LAUNCH(k_label_logit, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, (const bf16_t*)h, (const bf16_t*)W,
+                       labels, T, d, V, tok, err);
+    KD_LAUNCH_CHECK();
+  }
   KD_LAUNCH(k_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, (int)K, p.nVT, p.Tp, (int)mode,
-                     scale, part, zS, sidx, stlp, m_q, tok, coef, loss_tok, lse, m_p);
+                     scale, part, zS, sidx, stlp, m_q, ce ? labels : nullptr, ce_weight, V, tok, coef, ylab,
+                     loss_tok, lse, m_p);
   KD_LAUNCH_CHECK();
   KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, tok, err, loss);
   KD_LAUNCH_CHECK();
 
-  if (mode == KD_TAIL || mode == KD_FULL) {
+  if (p.dense) {
     bf16_t* dz = at<bf16_t>(ws, p.o_dz);
     for (int c = 0; c < p.nchunks; ++c) {
       const int64_t c0 = (int64_t)c * p.C;
@@ -920,7 +1013,8 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
       const int nCT = (int)kd_ceil_div(clen, VT);
       const int gz = grid_of(nCT * p.nTT);
       KD_LAUNCH(k_zdz, dim3(gz), dim3(TC::NT), ZDZ_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
-                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, dz);
+                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, ylab,
+                         ce_weight * scale, dz);
       KD_LAUNCH_CHECK();
       const int kdh = (int)kd_round_up(clen, 64);
       const int gdh = grid_of(p.nTT * p.nDT);
@@ -951,4 +1045,13 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
     KD_LAUNCH_CHECK();
   }
   return KD_OK;
+}
+
+extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                          const float* teacher_logp, const float* m_q, int64_t T, int64_t d,
+                                          int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale,
+                                          float* loss, float* loss_tok, float* lse, float* m_p, float* dh,
+                                          float* dW, void* ws, size_t ws_bytes, void* stream) {
+  return kd_topk_loss_fwd_bwd_ce(h, W, idx, teacher_logp, m_q, nullptr, 0.f, T, d, V, K, mode, chunk, scale, loss,
+                                 loss_tok, lse, m_p, dh, dW, ws, ws_bytes, stream);
 }
