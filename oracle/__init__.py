@@ -27,6 +27,9 @@ Sources (cited by title and section, figure or equation):
 * "Sparse Teacher Support Cuts LLM Distillation Cost Without Losing
   Accuracy", definition of k_rho: the smallest k whose top-k teacher mass
   reaches rho.
+* "The Gradient That Top-k Distillation Never Computes", Figure 3 (bottom):
+  the hidden-state teacher cache, whose head reconstruction gives the exact
+  full-vocabulary KL.
 * The hard-label cross-entropy term that "The Gradient That Top-k
   Distillation Never Computes" (abstract) trains with or without, added
   with a weight to any of the four distillation losses.
@@ -38,5 +41,5 @@ brute force; none is "parity unpinned".
 from .kd_oracle import (  # noqa: F401
     RENORM, TAIL, FULL, REVERSE, MODES, MODE_NAMES,
     logsumexp, student_logits, loss_rows_from_logits, loss_fwd_bwd,
-    topk_row, cache_from_logits, cache_build, teacher_logp, adaptive_k_row,
+    topk_row, cache_from_logits, cache_build, teacher_logp, adaptive_k_row, kl_hidden_fwd_bwd,
 )

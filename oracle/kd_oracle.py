@@ -278,3 +278,47 @@ def cache_build(g, U, b, K, rho=(), block=256):
             z = z + np.asarray(b, np.float64)[None, :]
         outs.append(cache_from_logits(z, K, rho))
     return tuple(np.concatenate([o[i] for o in outs], axis=0) for i in range(5))
+
+
+def kl_hidden_fwd_bwd(h, W, g, U, b=None, scale=None, block=256):
+    """Exact full-vocabulary KL(q || p) with the teacher rebuilt from a cached
+    hidden state: q = softmax(U g + b), p = softmax(W h).
+
+    "The Gradient That Top-k Distillation Never Computes", Figure 3 (bottom):
+    caching the teacher's final hidden state g instead of its top-k logits
+    reconstructs the full teacher distribution exactly at 2dV FLOP per
+    token.  Per token L = sum_v q_v (log q_v - log p_v), dL/dz = p - q;
+    loss = scale * sum_t L (default scale 1/T), dh = scale * dz W,
+    dW = scale * dz^T h.  Returns a dict with loss, loss_tok, lse (student),
+    lse_t (teacher), dh, dW.
+    """
+    h = np.asarray(h, np.float64)
+    W = np.asarray(W, np.float64)
+    g = np.asarray(g, np.float64)
+    U = np.asarray(U, np.float64)
+    T, d = h.shape
+    V = W.shape[0]
+    if scale is None:
+        scale = 1.0 / max(T, 1)
+    L = np.zeros(T)
+    lse = np.zeros(T)
+    lse_t = np.zeros(T)
+    dh = np.zeros((T, d))
+    dW = np.zeros((V, d))
+    for t0 in range(0, T, block):
+        t1 = min(T, t0 + block)
+        z = h[t0:t1] @ W.T
+        zt = g[t0:t1] @ U.T
+        if b is not None:
+            zt = zt + np.asarray(b, np.float64)[None, :]
+        for r in range(t1 - t0):
+            lse[t0 + r] = logsumexp(z[r])
+            lse_t[t0 + r] = logsumexp(zt[r])
+        logp = z - lse[t0:t1, None]
+        logq = zt - lse_t[t0:t1, None]
+        q = np.exp(logq)
+        L[t0:t1] = np.sum(q * (logq - logp), axis=1)
+        dz = np.exp(logp) - q
+        dh[t0:t1] = scale * (dz @ W)
+        dW += scale * (dz.T @ h[t0:t1])
+    return {"loss": scale * float(np.sum(L)), "loss_tok": L, "lse": lse, "lse_t": lse_t, "dh": dh, "dW": dW}

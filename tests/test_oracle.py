@@ -461,3 +461,69 @@ def test_label_term_alone_is_cross_entropy():
     zt = torch.tensor(h @ W.T)
     ce = float(torch.nn.functional.cross_entropy(zt, torch.tensor(y)))
     assert abs(out["loss"] - ce) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Exact full-vocabulary KL from a hidden-state teacher cache ("The Gradient
+# That Top-k Distillation Never Computes", Figure 3 bottom)
+# --------------------------------------------------------------------------
+
+def _hidden_problem(seed, T=5, d=6, dt=7, V=33):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((T, d)), r.standard_normal((V, d)) / np.sqrt(d),
+            r.standard_normal((T, dt)), r.standard_normal((V, dt)) / np.sqrt(dt), 0.3 * r.standard_normal(V))
+
+
+def test_kl_hidden_against_torch_kl_div():
+    h, W, g, U, b = _hidden_problem(1)
+    out = oracle.kl_hidden_fwd_bwd(h, W, g, U, b, scale=1.0)
+    z = torch.tensor(h @ W.T, requires_grad=True)
+    zt = torch.tensor(g @ U.T + b[None, :])
+    kl = torch.nn.functional.kl_div(torch.log_softmax(z, 1), torch.log_softmax(zt, 1), log_target=True,
+                                    reduction="none").sum(1)
+    kl.sum().backward()
+    np.testing.assert_allclose(out["loss_tok"], kl.detach().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out["dh"], z.grad.numpy() @ W, atol=1e-13)
+    np.testing.assert_allclose(out["dW"], z.grad.numpy().T @ h, atol=1e-13)
+    np.testing.assert_allclose(out["lse_t"], scipy.special.logsumexp(g @ U.T + b[None, :], axis=1), rtol=1e-14)
+
+
+def test_kl_hidden_finite_differences():
+    h, W, g, U, b = _hidden_problem(2, T=3, d=4, dt=5, V=11)
+    out = oracle.kl_hidden_fwd_bwd(h, W, g, U, b, scale=0.5)
+
+    def f(hh, WW):
+        return oracle.kl_hidden_fwd_bwd(hh, WW, g, U, b, scale=0.5)["loss"]
+
+    eps = 1e-6
+    for name, X, G in (("h", h, out["dh"]), ("W", W, out["dW"])):
+        num = np.zeros_like(X)
+        for i in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[i] += eps
+            Xm[i] -= eps
+            num[i] = (f(Xp, W) - f(Xm, W)) / (2 * eps) if name == "h" else (f(h, Xp) - f(h, Xm)) / (2 * eps)
+        assert np.linalg.norm(num - G) / np.linalg.norm(G) < 1e-6, name
+
+
+def test_kl_hidden_self_distillation_is_zero():
+    """Teacher = student (U = W, g = h, no bias): KL and every gradient vanish."""
+    h, W, _, _, _ = _hidden_problem(3)
+    out = oracle.kl_hidden_fwd_bwd(h, W, h, W, None)
+    assert abs(out["loss"]) < 1e-14
+    assert np.abs(out["dh"]).max() < 1e-14 and np.abs(out["dW"]).max() < 1e-14
+
+
+def test_kl_hidden_equals_cached_full_support():
+    """A top-K cache that keeps every index (K = V) of the same teacher gives
+    the same loss and gradients through the full-vocabulary mode."""
+    h, W, g, U, b = _hidden_problem(4)
+    out = oracle.kl_hidden_fwd_bwd(h, W, g, U, b)
+    zt = g @ U.T + b[None, :]
+    V = zt.shape[1]
+    idx = np.tile(np.arange(V), (zt.shape[0], 1))
+    tlp = zt - scipy.special.logsumexp(zt, axis=1)[:, None]
+    ref = oracle.loss_fwd_bwd(h, W, idx, tlp, None, FULL)
+    assert abs(out["loss"] - ref["loss"]) < 1e-12
+    np.testing.assert_allclose(out["dh"], ref["dh"], atol=1e-13)
+    np.testing.assert_allclose(out["dW"], ref["dW"], atol=1e-13)
