@@ -135,6 +135,35 @@ kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int3
                                   float* dh, float* dW,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace kd_kl_hidden_fwd_bwd needs (0 for invalid sizes).
+ * Linear in T for fixed (d, dt, V, chunk). */
+size_t kd_kl_hidden_workspace(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk);
+
+/* Exact full-vocabulary KL(q || p) with the teacher rebuilt from a cached
+ * hidden state [TG Fig. 3 bottom: caching the teacher's final hidden state
+ * reconstructs its full distribution at 2 dt V FLOP per token]:
+ *   q = softmax(U g_t + b), p = softmax(W h_t),
+ *   L_t = sum_v q_v (log q_v - log p_v),  dL_t/dz = p - q.
+ *
+ * In:  h  [T, d]  bf16  student final hidden states
+ *      W  [V, d]  bf16  student LM-head rows
+ *      g  [T, dt] bf16  cached teacher final hidden states
+ *      U  [V, dt] bf16  teacher LM-head rows
+ *      b  [V]     fp32  teacher bias, or NULL
+ *      d, dt multiples of 64 (<= 16384); chunk as kd_topk_loss_fwd_bwd
+ *      (chunk x max(d, dt) bf16, T x max(d, dt) bf16 and T x chunk fp32 each
+ *      below 4 GiB); scale: loss = scale * sum_t L_t
+ * Out: loss [1], loss_tok [T] or NULL, lse [T] or NULL (student), lse_t [T]
+ *      or NULL (teacher), dh [T, d] fp32, dW [V, d] fp32 (fully written).
+ * Neither [T, V] logit tensor is stored: both heads are evaluated one
+ * vocabulary chunk at a time (twice, forward and backward). */
+kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, const kd_bf16* U,
+                               const float* b, int64_t T, int64_t d, int64_t dt, int64_t V,
+                               int32_t chunk, float scale,
+                               float* loss, float* loss_tok, float* lse, float* lse_t,
+                               float* dh, float* dW,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace kd_topk_cache_build needs.  Returns 0 for
  * invalid sizes. */
 size_t kd_topk_cache_build_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho);

@@ -34,6 +34,9 @@ _SIGS = {
     "kd_topk_loss_ce_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _f32]),
     "kd_topk_loss_fwd_bwd_ce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, _i32, _i32,
                                                _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_kl_hidden_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32]),
+    "kd_kl_hidden_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _f32,
+                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -159,6 +162,52 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
                                         _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
                                         _stream(dev))
     _check(st, "kd_topk_loss_fwd_bwd_ce" if ce else "kd_topk_loss_fwd_bwd")
+    return out
+
+
+class KlOut(NamedTuple):
+    loss: torch.Tensor
+    dh: torch.Tensor
+    dW: torch.Tensor
+    loss_tok: torch.Tensor
+    lse: torch.Tensor
+    lse_t: torch.Tensor
+
+
+def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torch.Tensor,
+                      b: Optional[torch.Tensor] = None, chunk: int = 8192, scale: Optional[float] = None,
+                      workspace: Optional[torch.Tensor] = None, out: Optional[KlOut] = None) -> KlOut:
+    """Exact full-vocabulary KL(softmax(U g + b) || softmax(W h)), forward and
+    backward, with the teacher rebuilt from its cached hidden state g
+    (kd_kl_hidden_fwd_bwd)."""
+    dev = h.device
+    T, d = h.shape
+    V = W.shape[0]
+    dt = g.shape[1]
+    _need(h, "h", torch.bfloat16, (T, d), dev)
+    _need(W, "W", torch.bfloat16, (V, d), dev)
+    _need(g, "g", torch.bfloat16, (T, dt), dev)
+    _need(U, "U", torch.bfloat16, (V, dt), dev)
+    if b is not None:
+        _need(b, "b", torch.float32, (V,), dev)
+    if scale is None:
+        scale = 1.0 / max(T, 1)
+    L = lib()
+    ws_bytes = int(L.kd_kl_hidden_workspace(T, d, dt, V, chunk))
+    if ws_bytes == 0:
+        _check(L.kd_kl_hidden_fwd_bwd(None, None, None, None, None, T, d, dt, V, chunk, scale,
+                                      None, None, None, None, None, None, None, 0, None), "kd_kl_hidden_fwd_bwd")
+    with torch.cuda.device(dev):
+        if workspace is None or workspace.numel() < ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        if out is None:
+            f32 = dict(dtype=torch.float32, device=dev)
+            out = KlOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
+                        torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
+        st = L.kd_kl_hidden_fwd_bwd(_ptr(h), _ptr(W), _ptr(g), _ptr(U), _ptr(b), T, d, dt, V, chunk, scale,
+                                    _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.lse_t),
+                                    _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "kd_kl_hidden_fwd_bwd")
     return out
 
 

@@ -454,7 +454,8 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
   }
 }
 
-// loss = scale * sum_t L_t in a fixed order; NaN when the prep flagged bad indices.
+// loss = scale * sum_t L_t in a fixed order; NaN when the prep flagged bad
+// indices (err may be NULL: no flag).
 __global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const float* __restrict__ tok,
                                                    const int32_t* __restrict__ err, float* __restrict__ loss) {
   __shared__ double red[1024];
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const
     if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
-  if (threadIdx.x == 0) loss[0] = (*err) ? __builtin_nanf("") : (float)(scale * red[0]);
+  if (threadIdx.x == 0) loss[0] = (err != nullptr && *err) ? __builtin_nanf("") : (float)(scale * red[0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -691,6 +692,334 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
         }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Exact full-vocabulary KL(q || p) with the teacher rebuilt from a cached
+// hidden state, q = softmax(U g + b) ("The Gradient That Top-k Distillation
+// Never Computes", Figure 3 bottom).  Per token
+//   L = sum_v q_v (log q_v - log p_v) = H_t - sum_v q_v z_v + lse,
+//   H_t = sum_v q_v log q_v = E_q[zt] - lse_t,    dL/dz = p - q.
+// Pass 1: logsumexp partials of the student and the teacher tiles (the
+// teacher's also carry sum exp(x - m) (x - m), which gives E_q[zt]); per
+// vocabulary chunk: the teacher tiles again -> q (fp32 [Tp, C] workspace),
+// the student tiles -> dz = scale (p - q) and per-tile sums of q z, then the
+// dh / dW GEMMs of the dense path.
+// ---------------------------------------------------------------------------
+constexpr int LP_RED = TC::WM * TT * 3 * 4;  // (m, s, u) per wavefront row and token
+static_assert(LP_RED + VT * 4 <= TC::LDS_BYTES, "lse-pass reduction space");
+
+// Rows of the tile's accumulators get the bias of their vocabulary row
+// (bl: the tile's VT biases in LDS).
+__device__ __forceinline__ void add_row_bias(Acc<TC>& acc, const float* bl, int wm, int lane) {
+#pragma unroll
+  for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float bv = bl[acc_row<TC>(wm, fm, e, lane)];
+#pragma unroll
+      for (int fn = 0; fn < TC::FN; ++fn) acc.v[fm][fn][e] += bv;
+    }
+}
+
+template <bool TEACHER, bool MASK>
+__device__ __forceinline__ void lse_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, int64_t K,
+                                         int64_t T, int64_t V, const float* __restrict__ bias, int vt, int tt,
+                                         int64_t Tp, float2* __restrict__ part, float4* __restrict__ partT,
+                                         bf16_t* lds) {
+  const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TC::WN, wn = wave % TC::WN;
+  Acc<TC> acc;
+  gemm_tile_pipe<TC>(A, K, m0, V, B, K, n0, T, (int)K, lds, acc);
+  __syncthreads();  // every wavefront is done with the operand stages
+  float* red = (float*)lds;
+  if (TEACHER) {
+    float* bl = (float*)((char*)lds + LP_RED);
+    for (int i = threadIdx.x; i < VT; i += TC::NT) bl[i] = (bias != nullptr && m0 + i < V) ? bias[m0 + i] : 0.f;
+    __syncthreads();
+    add_row_bias(acc, bl, wm, lane);
+  }
+  if (MASK) mask_rows(acc, (int)(V - m0), wm, lane);
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    float mx = -KD_INF;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc.v[fm][fn][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float nm = (mx == -KD_INF) ? 0.f : -mx * KD_LOG2E;
+    float s = 0.f, u = 0.f;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float x = acc.v[fm][fn][e];
+        const float ex = __builtin_amdgcn_exp2f(fmaf(x, KD_LOG2E, nm));
+        s += ex;
+        if (TEACHER) u += (ex > 0.f) ? ex * (x - mx) : 0.f;  // masked rows: 0, not 0 * -inf
+      }
+    s += __shfl_xor(s, 32, 64);
+    if (TEACHER) u += __shfl_xor(u, 32, 64);
+    const int col = acc_col<TC>(wn, fn, lane);
+    if (lane < 32) {
+      red[(wm * TT + col) * 3 + 0] = mx;
+      red[(wm * TT + col) * 3 + 1] = s;
+      red[(wm * TT + col) * 3 + 2] = u;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  for (int col = threadIdx.x; col < TT; col += TC::NT) {
+    float M = -KD_INF;
+#pragma unroll
+    for (int w = 0; w < TC::WM; ++w) M = fmaxf(M, red[(w * TT + col) * 3]);
+    float S = 0.f, Uq = 0.f;
+#pragma unroll
+    for (int w = 0; w < TC::WM; ++w) {
+      const float mw = red[(w * TT + col) * 3], sw = red[(w * TT + col) * 3 + 1], uw = red[(w * TT + col) * 3 + 2];
+      if (mw == -KD_INF) continue;
+      const float f = __expf(mw - M);
+      S += sw * f;
+      if (TEACHER) Uq += f * (uw + (mw - M) * sw);
+    }
+    const int64_t t = n0 + col;
+    if (t < T) {
+      if (TEACHER)
+        partT[(int64_t)vt * Tp + t] = make_float4(M, S, Uq, 0.f);
+      else
+        part[(int64_t)vt * Tp + t] = make_float2(M, S);
+    }
+  }
+}
+
+template <bool TEACHER>
+__global__ __launch_bounds__(256, 1) void k_lse_pass(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+                                                     int64_t K, int64_t T, int64_t V, const float* __restrict__ bias,
+                                                     int nVT, int nTT, int64_t Tp, float2* __restrict__ part,
+                                                     float4* __restrict__ partT) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int vt, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 8, vt, tt)) return;
+  if ((int64_t)(vt + 1) * VT > V)
+    lse_tile<TEACHER, true>(A, B, K, T, V, bias, vt, tt, Tp, part, partT, lds);
+  else
+    lse_tile<TEACHER, false>(A, B, K, T, V, bias, vt, tt, Tp, part, partT, lds);
+}
+
+// Per token (one wavefront): student lse; teacher lse_t and H_t = E_q[zt] -
+// lse_t from the (m, s, u) partials, merged in fp64.
+__global__ __launch_bounds__(256) void k_kl_combine(int64_t T, int nVT, int64_t Tp, float scale,
+                                                    const float2* __restrict__ part,
+                                                    const float4* __restrict__ partT, float* __restrict__ tok) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  double m = -INFINITY, s = 0.0, mt = -INFINITY, st = 0.0, ut = 0.0;
+  for (int vt = lane; vt < nVT; vt += 64) {
+    const float2 p = part[(int64_t)vt * Tp + t];
+    if (p.x != -INFINITY) {
+      const double mn = fmax(m, (double)p.x);
+      s = (m == -INFINITY ? 0.0 : s * exp(m - mn)) + (double)p.y * exp((double)p.x - mn);
+      m = mn;
+    }
+    const float4 q = partT[(int64_t)vt * Tp + t];
+    if (q.x != -INFINITY) {
+      const double mn = fmax(mt, (double)q.x);
+      const double fo = (mt == -INFINITY) ? 0.0 : exp(mt - mn), fp = exp((double)q.x - mn);
+      ut = (mt == -INFINITY ? 0.0 : fo * (ut + (mt - mn) * st)) + fp * ((double)q.z + ((double)q.x - mn) * (double)q.y);
+      st = (mt == -INFINITY ? 0.0 : st * fo) + (double)q.y * fp;
+      mt = mn;
+    }
+  }
+  double M = m, Mt = mt;
+  for (int o = 32; o > 0; o >>= 1) {
+    M = fmax(M, __shfl_xor(M, o, 64));
+    Mt = fmax(Mt, __shfl_xor(Mt, o, 64));
+  }
+  const double f = (m == -INFINITY) ? 0.0 : exp(m - M);
+  const double ft = (mt == -INFINITY) ? 0.0 : exp(mt - Mt);
+  s = wave_sum_f64(s * f);
+  const double ut_l = (mt == -INFINITY) ? 0.0 : ft * (ut + (mt - Mt) * st);
+  st = wave_sum_f64(st * ft);
+  ut = wave_sum_f64(ut_l);
+  if (lane == 0) {
+    float* tk = tok + t * TOKF;
+    const double lse_t = Mt + log(st);
+    tk[TK_LSE] = (float)(M + log(s));
+    tk[TK_LSEQ] = (float)lse_t;
+    tk[TK_ALPHA] = scale;
+    tk[TK_L] = (float)(ut / st - log(st));  // H_t = E_q[zt] - lse_t
+  }
+}
+
+// Teacher tile of one chunk -> q = exp(U g + b - lse_t) as fp32 token rows
+// qbuf [Tp][Cp] (0 past the chunk end and for padding tokens).  The tile is
+// staged half its tokens at a time in LDS (1 KB rows, 16-byte chunks
+// XOR-swizzled by token) and leaves as whole token rows.
+constexpr int TQ_LDS = (TC::BN / 2) * TC::BM * 4;  // 128 tokens x 256 vocabulary fp32
+static_assert(TQ_LDS >= TC::LDS_BYTES, "q staging reuses the operand stages");
+
+__global__ __launch_bounds__(256, 1) void k_teacher_q(const bf16_t* __restrict__ U, const bf16_t* __restrict__ g,
+                                                      const float* __restrict__ bias, int64_t T, int64_t dt,
+                                                      int64_t Cp, int64_t c0, int64_t c1, int nCT, int nTT,
+                                                      const float* __restrict__ tok, float* __restrict__ qbuf) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int ct, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
+  const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
+  Acc<TC> acc;
+  gemm_tile_pipe<TC>(U, dt, m0, c1, g, dt, n0, T, (int)dt, lds, acc);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TC::WN, wn = wave % TC::WN;
+  float* E = (float*)lds;
+  const int c = tid & 63;  // this thread's 16-byte chunk of a token row: vocabulary m0 + 4c .. +3
+  const int64_t v = m0 + 4 * c;
+  float bv[4];
+  bool in[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    in[e] = v + e < c1;
+    bv[e] = (bias != nullptr && in[e]) ? bias[v + e] : 0.f;
+  }
+  __syncthreads();  // every wavefront is done with the operand stages
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wn == half) {
+#pragma unroll
+      for (int fn = 0; fn < TC::FN; ++fn) {
+        const int tl = fn * 32 + (lane & 31);
+        float* row = E + tl * TC::BM;
+#pragma unroll
+        for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cv = (wm * TC::TM + fm * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+            *(f32x4*)(row + ((cv ^ ((tl & 31) << 1)) << 2)) =
+                f32x4{acc.v[fm][fn][4 * q], acc.v[fm][fn][4 * q + 1], acc.v[fm][fn][4 * q + 2], acc.v[fm][fn][4 * q + 3]};
+          }
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < TC::BN / 2 / 4; ++i) {
+      const int tl = wave + 4 * i;
+      const int64_t t = n0 + half * (TC::BN / 2) + tl;
+      const f32x4 x = *(const f32x4*)(E + tl * TC::BM + ((c ^ ((tl & 31) << 1)) << 2));
+      f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < T) {
+        const float nl = -tok[t * TOKF + TK_LSEQ] * KD_LOG2E;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = in[e] ? __builtin_amdgcn_exp2f(fmaf(x[e] + bv[e], KD_LOG2E, nl)) : 0.f;
+      }
+      if (m0 + 4 * c < c0 + Cp) *(f32x4*)(qbuf + t * Cp + (v - c0)) = q;
+    }
+    __syncthreads();
+  }
+}
+
+// Student tile of one chunk: dz = scale (exp(z - lse) - q) as bf16 token rows
+// (staged in LDS as in k_zdz), and per (vocabulary tile, token) the sum of
+// q z, merged over the wavefront rows.
+constexpr int ZK_LDS = ZDZ_LDS + TC::WM * TT * 4;
+
+template <bool MASK>
+__device__ __forceinline__ void zdz_kl_tile(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h, int64_t T,
+                                            int64_t d, int64_t Tp, int64_t Cp, int64_t c0, int64_t c1,
+                                            const float* __restrict__ tok, const float* __restrict__ qbuf,
+                                            float* __restrict__ partQZ, bf16_t* __restrict__ dz, int ct, int tt,
+                                            bf16_t* lds) {
+  const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
+  const int vt = (int)(m0 / VT);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TC::WN, wn = wave % TC::WN;
+  Acc<TC> acc;
+  gemm_tile_pipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
+  if (MASK) mask_rows(acc, (int)(c1 - m0), wm, lane);
+  __syncthreads();  // every wavefront is done with the operand stages
+  char* E = (char*)lds;
+  float* red = (float*)((char*)lds + ZDZ_LDS);
+  const int rbase = wm * TC::TM + 4 * (lane >> 5);
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int tl = acc_col<TC>(wn, fn, lane);
+    const int64_t t = n0 + tl;
+    const bool tok_ok = t < T;
+    const float nl = tok_ok ? -tok[t * TOKF + TK_LSE] * KD_LOG2E : -KD_INF;
+    const float a = tok_ok ? tok[t * TOKF + TK_ALPHA] : 0.f;
+    const float* qrow = qbuf + (tok_ok ? t : 0) * Cp + (m0 - c0);
+    char* row = E + tl * (VT * 2);
+    const int sw = zdz_swz(tl);
+    float qz = 0.f;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int vl = rbase + fm * 32 + 8 * g;  // multiple of 4
+        const f32x4 q = tok_ok ? *(const f32x4*)(qrow + vl) : f32x4{0.f, 0.f, 0.f, 0.f};
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float z = acc.v[fm][fn][g * 4 + r];
+          x[r] = a * (__builtin_amdgcn_exp2f(fmaf(z, KD_LOG2E, nl)) - q[r]);
+          qz += (q[r] != 0.f) ? q[r] * z : 0.f;  // masked rows: q = 0, z = -inf
+        }
+        uint2 pk;
+        pk.x = pack_bf16x2(x[0], x[1]);
+        pk.y = pack_bf16x2(x[2], x[3]);
+        *(uint2*)(row + (((vl >> 3) ^ sw) << 4) + (vl & 7) * 2) = pk;
+      }
+    qz += __shfl_xor(qz, 32, 64);
+    if (lane < 32) red[wm * TT + tl] = qz;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  for (int col = threadIdx.x; col < TT; col += TC::NT) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < TC::WM; ++w) sum += red[w * TT + col];
+    if (n0 + col < T) partQZ[(int64_t)vt * Tp + n0 + col] = sum;
+  }
+  const int tid = threadIdx.x;
+  const int64_t vo = m0 - c0;
+#pragma unroll 4
+  for (int it = 0; it < TT / 8; ++it) {
+    const int tl = it * 8 + (tid >> 5), cc = tid & 31;
+    const u32x4 q = *(const u32x4*)(E + tl * (VT * 2) + ((cc ^ zdz_swz(tl)) << 4));
+    *(u32x4*)(dz + (n0 + tl) * Cp + vo + cc * 8) = q;
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void k_zdz_kl(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+                                                   int64_t T, int64_t d, int64_t Tp, int64_t Cp, int64_t c0,
+                                                   int64_t c1, int nCT, int nTT, const float* __restrict__ tok,
+                                                   const float* __restrict__ qbuf, float* __restrict__ partQZ,
+                                                   bf16_t* __restrict__ dz) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int ct, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
+  if (c0 + (int64_t)(ct + 1) * VT > c1)
+    zdz_kl_tile<true>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, ct, tt, lds);
+  else
+    zdz_kl_tile<false>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, ct, tt, lds);
+}
+
+// L_t = H_t - sum_v q_v z_v + lse, one thread per token (partials summed in
+// vocabulary-tile order).
+__global__ __launch_bounds__(256) void k_kl_finish(int64_t T, int nVT, int64_t Tp, const float* __restrict__ partQZ,
+                                                   float* __restrict__ tok, float* __restrict__ loss_tok,
+                                                   float* __restrict__ lse_out, float* __restrict__ lset_out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  double qz = 0.0;
+  for (int vt = 0; vt < nVT; ++vt) qz += (double)partQZ[(int64_t)vt * Tp + t];
+  float* tk = tok + t * TOKF;
+  const float L = (float)((double)tk[TK_L] - qz + (double)tk[TK_LSE]);
+  tk[TK_L] = L;
+  if (loss_tok) loss_tok[t] = L;
+  if (lse_out) lse_out[t] = tk[TK_LSE];
+  if (lset_out) lset_out[t] = tk[TK_LSEQ];
 }
 
 // ---------------------------------------------------------------------------
@@ -1054,4 +1383,110 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
                                           float* dW, void* ws, size_t ws_bytes, void* stream) {
   return kd_topk_loss_fwd_bwd_ce(h, W, idx, teacher_logp, m_q, nullptr, 0.f, T, d, V, K, mode, chunk, scale, loss,
                                  loss_tok, lse, m_p, dh, dW, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Exact full-vocabulary KL from a hidden-state teacher cache: host side
+// ---------------------------------------------------------------------------
+namespace {
+
+struct KlPlan {
+  int64_t Tp, C, Cp;
+  int nVT, nTT, nDT, nchunks;
+  size_t o_tok, o_part, o_partT, o_partQZ, o_q, o_dz, total;
+};
+
+static bool plan_kl(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk, KlPlan& p) {
+  if (T < 0 || d <= 0 || dt <= 0 || V <= 0 || d % 64 != 0 || dt % 64 != 0 || d > 16384 || dt > 16384 || chunk <= 0)
+    return false;
+  if (V > (int64_t)1 << 30 || T > (int64_t)1 << 26) return false;
+  p.Tp = kd_round_up(T > 0 ? T : 1, TT);
+  p.C = kd_round_up(chunk, VT);
+  if (p.C > kd_round_up(V, VT)) p.C = kd_round_up(V, VT);
+  p.Cp = p.C;
+  const uint64_t lim = (uint64_t)1 << 32;
+  const uint64_t dm = (uint64_t)(d > dt ? d : dt);
+  if ((uint64_t)p.C * dm * 2u >= lim || (uint64_t)p.Tp * dm * 2u >= lim || (uint64_t)p.Tp * (uint64_t)p.C * 4u >= lim)
+    return false;
+  p.nVT = (int)kd_ceil_div(V, VT);
+  p.nTT = (int)(p.Tp / TT);
+  p.nDT = (int)kd_ceil_div(d, TC::BN);
+  p.nchunks = (int)kd_ceil_div(V, p.C);
+  size_t o = 0;
+  p.o_tok = o; o = align_up(o + (size_t)p.Tp * TOKF * 4);
+  p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
+  p.o_partT = o; o = align_up(o + (size_t)p.nVT * p.Tp * 16);
+  p.o_partQZ = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
+  p.o_q = o; o = align_up(o + (size_t)p.Tp * p.Cp * 4);
+  p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
+  p.total = o;
+  return true;
+}
+
+}  // namespace
+
+extern "C" size_t kd_kl_hidden_workspace(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk) {
+  KlPlan p;
+  if (!plan_kl(T, d, dt, V, chunk, p)) return 0;
+  return p.total;
+}
+
+extern "C" kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, const kd_bf16* U,
+                                          const float* b, int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk,
+                                          float scale, float* loss, float* loss_tok, float* lse, float* lse_t,
+                                          float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
+  KlPlan p;
+  if (!plan_kl(T, d, dt, V, chunk, p))
+    return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld dt=%lld V=%lld chunk=%d (need d%%64==0, dt%%64==0, d,dt<=16384, chunk>0, and chunk*d, T*d bf16 and T*chunk fp32 each < 4 GiB)",
+                   (long long)T, (long long)d, (long long)dt, (long long)V, (int)chunk);
+  if (!loss || !dW || !W || !U) return kd_fail(KD_EINVAL, "null required pointer (loss, W, U, dW)");
+  if (T > 0 && (!h || !g || !dh)) return kd_fail(KD_EINVAL, "null required pointer (h, g, dh)");
+  if (!ws || ws_bytes < p.total)
+    return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  float* tok = at<float>(ws, p.o_tok);
+  if (T == 0) {
+    KD_LAUNCH(k_fill_i32, dim3(1024), dim3(256), 0, s, (int32_t*)dW, V * d, 0);
+    KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, (int64_t)0, scale, (const float*)tok, (const int32_t*)nullptr, loss);
+    KD_LAUNCH_CHECK();
+    return KD_OK;
+  }
+  float2* part = at<float2>(ws, p.o_part);
+  float4* partT = at<float4>(ws, p.o_partT);
+  float* partQZ = at<float>(ws, p.o_partQZ);
+  float* qbuf = at<float>(ws, p.o_q);
+  bf16_t* dz = at<bf16_t>(ws, p.o_dz);
+  const int g1 = grid_of(p.nVT * p.nTT);
+  KD_LAUNCH(k_lse_pass<false>, dim3(g1), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)W, (const bf16_t*)h, d, T, V,
+                     (const float*)nullptr, p.nVT, p.nTT, p.Tp, part, (float4*)nullptr);
+  KD_LAUNCH(k_lse_pass<true>, dim3(g1), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)U, (const bf16_t*)g, dt, T, V,
+                     b, p.nVT, p.nTT, p.Tp, (float2*)nullptr, partT);
+  KD_LAUNCH_CHECK();
+  KD_LAUNCH(k_kl_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, p.nVT, p.Tp, scale, part, partT, tok);
+  KD_LAUNCH_CHECK();
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int64_t c0 = (int64_t)c * p.C;
+    const int64_t c1 = (c0 + p.C < V) ? c0 + p.C : V;
+    const int64_t clen = c1 - c0;
+    const int nCT = (int)kd_ceil_div(clen, VT);
+    const int gz = grid_of(nCT * p.nTT);
+    KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), TQ_LDS, s, (const bf16_t*)U, (const bf16_t*)g, b, T, dt, p.Cp, c0,
+                       c1, nCT, p.nTT, (const float*)tok, qbuf);
+    KD_LAUNCH(k_zdz_kl, dim3(gz), dim3(TC::NT), ZK_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0,
+                       c1, nCT, p.nTT, (const float*)tok, (const float*)qbuf, partQZ, dz);
+    KD_LAUNCH_CHECK();
+    const int kdh = (int)kd_round_up(clen, 64);
+    const int gdh = grid_of(p.nTT * p.nDT);
+    const int nCTw = (int)kd_ceil_div(clen, TC::BN);
+    const int gdw = grid_of(nCTw * p.nDT);
+    KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)dz, (const bf16_t*)W,
+                       (const bf16_t*)h, T, d, p.Tp, p.Cp, c0, clen, kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh,
+                       dh, dW);
+    KD_LAUNCH_CHECK();
+  }
+  KD_LAUNCH(k_kl_finish, dim3((unsigned)kd_ceil_div(T, 256)), dim3(256), 0, s, T, p.nVT, p.Tp, (const float*)partQZ,
+                     tok, loss_tok, lse, lse_t);
+  KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, (const float*)tok, (const int32_t*)nullptr, loss);
+  KD_LAUNCH_CHECK();
+  return KD_OK;
 }
