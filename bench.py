@@ -240,6 +240,8 @@ def main():
         res["other_mode"] = {"mode": {kd.RENORM: "renorm", kd.TAIL: "tail"}[other], "ms_per_step": ms2,
                              "tokens_per_s": T / (ms2 * 1e-3), "mfma_frac_step": cr2 / (ms2 * 1e-3) / PEAK_BF16}
         log(f"[bench] other mode: {ms2:.3f} ms/step")
+        res["kl_hidden"] = bench_kl_hidden(torch, kd, synth, dev, hd, Wd, max(3, args.steps // 2))
+        log(f"[bench] kl_hidden: {res['kl_hidden']}")
         del hd, Wd
         torch.cuda.empty_cache()
         res["cache_build"] = bench_cache_build(torch, kd, synth, dev)
@@ -255,6 +257,32 @@ def main():
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def bench_kl_hidden(torch, kd, synth, dev, hd, Wd, steps):
+    """Exact full-vocabulary KL with the teacher rebuilt from a cached hidden
+    state: Qwen3-8B-shaped teacher head (d_t = 4096) over the same student."""
+    T, d, V = CFG["T"], CFG["d"], CFG["V"]
+    dt = 4096
+    g, U, b = synth.teacher_head(T, dt, V, seed=1)
+    gd, Ud, bd = g.to(dev), U.to(dev), b.to(dev)
+    del g, U
+    ws = torch.empty(kd.lib().kd_kl_hidden_workspace(T, d, dt, V, CFG["chunk"]), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = kd.KlOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
+                   torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
+    fn = lambda: kd.kl_hidden_fwd_bwd(hd, Wd, gd, Ud, bd, chunk=CFG["chunk"], workspace=ws, out=out)
+    ms = time_steps(torch, fn, steps, 2)
+    prof = kernel_profile(kd, torch, fn, 2)
+    credited = 2 * T * d * V + 2 * T * dt * V + 4 * T * d * V      # student forward, teacher head, dh + dW
+    executed = 2 * (2 * T * d * V) + 2 * (2 * T * dt * V) + 4 * T * d * V
+    del gd, Ud, bd, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": "Qwen3-8B-shaped teacher head (hidden-state cache) over the Qwen3-1.7B-shaped student",
+            "T": T, "d": d, "d_teacher": dt, "V": V, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "mfma_frac_credited": credited / (ms * 1e-3) / PEAK_BF16,
+            "mfma_frac_executed": executed / (ms * 1e-3) / PEAK_BF16,
+            "kernels_ms_per_step": {k: round(v[0], 4) for k, v in prof.items()}}
 
 
 def bench_cache_build(torch, kd, synth, dev, steps=3):
