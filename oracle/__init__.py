@@ -16,7 +16,8 @@ Sources (cited by title and section, figure or equation):
   tail masses m_q / m_p, the truncated-gradient decomposition, and the
   twelve-token worked example (Figure 2).
 * "Tail-Aware Top-k On-Policy Distillation" (Huang, Wei), abstract: the
-  top-k bins plus one tail bin carrying the tail probability.
+  top-k bins plus one tail bin carrying the tail probability, in the forward
+  (TAIL) and in the paper's own reverse (TAIL_REVERSE) direction.
 * "Unbiased Top-k Estimation for On-Policy Distillation" (Meng et al.),
   abstract and Table 2: reverse KL between the normalized top-k
   distributions, with the student's own top-16 as the support.
@@ -39,7 +40,7 @@ printed values, closed forms, library routines, finite differences or
 brute force; none is "parity unpinned".
 """
 from .kd_oracle import (  # noqa: F401
-    RENORM, TAIL, FULL, REVERSE, MODES, MODE_NAMES,
+    RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, MODES, MODE_NAMES,
     logsumexp, student_logits, loss_rows_from_logits, loss_fwd_bwd,
     topk_row, cache_from_logits, cache_build, teacher_logp, adaptive_k_row, kl_hidden_fwd_bwd,
 )

@@ -16,9 +16,9 @@ from __future__ import annotations
 
 import numpy as np
 
-RENORM, TAIL, FULL, REVERSE = 0, 1, 2, 3
-MODES = (RENORM, TAIL, FULL, REVERSE)
-MODE_NAMES = {RENORM: "renorm", TAIL: "tail", FULL: "full", REVERSE: "reverse"}
+RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE = 0, 1, 2, 3, 4
+MODES = (RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE)
+MODE_NAMES = {RENORM: "renorm", TAIL: "tail", FULL: "full", REVERSE: "reverse", TAIL_REVERSE: "tail_reverse"}
 
 # Smallest normal float32: the floor for a student tail mass that rounds to 0
 # while the teacher still has tail mass (the loss is then huge but finite).
@@ -99,6 +99,21 @@ def _loss_row(z: np.ndarray, S: np.ndarray, tl: np.ndarray, m_q: float, mode: in
         ph = np.exp(log_ph)
         L = float(np.sum(ph * (log_ph - log_qh)))
         dz[S] = ph * (log_ph - log_qh - L)
+    elif mode == TAIL_REVERSE:
+        # Reverse KL over the top-k bins plus one tail token carrying the
+        # tail mass: KL((p_S, m_p) || (q_S, m_q)) ("Tail-Aware Top-k
+        # On-Policy Distillation", abstract).  With a_v = log(p_v / q_v) -
+        # log(m_p / m_q) on S (the derivative of L in p_v, m_p = 1 - sum_S p),
+        # dz_u = p_u (a_u [u in S] - sum_S p a).  Both tail masses are
+        # floored at the smallest normal float32 inside the logarithms.
+        mp = max(m_p, _TINY)
+        mq = max(m_q, _TINY)
+        tail_log = np.log(mp) - np.log(mq)
+        L = float(np.sum(p[S] * (logp[S] - tl))) + m_p * tail_log
+        a = (logp[S] - tl) - tail_log
+        A = float(np.sum(p[S] * a))
+        dz = -A * p
+        dz[S] += p[S] * a
     else:
         raise ValueError(f"unknown mode {mode}")
     return L, dz, lse, m_p

@@ -16,7 +16,7 @@ import scipy.special
 import torch
 
 import oracle
-from oracle import RENORM, TAIL, FULL, REVERSE
+from oracle import RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -154,13 +154,16 @@ def _torch_loss(z_row, S, tl, m_q, mode):
         target = torch.zeros_like(zt)
         target[S_t] = torch.exp(tl_t)
         L = torch.nn.functional.kl_div(torch.log_softmax(zt, 0), target, reduction="sum")
-    else:  # TAIL: KL between the two (K+1)-categoricals
+    else:  # TAIL / TAIL_REVERSE: KL between the two (K+1)-categoricals
         p = torch.softmax(zt, 0)
         mask = torch.ones_like(zt, dtype=torch.bool)
         mask[S_t] = False
         pt = torch.cat([p[S_t], p[mask].sum().reshape(1)])
         qt = torch.cat([torch.exp(tl_t), torch.tensor([m_q], dtype=torch.float64)])
-        L = torch.sum(qt * (torch.log(qt) - torch.log(pt)))
+        if mode == TAIL:
+            L = torch.sum(qt * (torch.log(qt) - torch.log(pt)))
+        else:
+            L = torch.sum(pt * (torch.log(pt) - torch.log(qt)))
     L.backward()
     return float(L.detach()), zt.grad.numpy()
 
@@ -527,3 +530,24 @@ def test_kl_hidden_equals_cached_full_support():
     assert abs(out["loss"] - ref["loss"]) < 1e-12
     np.testing.assert_allclose(out["dh"], ref["dh"], atol=1e-13)
     np.testing.assert_allclose(out["dW"], ref["dW"], atol=1e-13)
+
+
+def test_tail_reverse_at_full_support_is_dense_reverse_kl():
+    """K = V: no tail on either side, and the tail-token reverse KL is the
+    dense KL(p || q) with gradient p (log p - log q - KL)."""
+    from torch.distributions import Categorical, kl_divergence
+    r = np.random.default_rng(21)
+    T, d, V = 4, 5, 17
+    h, W = r.standard_normal((T, d)), r.standard_normal((V, d))
+    zt_teacher = r.standard_normal((T, V))
+    tlp = zt_teacher - scipy.special.logsumexp(zt_teacher, axis=1)[:, None]
+    idx = np.tile(np.arange(V), (T, 1))
+    z = oracle.student_logits(h, W)
+    L, dz, _, m_p = oracle.loss_rows_from_logits(z, idx, tlp, np.zeros(T), TAIL_REVERSE)
+    assert np.abs(m_p).max() < 1e-15
+    for t in range(T):
+        zt = torch.tensor(z[t], requires_grad=True)
+        kl = kl_divergence(Categorical(logits=zt), Categorical(logits=torch.tensor(tlp[t])))
+        kl.backward()
+        assert abs(L[t] - float(kl.detach())) < 1e-12
+        np.testing.assert_allclose(dz[t], zt.grad.numpy(), atol=1e-13)
