@@ -66,8 +66,11 @@ typedef enum {
  *   KD_FULL    L = sum_S q (log q - z) + Q * logsumexp(z) [FK sec. 3.2, (2);
  *              equals the dense KL(q || p) when S covers the vocabulary]
  *   KD_REVERSE L = KL(p_hat || q_hat)                    [TT abstract]
- * The gradient dL/dz is the exact derivative of L; for KD_FULL it is Eq. (3). */
-typedef enum { KD_RENORM = 0, KD_TAIL = 1, KD_FULL = 2, KD_REVERSE = 3 } kd_mode;
+ *   KD_TAIL_REVERSE  L = sum_S p log(p/q) + m_p log(m_p/m_q) [TA abstract: the
+ *              reverse KL over the top-k tokens plus a tail token]
+ * The gradient dL/dz is the exact derivative of L; for KD_FULL it is Eq. (3).
+ * Tail masses inside logarithms are floored at the smallest normal float. */
+typedef enum { KD_RENORM = 0, KD_TAIL = 1, KD_FULL = 2, KD_REVERSE = 3, KD_TAIL_REVERSE = 4 } kd_mode;
 
 /* Bytes of device workspace kd_topk_loss_fwd_bwd needs for these sizes.
  * Linear in T for fixed (d, V, K, chunk).  Returns 0 for invalid sizes. */
@@ -81,10 +84,11 @@ size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_
  *                                 row, in [0, V) or -1 for an ignored padding slot;
  *                                 any order.  Values >= V are rejected on the
  *                                 device by writing NaN to *loss.
- *      teacher_logp [T, K] fp32   teacher log-probabilities at idx.  KD_TAIL and
- *                                 KD_FULL expect full-vocabulary-normalised values;
+ *      teacher_logp [T, K] fp32   teacher log-probabilities at idx.  KD_TAIL,
+ *                                 KD_TAIL_REVERSE and KD_FULL expect
+ *                                 full-vocabulary-normalised values;
  *                                 KD_RENORM and KD_REVERSE accept any per-row shift.
- *      m_q          [T]    fp32   teacher tail mass (KD_TAIL only; may be NULL
+ *      m_q          [T]    fp32   teacher tail mass (KD_TAIL, KD_TAIL_REVERSE; may be NULL
  *                                 for the other modes)
  *      mode         kd_mode
  *      chunk        vocabulary rows per chunk of the backward (> 0; e.g. 8192;

@@ -69,7 +69,7 @@ def qwen17_head():
 
 
 @pytest.mark.timeout(400)
-@pytest.mark.parametrize("mode", [kd.TAIL, kd.RENORM])
+@pytest.mark.parametrize("mode", [kd.TAIL, kd.RENORM, kd.TAIL_REVERSE])
 def test_qwen3_1p7b_head_full_size(qwen17_head, mode):
     T, d, V, K, h, W, idx, tlp, mq, h64, W64 = qwen17_head
     g = _gpu(h, W, idx, tlp, mq, mode)

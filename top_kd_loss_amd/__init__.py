@@ -18,8 +18,8 @@ from typing import NamedTuple, Optional, Sequence
 
 import torch
 
-RENORM, TAIL, FULL, REVERSE = 0, 1, 2, 3
-MODE_BY_NAME = {"renorm": RENORM, "tail": TAIL, "full": FULL, "reverse": REVERSE}
+RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE = 0, 1, 2, 3, 4
+MODE_BY_NAME = {"renorm": RENORM, "tail": TAIL, "full": FULL, "reverse": REVERSE, "tail_reverse": TAIL_REVERSE}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdtopk.so")

@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
   const double lseS = (nv > 0) ? zmax + log(es) : -INFINITY;
   double mp = (nv > 0) ? -expm1(lseS - lse) : 1.0;
   if (mp < 0.0) mp = 0.0;
-  const double mq = (mode == KD_TAIL) ? (double)m_q[t] : 0.0;
+  const double mq = (mode == KD_TAIL || mode == KD_TAIL_REVERSE) ? (double)m_q[t] : 0.0;
   const double tiny = 1.1754943508222875e-38;
   const double mps = mp > tiny ? mp : tiny;
   const double ratio = (mode == KD_TAIL && mq > 0.0) ? mq / mps : 0.0;
@@ -395,6 +395,8 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
       L += exp(lqh) * (lqh - lph);
     } else if (mode == KD_TAIL) {
       L += q * (tl - (z - lse));
+    } else if (mode == KD_TAIL_REVERSE) {
+      L += exp(z - lse) * ((z - lse) - tl);
     } else if (mode == KD_FULL) {
       L += q * (tl - z);
     } else {
@@ -404,11 +406,19 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
   }
   L = wave_sum_f64(L);
   if (mode == KD_TAIL && mq > 0.0) L += mq * (log(mq) - log(mps));
+  // tail-token reverse KL: a_v = log(p_v / q_v) - log(m_p / m_q) on S, alpha = -sum_S p a
+  const double tail_log = log(mps) - log(mq > tiny ? mq : tiny);
+  double rev_A = 0.0;
+  if (mode == KD_TAIL_REVERSE) {
+    rev_A = L - tail_log * ((nv > 0) ? exp(lseS - lse) : 0.0);
+    L += mp * tail_log;
+  }
   if (mode == KD_FULL) L += Q * lse;
   const double Lkd = L;  // the distillation term alone (REVERSE's gradient uses it)
 
   double alpha = 0.0;
   if (mode == KD_TAIL) alpha = Q + mq - ratio;
+  if (mode == KD_TAIL_REVERSE) alpha = -rev_A;
   if (mode == KD_FULL) alpha = Q;
   const int y = (labels != nullptr && ce_weight != 0.f) ? labels[t] : -1;
   const bool has_y = y >= 0 && y < V;
@@ -427,6 +437,8 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
         r = exp(z - lseS) - exp(tl - lseq);
       } else if (mode == KD_TAIL) {
         r = -q + ratio * exp(z - lse);
+      } else if (mode == KD_TAIL_REVERSE) {
+        r = exp(z - lse) * ((z - lse - tl) - tail_log);
       } else if (mode == KD_FULL) {
         r = -q;
       } else {
@@ -1193,7 +1205,7 @@ static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, bool ce,
                       LossPlan& p) {
   if (T < 0 || d <= 0 || V <= 0 || K < 1 || K > KMAX || K > V || d % 64 != 0 || d > 16384 || chunk <= 0) return false;
-  if (mode < KD_RENORM || mode > KD_REVERSE) return false;
+  if (mode < KD_RENORM || mode > KD_TAIL_REVERSE) return false;
   if (V > (int64_t)1 << 30 || T > (int64_t)1 << 26) return false;
   p.T = T;
   p.d = d;
@@ -1201,7 +1213,7 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.K = K;
   p.mode = mode;
   p.ce = ce;
-  p.dense = (mode == KD_TAIL || mode == KD_FULL || ce);
+  p.dense = (mode == KD_TAIL || mode == KD_FULL || mode == KD_TAIL_REVERSE || ce);
   p.Kp2 = 1;
   while (p.Kp2 < K) p.Kp2 <<= 1;
   p.Tp = kd_round_up(T > 0 ? T : 1, TT);
@@ -1278,7 +1290,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W,
                                              float* loss_tok, float* lse, float* m_p, float* dh, float* dW,
                                              void* ws, size_t ws_bytes, void* stream) {
   LossPlan p;
-  if (mode < KD_RENORM || mode > KD_REVERSE) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
+  if (mode < KD_RENORM || mode > KD_TAIL_REVERSE) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
   if (!(ce_weight == ce_weight) || ce_weight < 0.f || ce_weight > 3.4e38f)
     return kd_fail(KD_EINVAL, "ce_weight must be finite and >= 0 (got %g)", (double)ce_weight);
   const bool ce = ce_weight != 0.f;
@@ -1288,7 +1300,8 @@ extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W,
                    (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
   if (!loss || !dW || !W) return kd_fail(KD_EINVAL, "null required pointer (loss, W, dW)");
   if (T > 0 && (!h || !idx || !teacher_logp || !dh)) return kd_fail(KD_EINVAL, "null required pointer (h, idx, teacher_logp, dh)");
-  if (T > 0 && mode == KD_TAIL && !m_q) return kd_fail(KD_EINVAL, "KD_TAIL needs m_q");
+  if (T > 0 && (mode == KD_TAIL || mode == KD_TAIL_REVERSE) && !m_q)
+    return kd_fail(KD_EINVAL, "KD_TAIL and KD_TAIL_REVERSE need m_q");
   if (!ws || ws_bytes < p.total)
     return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
