@@ -20,7 +20,9 @@ Sources (cited by title and section, figure or equation):
   (TAIL) and in the paper's own reverse (TAIL_REVERSE) direction.
 * "Unbiased Top-k Estimation for On-Policy Distillation" (Meng et al.),
   abstract and Table 2: reverse KL between the normalized top-k
-  distributions, with the student's own top-16 as the support.
+  distributions, with the student's own top-16 as the support; abstract and
+  Figure 1: the top-k reverse-KL gradient plus a sampled-token tail
+  correction under a stop-gradient (REVERSE_TT).
 * "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a
   Fused Chunked KL Loss", section 3.2, Eq. (2) and Eq. (3): the partial-mass
   forward KL against an unrenormalized top-K teacher and its closed-form
@@ -40,7 +42,7 @@ printed values, closed forms, library routines, finite differences or
 brute force; none is "parity unpinned".
 """
 from .kd_oracle import (  # noqa: F401
-    RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, MODES, MODE_NAMES,
+    RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, REVERSE_TT, MODES, MODE_NAMES,
     logsumexp, student_logits, loss_rows_from_logits, loss_fwd_bwd,
     topk_row, cache_from_logits, cache_build, teacher_logp, adaptive_k_row, kl_hidden_fwd_bwd,
 )

@@ -16,9 +16,10 @@ from __future__ import annotations
 
 import numpy as np
 
-RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE = 0, 1, 2, 3, 4
-MODES = (RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE)
-MODE_NAMES = {RENORM: "renorm", TAIL: "tail", FULL: "full", REVERSE: "reverse", TAIL_REVERSE: "tail_reverse"}
+RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, REVERSE_TT = 0, 1, 2, 3, 4, 5
+MODES = (RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE)   # the modes that need no sampled token
+MODE_NAMES = {RENORM: "renorm", TAIL: "tail", FULL: "full", REVERSE: "reverse", TAIL_REVERSE: "tail_reverse",
+              REVERSE_TT: "reverse_tt"}
 
 # Smallest normal float32: the floor for a student tail mass that rounds to 0
 # while the teacher still has tail mass (the loss is then huge but finite).
@@ -114,6 +115,17 @@ def _loss_row(z: np.ndarray, S: np.ndarray, tl: np.ndarray, m_q: float, mode: in
         A = float(np.sum(p[S] * a))
         dz = -A * p
         dz[S] += p[S] * a
+    elif mode == REVERSE_TT:
+        # Top-k part of the tail-corrected reverse-KL gradient estimator
+        # ("Unbiased Top-k Estimation for On-Policy Distillation", abstract and
+        # Figure 1): the full-vocabulary reverse KL restricted to S,
+        # sum_S p_v (log p_v - log q_v), with its exact gradient
+        # dz_u = p_u (a_u [u in S] - sum_S p a), a = log p - log q.  The
+        # sampled-token correction is added by _sampled_tail_term.
+        a = logp[S] - tl
+        L = float(np.sum(p[S] * a))
+        dz = -L * p
+        dz[S] += p[S] * a
     else:
         raise ValueError(f"unknown mode {mode}")
     return L, dz, lse, m_p
@@ -142,11 +154,33 @@ def _label_term(z: np.ndarray, y: int, lse: float, ce_weight: float):
     return ce_weight * (lse - float(z[y])), g
 
 
-def loss_rows_from_logits(z, idx, tlp, m_q, mode, labels=None, ce_weight=0.0):
+def _sampled_tail_term(z: np.ndarray, y: int, tly: float, lse: float, S: np.ndarray):
+    """Sampled-token tail correction of REVERSE_TT.
+
+    The full reverse KL R = sum_v p_v l_v (l = log p - log q) has gradient
+    sum_v l_v grad p_v; the part outside S equals E_{y ~ p}[1(y not in S)
+    l_y grad log p_y].  With y the token the student sampled in its own
+    rollout, 1(y not in S) l_y grad log p_y (l_y held fixed: the stop-gradient
+    of "Unbiased Top-k Estimation for On-Policy Distillation", Figure 1) is
+    an unbiased estimate of it, and 1(y not in S) l_y of the tail part of R.
+    The paper's equation is not printed; this is the reading taken.
+    Returns (loss term, gradient term) or (0, None).
+    """
+    if y < 0 or np.any(S == y):
+        return 0.0, None
+    ell = float(z[y] - lse) - float(tly)
+    g = -ell * np.exp(z - lse)
+    g[y] += ell
+    return ell, g
+
+
+def loss_rows_from_logits(z, idx, tlp, m_q, mode, labels=None, ce_weight=0.0, tlp_labels=None):
     """Per-token (L, dz, lse, m_p) for logits z [T, V].  Returns arrays.
 
     With labels [T] (int, -1 = none) and ce_weight, each labelled token also
-    carries the hard-label cross-entropy term of _label_term."""
+    carries the hard-label cross-entropy term of _label_term.  For
+    REVERSE_TT, labels are the sampled tokens and tlp_labels [T] the teacher
+    log-probabilities at them (_sampled_tail_term)."""
     z = np.asarray(z, np.float64)
     T, V = z.shape
     L = np.zeros(T)
@@ -157,7 +191,12 @@ def loss_rows_from_logits(z, idx, tlp, m_q, mode, labels=None, ce_weight=0.0):
     for t in range(T):
         S, tl = _support(idx[t], tlp[t])
         L[t], dz[t], lse[t], m_p[t] = _loss_row(z[t], S, tl, float(mq[t]), mode)
-        if labels is not None:
+        if mode == REVERSE_TT and labels is not None:
+            Ls, gs = _sampled_tail_term(z[t], int(labels[t]), float(tlp_labels[t]), lse[t], S)
+            if gs is not None:
+                L[t] += Ls
+                dz[t] += gs
+        elif labels is not None:
             Lc, gc = _label_term(z[t], int(labels[t]), lse[t], float(ce_weight))
             if gc is not None:
                 L[t] += Lc
@@ -165,7 +204,7 @@ def loss_rows_from_logits(z, idx, tlp, m_q, mode, labels=None, ce_weight=0.0):
     return L, dz, lse, m_p
 
 
-def loss_fwd_bwd(h, W, idx, tlp, m_q, mode, scale=None, block=256, labels=None, ce_weight=0.0):
+def loss_fwd_bwd(h, W, idx, tlp, m_q, mode, scale=None, block=256, labels=None, ce_weight=0.0, tlp_labels=None):
     """Fused LM head + top-K KD loss, forward and backward, as dense math.
 
     loss = scale * sum_t L_t; dh = scale * dz W; dW = scale * dz^T h,
@@ -195,7 +234,8 @@ def loss_fwd_bwd(h, W, idx, tlp, m_q, mode, scale=None, block=256, labels=None, 
         z = h[t0:t1] @ W.T
         Lb, dz, lb, mb = loss_rows_from_logits(
             z, idx[t0:t1], tlp[t0:t1], None if mq is None else mq[t0:t1], mode,
-            None if labels is None else labels[t0:t1], ce_weight)
+            None if labels is None else labels[t0:t1], ce_weight,
+            None if tlp_labels is None else tlp_labels[t0:t1])
         L[t0:t1], lse[t0:t1], m_p[t0:t1] = Lb, lb, mb
         dh[t0:t1] = scale * (dz @ W)
         dW += scale * (dz.T @ h[t0:t1])

@@ -16,7 +16,7 @@ import scipy.special
 import torch
 
 import oracle
-from oracle import RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE
+from oracle import RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, REVERSE_TT
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -551,3 +551,61 @@ def test_tail_reverse_at_full_support_is_dense_reverse_kl():
         kl.backward()
         assert abs(L[t] - float(kl.detach())) < 1e-12
         np.testing.assert_allclose(dz[t], zt.grad.numpy(), atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Tail-corrected top-k reverse KL ("Unbiased Top-k Estimation for On-Policy
+# Distillation", abstract and Figure 1)
+# --------------------------------------------------------------------------
+
+def _reverse_kl_torch(z_row, logq_row):
+    from torch.distributions import Categorical, kl_divergence
+    zt = torch.tensor(z_row, requires_grad=True)
+    kl = kl_divergence(Categorical(logits=zt), Categorical(logits=torch.tensor(logq_row)))
+    kl.backward()
+    return float(kl.detach()), zt.grad.numpy()
+
+
+def test_reverse_tt_is_unbiased_over_the_sampled_token():
+    """Averaged over the sampled token y ~ p (every y enumerated, weighted by
+    the student's probability), the loss estimate is the full reverse KL
+    KL(p || q) and the logit gradient is its exact gradient."""
+    r = np.random.default_rng(17)
+    V, K = 23, 5
+    z = r.standard_normal(V) * 1.3
+    zt = r.standard_normal(V) * 1.1
+    logq = zt - scipy.special.logsumexp(zt)
+    S = r.choice(V, size=K, replace=False)
+    p = scipy.special.softmax(z)
+    Lbar, gbar = 0.0, np.zeros(V)
+    for y in range(V):
+        L, dz, _, _ = oracle.loss_rows_from_logits(z[None], S[None], logq[S][None], None, REVERSE_TT,
+                                                   labels=np.array([y]), tlp_labels=np.array([logq[y]]))
+        Lbar += p[y] * L[0]
+        gbar += p[y] * dz[0]
+    kl, grad = _reverse_kl_torch(z, logq)
+    assert abs(Lbar - kl) < 1e-12
+    np.testing.assert_allclose(gbar, grad, atol=1e-13)
+
+
+def test_reverse_tt_sample_inside_support_or_absent_adds_nothing():
+    r = np.random.default_rng(18)
+    V, K = 19, 4
+    z = r.standard_normal((3, V))
+    logq = r.standard_normal((3, V))
+    logq -= scipy.special.logsumexp(logq, axis=1)[:, None]
+    S = np.stack([r.choice(V, size=K, replace=False) for _ in range(3)])
+    tl = np.take_along_axis(logq, S, 1)
+    y = np.array([S[0, 2], -1, S[2, 0]])
+    L0, d0, _, _ = oracle.loss_rows_from_logits(z, S, tl, None, REVERSE_TT)
+    L1, d1, _, _ = oracle.loss_rows_from_logits(z, S, tl, None, REVERSE_TT, labels=y,
+                                                tlp_labels=np.array([logq[0, y[0]], 0.0, logq[2, y[2]]]))
+    np.testing.assert_array_equal(L0, L1)
+    np.testing.assert_array_equal(d0, d1)
+    # full support: the top-k part alone is the dense reverse KL
+    Sfull = np.tile(np.arange(V), (3, 1))
+    Lf, df, _, _ = oracle.loss_rows_from_logits(z, Sfull, logq, None, REVERSE_TT)
+    for t in range(3):
+        kl, grad = _reverse_kl_torch(z[t], logq[t])
+        assert abs(Lf[t] - kl) < 1e-12
+        np.testing.assert_allclose(df[t], grad, atol=1e-13)
