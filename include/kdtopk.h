@@ -68,9 +68,13 @@ typedef enum {
  *   KD_REVERSE L = KL(p_hat || q_hat)                    [TT abstract]
  *   KD_TAIL_REVERSE  L = sum_S p log(p/q) + m_p log(m_p/m_q) [TA abstract: the
  *              reverse KL over the top-k tokens plus a tail token]
+ *   KD_REVERSE_TT    L = sum_S p log(p/q) (+ the sampled-token tail correction of
+ *              kd_topk_loss_fwd_bwd_tt) [TT abstract, Figure 1]
  * The gradient dL/dz is the exact derivative of L; for KD_FULL it is Eq. (3).
  * Tail masses inside logarithms are floored at the smallest normal float. */
-typedef enum { KD_RENORM = 0, KD_TAIL = 1, KD_FULL = 2, KD_REVERSE = 3, KD_TAIL_REVERSE = 4 } kd_mode;
+typedef enum {
+  KD_RENORM = 0, KD_TAIL = 1, KD_FULL = 2, KD_REVERSE = 3, KD_TAIL_REVERSE = 4, KD_REVERSE_TT = 5
+} kd_mode;
 
 /* Bytes of device workspace kd_topk_loss_fwd_bwd needs for these sizes.
  * Linear in T for fixed (d, V, K, chunk).  Returns 0 for invalid sizes. */
@@ -135,6 +139,29 @@ kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int3
                                   const int32_t* labels, float ce_weight,
                                   int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
                                   int32_t chunk, float scale,
+                                  float* loss, float* loss_tok, float* lse, float* m_p,
+                                  float* dh, float* dW,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Tail-corrected top-k reverse KL [TT abstract and Figure 1: the selected
+ * top-k tokens plus the token the student sampled, under a stop-gradient,
+ * give an unbiased estimate of the full reverse-KL gradient].  Per token,
+ * with S the selected tokens (e.g. the student's top-k), a = log p - log q
+ * on S, y the sampled token and l = log p_y - log q_y:
+ *   L_t   = sum_S p a + [y not in S] l          (unbiased for KL(p || q))
+ *   dL/dz = p (a [v in S] - sum_S p a) + [y not in S] l (e_y - p)
+ * (the gradient of sum_S p a plus l log p_y with l held fixed).
+ *
+ * In:  idx, teacher_logp  [T, K]  S and log q on S, full-vocabulary normalised
+ *      sampled            [T] int32  y per token, -1 for none (no correction);
+ *                                    values >= V give a NaN loss
+ *      teacher_logp_sampled [T] fp32 log q_y
+ * Everything else as kd_topk_loss_fwd_bwd with mode KD_REVERSE_TT (whose
+ * workspace size kd_topk_loss_workspace gives). */
+kd_status kd_topk_loss_fwd_bwd_tt(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                  const float* teacher_logp, const int32_t* sampled,
+                                  const float* teacher_logp_sampled,
+                                  int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk, float scale,
                                   float* loss, float* loss_tok, float* lse, float* m_p,
                                   float* dh, float* dW,
                                   void* ws, size_t ws_bytes, void* stream);

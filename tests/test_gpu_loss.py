@@ -250,3 +250,33 @@ def test_label_out_of_range_gives_nan():
     y[5] = V
     g = _run_ce(h, W, idx, tlp, mq, kd.TAIL, 8192, y, 1.0)
     assert np.isnan(g["loss"])
+
+
+# --------------------------------------------------------------------------
+# Tail-corrected top-k reverse KL (kd_topk_loss_fwd_bwd_tt)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", ["tiny", "ragged"])
+def test_reverse_tt_sampled_token_correction(shape):
+    """S = the student's own top-k with teacher log-probs from the full
+    teacher rows; sampled tokens outside S, inside S and absent (-1)."""
+    if shape == "tiny":
+        T, d, V, K, chunk, seed = 64, 64, 1024, 8, 8192, 0
+    else:
+        T, d, V, K, chunk, seed = 300, 128, 2500, 13, 700, 3
+    h, W = synth.student_head(T, d, V, seed=seed)
+    idx, tlp = student_topk_cache(h, W, K, T, V, seed=seed)
+    zt = synth.zipf_teacher_logits(T, V, seed=seed).astype(np.float64)
+    logq = zt - np.array([oracle.logsumexp(r) for r in zt])[:, None]
+    y = synth.token_labels(T, V, seed=seed + 1)
+    y[2::9] = idx[2::9, 1]
+    tly = np.where(y >= 0, logq[np.arange(T), np.maximum(y, 0)], 0.0).astype(np.float32)
+    out = kd.loss_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV), None,
+                          mode=kd.REVERSE_TT, chunk=chunk, labels=torch.from_numpy(y).to(DEV),
+                          labels_teacher_logp=torch.from_numpy(tly).to(DEV))
+    torch.cuda.synchronize()
+    g = {k: getattr(out, k).cpu().numpy() for k in out._fields}
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, None, oracle.REVERSE_TT, labels=y,
+                            tlp_labels=tly)
+    e = _compare(g, r, f"reverse_tt {shape}")
+    print(f"reverse_tt {shape} loss={float(g['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")

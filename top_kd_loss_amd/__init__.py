@@ -18,8 +18,9 @@ from typing import NamedTuple, Optional, Sequence
 
 import torch
 
-RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE = 0, 1, 2, 3, 4
-MODE_BY_NAME = {"renorm": RENORM, "tail": TAIL, "full": FULL, "reverse": REVERSE, "tail_reverse": TAIL_REVERSE}
+RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, REVERSE_TT = 0, 1, 2, 3, 4, 5
+MODE_BY_NAME = {"renorm": RENORM, "tail": TAIL, "full": FULL, "reverse": REVERSE, "tail_reverse": TAIL_REVERSE,
+                "reverse_tt": REVERSE_TT}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdtopk.so")
@@ -37,6 +38,8 @@ _SIGS = {
     "kd_kl_hidden_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "kd_kl_hidden_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _f32,
                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_topk_loss_fwd_bwd_tt": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32,
+                                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -115,10 +118,12 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
                  m_q: Optional[torch.Tensor] = None, mode: int = TAIL, chunk: int = 8192,
                  scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                  out: Optional[LossOut] = None, labels: Optional[torch.Tensor] = None,
-                 ce_weight: float = 0.0) -> LossOut:
+                 ce_weight: float = 0.0, labels_teacher_logp: Optional[torch.Tensor] = None) -> LossOut:
     """Fused LM head + top-K KD loss, forward and backward (kd_topk_loss_fwd_bwd;
     with labels [T] int32 (-1 = none) and ce_weight > 0, kd_topk_loss_fwd_bwd_ce
-    adds the weighted hard-label cross-entropy term)."""
+    adds the weighted hard-label cross-entropy term; with mode REVERSE_TT,
+    labels are the sampled tokens and labels_teacher_logp [T] the teacher's
+    log-probabilities at them, kd_topk_loss_fwd_bwd_tt)."""
     if isinstance(mode, str):
         mode = MODE_BY_NAME[mode]
     dev = h.device
@@ -133,7 +138,10 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
         _need(m_q, "m_q", torch.float32, (T,), dev)
     if labels is not None:
         _need(labels, "labels", torch.int32, (T,), dev)
+    if labels_teacher_logp is not None:
+        _need(labels_teacher_logp, "labels_teacher_logp", torch.float32, (T,), dev)
     ce = ce_weight != 0.0
+    tt = mode == REVERSE_TT and labels is not None
     if scale is None:
         scale = 1.0 / max(T, 1)
     L = lib()
@@ -149,7 +157,13 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
             f32 = dict(dtype=torch.float32, device=dev)
             out = LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
                           torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
-        if ce:
+        if tt:
+            st = L.kd_topk_loss_fwd_bwd_tt(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(labels),
+                                           _ptr(labels_teacher_logp), T, d, V, K, chunk, scale,
+                                           _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
+                                           _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
+                                           _stream(dev))
+        elif ce:
             st = L.kd_topk_loss_fwd_bwd_ce(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
                                            _ptr(labels), ce_weight, T, d, V, K, mode, chunk, scale,
                                            _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
@@ -161,7 +175,7 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
                                         _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
                                         _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
                                         _stream(dev))
-    _check(st, "kd_topk_loss_fwd_bwd_ce" if ce else "kd_topk_loss_fwd_bwd")
+    _check(st, "kd_topk_loss_fwd_bwd_tt" if tt else "kd_topk_loss_fwd_bwd_ce" if ce else "kd_topk_loss_fwd_bwd")
     return out
 
 

@@ -38,7 +38,12 @@ constexpr int KMAX = 1024;
 constexpr int SENT = 0x7fffffff;  // sorted-index sentinel (padding)
 
 // Per-token scalars kept in the workspace (float, stride TOKF).
-enum { TK_LSE = 0, TK_ALPHA = 1, TK_L = 2, TK_MP = 3, TK_Q = 4, TK_LSEQ = 5, TK_NV = 6, TK_ZY = 7, TOKF = 8 };
+enum {
+  TK_LSE = 0, TK_ALPHA = 1, TK_L = 2, TK_MP = 3, TK_Q = 4, TK_LSEQ = 5, TK_NV = 6,
+  TK_ZY = 7,   // logit of the token's label / sampled token
+  TK_YR = 8,   // scaled dz residual at that token when it lies outside S
+  TOKF = 12
+};
 
 // ---------------------------------------------------------------------------
 // Tile ordering: workgroup id -> (m tile, n tile).  Workgroups are handed to
@@ -339,14 +344,19 @@ __global__ __launch_bounds__(256) void k_label_logit(const bf16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // combine: one wavefront per token.  All per-token math in fp64.
 // ---------------------------------------------------------------------------
-// With labels (ce_weight != 0): L += ce_weight (lse - z_y), alpha += ce_weight,
-// r_y -= ce_weight when y is in S; otherwise ylab[t] = y for the pass-2 fixup
-// (-1 when there is none).
+// Tokens y per token (labels; -1 = none):
+//  * cross-entropy term (ce_weight != 0): L += ce_weight (lse - z_y),
+//    alpha += ce_weight, residual -ce_weight at y (added to r_y when y is in S);
+//  * KD_REVERSE_TT (y = the sampled token, tly its teacher log-prob): when y
+//    is outside S, with l = z_y - lse - tly: L += l, alpha -= l, residual +l.
+// ylab[t] = y when y carries a residual outside S (pass 2 writes that entry),
+// else -1.
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int64_t Tp, int mode, float scale,
                                                  const float2* __restrict__ part, const float* __restrict__ zS,
                                                  const int32_t* __restrict__ sidx, const float* __restrict__ stlp,
                                                  const float* __restrict__ m_q, const int32_t* __restrict__ labels,
-                                                 float ce_weight, int64_t V, float* __restrict__ tok,
+                                                 float ce_weight, const float* __restrict__ tly, int64_t V,
+                                                 float* __restrict__ tok,
                                                  float* __restrict__ coef, int32_t* __restrict__ ylab,
                                                  float* __restrict__ loss_tok, float* __restrict__ lse_out,
                                                  float* __restrict__ mp_out) {
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
       L += exp(lqh) * (lqh - lph);
     } else if (mode == KD_TAIL) {
       L += q * (tl - (z - lse));
-    } else if (mode == KD_TAIL_REVERSE) {
+    } else if (mode == KD_TAIL_REVERSE || mode == KD_REVERSE_TT) {
       L += exp(z - lse) * ((z - lse) - tl);
     } else if (mode == KD_FULL) {
       L += q * (tl - z);
@@ -420,14 +430,27 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
   if (mode == KD_TAIL) alpha = Q + mq - ratio;
   if (mode == KD_TAIL_REVERSE) alpha = -rev_A;
   if (mode == KD_FULL) alpha = Q;
-  const int y = (labels != nullptr && ce_weight != 0.f) ? labels[t] : -1;
+  if (mode == KD_REVERSE_TT) alpha = -L;  // -sum_S p a, a = log p - log q
+  const bool tt = mode == KD_REVERSE_TT;
+  const int y = (labels != nullptr && (ce_weight != 0.f || tt)) ? labels[t] : -1;
   const bool has_y = y >= 0 && y < V;
-  const double lam = has_y ? (double)ce_weight : 0.0;
-  if (has_y) {
+  bool y_in_s = false;
+  if (has_y)
+    for (int k = lane; k < nv; k += 64) y_in_s = y_in_s || sidx[t * K + k] == y;
+  y_in_s = __ballot(y_in_s) != 0ull;
+  const double lam = (has_y && !tt) ? (double)ce_weight : 0.0;
+  double yres = 0.0;  // unscaled residual at y outside S
+  if (has_y && !tt) {
     L += lam * (lse - (double)tk[TK_ZY]);
     alpha += lam;
+    yres = -lam;
   }
-  bool y_in_s = false;
+  if (has_y && tt && !y_in_s) {
+    const double ell = ((double)tk[TK_ZY] - lse) - (double)tly[t];
+    L += ell;
+    alpha -= ell;
+    yres = ell;
+  }
   for (int k = lane; k < K; k += 64) {
     double r = 0.0;
     if (k < nv) {
@@ -439,27 +462,26 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
         r = -q + ratio * exp(z - lse);
       } else if (mode == KD_TAIL_REVERSE) {
         r = exp(z - lse) * ((z - lse - tl) - tail_log);
+      } else if (mode == KD_REVERSE_TT) {
+        r = exp(z - lse) * (z - lse - tl);
       } else if (mode == KD_FULL) {
         r = -q;
       } else {
         const double lph = z - lseS, lqh = tl - lseq;
         r = exp(lph) * (lph - lqh - Lkd);
       }
-      if (has_y && sidx[t * K + k] == y) {
-        r -= lam;
-        y_in_s = true;
-      }
+      if (has_y && !tt && sidx[t * K + k] == y) r -= lam;
     }
     coef[t * K + k] = (float)(scale * r);
   }
-  y_in_s = __ballot(y_in_s) != 0ull;
-  if (ylab != nullptr && lane == 0) ylab[t] = (has_y && !y_in_s) ? y : -1;
+  if (ylab != nullptr && lane == 0) ylab[t] = (has_y && !y_in_s && yres != 0.0) ? y : -1;
   if (lane == 0) {
     float* tw = tok + t * TOKF;
     tw[TK_LSE] = (float)lse;
     tw[TK_ALPHA] = (float)(scale * alpha);
     tw[TK_L] = (float)L;
     tw[TK_MP] = (float)mp;
+    tw[TK_YR] = (float)(scale * yres);
     if (loss_tok) loss_tok[t] = (float)L;
     if (lse_out) lse_out[t] = (float)lse;
     if (mp_out) mp_out[t] = (float)mp;
@@ -536,7 +558,7 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
                                                 const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
                                                 const float* __restrict__ coef, const int32_t* __restrict__ ylab,
-                                                float lam_s, bf16_t* __restrict__ dz, int ct, int tt, bf16_t* lds) {
+                                                bf16_t* __restrict__ dz, int ct, int tt, bf16_t* lds) {
   const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
   const int vt = (int)(m0 / VT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -601,12 +623,12 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
       vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
     }
   }
-  // label outside S (cross-entropy term): dz = alpha * exp(z_y - lse) - ce_weight * scale
+  // label / sampled token outside S: dz = alpha * exp(z_y - lse) + its residual
   if (ylab != nullptr && ts < T) {
     const int y = ylab[ts];
     if (y >= m0 && y < vend) {
       const float* tk = tok + ts * TOKF;
-      const float val = tk[TK_ALPHA] * __expf(tk[TK_ZY] - tk[TK_LSE]) - lam_s;
+      const float val = tk[TK_ALPHA] * __expf(tk[TK_ZY] - tk[TK_LSE]) + tk[TK_YR];
       const int vl = y - (int)m0;
       *(bf16_t*)(E + tid * (VT * 2) + (((vl >> 3) ^ zdz_swz(tid)) << 4) + (vl & 7) * 2) = f32_to_bf16(val);
     }
@@ -629,14 +651,14 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
                                                 const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
                                                 const float* __restrict__ coef, const int32_t* __restrict__ ylab,
-                                                float lam_s, bf16_t* __restrict__ dz) {
+                                                bf16_t* __restrict__ dz) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
   if (c0 + (int64_t)(ct + 1) * VT > c1)
-    zdz_tile<true>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, ylab, lam_s, dz, ct, tt, lds);
+    zdz_tile<true>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, ylab, dz, ct, tt, lds);
   else
-    zdz_tile<false>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, ylab, lam_s, dz, ct, tt, lds);
+    zdz_tile<false>(W, h, T, d, V, K, Tp, Cp, c0, c1, nCT, nTT, sidx, starts, tok, zS, coef, ylab, dz, ct, tt, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1205,7 +1227,7 @@ static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, bool ce,
                       LossPlan& p) {
   if (T < 0 || d <= 0 || V <= 0 || K < 1 || K > KMAX || K > V || d % 64 != 0 || d > 16384 || chunk <= 0) return false;
-  if (mode < KD_RENORM || mode > KD_TAIL_REVERSE) return false;
+  if (mode < KD_RENORM || mode > KD_REVERSE_TT) return false;
   if (V > (int64_t)1 << 30 || T > (int64_t)1 << 26) return false;
   p.T = T;
   p.d = d;
@@ -1213,7 +1235,7 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.K = K;
   p.mode = mode;
   p.ce = ce;
-  p.dense = (mode == KD_TAIL || mode == KD_FULL || mode == KD_TAIL_REVERSE || ce);
+  p.dense = (mode == KD_TAIL || mode == KD_FULL || mode == KD_TAIL_REVERSE || mode == KD_REVERSE_TT || ce);
   p.Kp2 = 1;
   while (p.Kp2 < K) p.Kp2 <<= 1;
   p.Tp = kd_round_up(T > 0 ? T : 1, TT);
@@ -1240,7 +1262,7 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_err = o; o = align_up(o + 4);
   p.o_ylab = 0;
-  if (ce) {
+  if (ce || mode == KD_REVERSE_TT) {
     p.o_ylab = o; o = align_up(o + (size_t)(T > 0 ? T : 1) * 4);
   }
   p.o_dz = 0;
@@ -1283,18 +1305,24 @@ extern "C" size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int
     if (e_ != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e_)); \
   } while (0)
 
-extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
-                                             const float* teacher_logp, const float* m_q, const int32_t* labels,
-                                             float ce_weight, int64_t T, int64_t d, int64_t V, int32_t K,
-                                             int32_t mode, int32_t chunk, float scale, float* loss,
-                                             float* loss_tok, float* lse, float* m_p, float* dh, float* dW,
-                                             void* ws, size_t ws_bytes, void* stream) {
+// The loss with optional per-token tokens: labels + ce_weight (cross-entropy
+// term) or, for KD_REVERSE_TT, sampled tokens + their teacher log-probs tly.
+static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* idx, const float* teacher_logp,
+                           const float* m_q, const int32_t* labels, float ce_weight, const float* tly, int64_t T,
+                           int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale, float* loss,
+                           float* loss_tok, float* lse, float* m_p, float* dh, float* dW, void* ws, size_t ws_bytes,
+                           void* stream) {
   LossPlan p;
-  if (mode < KD_RENORM || mode > KD_TAIL_REVERSE) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
+  if (mode < KD_RENORM || mode > KD_REVERSE_TT) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
+  if (mode == KD_REVERSE_TT && ce_weight != 0.f)
+    return kd_fail(KD_EINVAL, "KD_REVERSE_TT takes no cross-entropy term");
+  if (mode == KD_REVERSE_TT && labels != nullptr && T > 0 && !tly)
+    return kd_fail(KD_EINVAL, "sampled tokens need their teacher log-probabilities");
   if (!(ce_weight == ce_weight) || ce_weight < 0.f || ce_weight > 3.4e38f)
     return kd_fail(KD_EINVAL, "ce_weight must be finite and >= 0 (got %g)", (double)ce_weight);
   const bool ce = ce_weight != 0.f;
   if (ce && T > 0 && !labels) return kd_fail(KD_EINVAL, "ce_weight != 0 needs labels");
+  const bool with_y = ce || (mode == KD_REVERSE_TT && labels != nullptr);
   if (!plan_loss(T, d, V, K, mode, chunk, ce, p))
     return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0, and chunk*d, T*d, T*chunk bf16 each < 4 GiB)",
                    (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
@@ -1333,15 +1361,15 @@ extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W,
   KD_LAUNCH(k_pass1, dim3(g1), dim3(TC::NT), P1_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
                      p.nVT, p.nTT, p.Tp, sidx, starts, zS, part);
   KD_LAUNCH_CHECK();
-  int32_t* ylab = ce ? at<int32_t>(ws, p.o_ylab) : nullptr;
-  if (ce) {
+  int32_t* ylab = with_y ? at<int32_t>(ws, p.o_ylab) : nullptr;
+  if (with_y) {
     KD_LAUNCH(k_label_logit, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, (const bf16_t*)h, (const bf16_t*)W,
                        labels, T, d, V, tok, err);
     KD_LAUNCH_CHECK();
   }
   KD_LAUNCH(k_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, (int)K, p.nVT, p.Tp, (int)mode,
-                     scale, part, zS, sidx, stlp, m_q, ce ? labels : nullptr, ce_weight, V, tok, coef, ylab,
-                     loss_tok, lse, m_p);
+                     scale, part, zS, sidx, stlp, m_q, with_y ? labels : nullptr, ce_weight, tly, V, tok, coef,
+                     ylab, loss_tok, lse, m_p);
   KD_LAUNCH_CHECK();
   KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, tok, err, loss);
   KD_LAUNCH_CHECK();
@@ -1355,8 +1383,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W,
       const int nCT = (int)kd_ceil_div(clen, VT);
       const int gz = grid_of(nCT * p.nTT);
       KD_LAUNCH(k_zdz, dim3(gz), dim3(TC::NT), ZDZ_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
-                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, ylab,
-                         ce_weight * scale, dz);
+                         p.Tp, p.Cp, c0, c1, nCT, p.nTT, sidx, starts, tok, zS, coef, ylab, dz);
       KD_LAUNCH_CHECK();
       const int kdh = (int)kd_round_up(clen, 64);
       const int gdh = grid_of(p.nTT * p.nDT);
@@ -1394,8 +1421,29 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
                                           int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale,
                                           float* loss, float* loss_tok, float* lse, float* m_p, float* dh,
                                           float* dW, void* ws, size_t ws_bytes, void* stream) {
-  return kd_topk_loss_fwd_bwd_ce(h, W, idx, teacher_logp, m_q, nullptr, 0.f, T, d, V, K, mode, chunk, scale, loss,
-                                 loss_tok, lse, m_p, dh, dW, ws, ws_bytes, stream);
+  return loss_impl(h, W, idx, teacher_logp, m_q, nullptr, 0.f, nullptr, T, d, V, K, mode, chunk, scale, loss, loss_tok,
+                   lse, m_p, dh, dW, ws, ws_bytes, stream);
+}
+
+extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                             const float* teacher_logp, const float* m_q, const int32_t* labels,
+                                             float ce_weight, int64_t T, int64_t d, int64_t V, int32_t K,
+                                             int32_t mode, int32_t chunk, float scale, float* loss,
+                                             float* loss_tok, float* lse, float* m_p, float* dh, float* dW,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  if (mode == KD_REVERSE_TT) return kd_fail(KD_EINVAL, "KD_REVERSE_TT takes sampled tokens: kd_topk_loss_fwd_bwd_tt");
+  return loss_impl(h, W, idx, teacher_logp, m_q, labels, ce_weight, nullptr, T, d, V, K, mode, chunk, scale, loss,
+                   loss_tok, lse, m_p, dh, dW, ws, ws_bytes, stream);
+}
+
+extern "C" kd_status kd_topk_loss_fwd_bwd_tt(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                             const float* teacher_logp, const int32_t* sampled,
+                                             const float* teacher_logp_sampled, int64_t T, int64_t d, int64_t V,
+                                             int32_t K, int32_t chunk, float scale, float* loss, float* loss_tok,
+                                             float* lse, float* m_p, float* dh, float* dW, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  return loss_impl(h, W, idx, teacher_logp, nullptr, sampled, 0.f, teacher_logp_sampled, T, d, V, K, KD_REVERSE_TT,
+                   chunk, scale, loss, loss_tok, lse, m_p, dh, dW, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
