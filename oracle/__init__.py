@@ -45,4 +45,5 @@ from .kd_oracle import (  # noqa: F401
     RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, REVERSE_TT, MODES, MODE_NAMES,
     logsumexp, student_logits, loss_rows_from_logits, loss_fwd_bwd,
     topk_row, cache_from_logits, cache_build, teacher_logp, adaptive_k_row, kl_hidden_fwd_bwd,
+    quantize_hidden_int8,
 )

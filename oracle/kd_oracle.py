@@ -335,7 +335,24 @@ def cache_build(g, U, b, K, rho=(), block=256):
     return tuple(np.concatenate([o[i] for o in outs], axis=0) for i in range(5))
 
 
-def kl_hidden_fwd_bwd(h, W, g, U, b=None, scale=None, block=256):
+def quantize_hidden_int8(g):
+    """Per-position symmetric int8 code of a hidden state: scale s = max|g| / 127
+    and codes rint(g / s) in [-127, 127], both in float32 ("The Gradient That
+    Top-k Distillation Never Computes", Table A2: the int8 hidden-state cache
+    of d + 4 bytes per position; the quantizer itself is not printed, absmax
+    with round-half-even is the reading taken).  A zero row has s = 0 and
+    zero codes.  Returns (codes int8 [T, d], s float32 [T])."""
+    g = np.asarray(g, np.float32)
+    amax = np.max(np.abs(g), axis=1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint(g / safe[:, None]).astype(np.float32)
+    q = np.clip(q, -127, 127)
+    q[s == 0] = 0
+    return q.astype(np.int8), s
+
+
+def kl_hidden_fwd_bwd(h, W, g, U, b=None, scale=None, block=256, g_scale=None):
     """Exact full-vocabulary KL(q || p) with the teacher rebuilt from a cached
     hidden state: q = softmax(U g + b), p = softmax(W h).
 
@@ -344,8 +361,9 @@ def kl_hidden_fwd_bwd(h, W, g, U, b=None, scale=None, block=256):
     reconstructs the full teacher distribution exactly at 2dV FLOP per
     token.  Per token L = sum_v q_v (log q_v - log p_v), dL/dz = p - q;
     loss = scale * sum_t L (default scale 1/T), dh = scale * dz W,
-    dW = scale * dz^T h.  Returns a dict with loss, loss_tok, lse (student),
-    lse_t (teacher), dh, dW.
+    dW = scale * dz^T h.  With g_scale [T] (an int8 cache: g holds the
+    codes), the teacher logits are g_scale_t * (U g_t) + b.  Returns a dict
+    with loss, loss_tok, lse (student), lse_t (teacher), dh, dW.
     """
     h = np.asarray(h, np.float64)
     W = np.asarray(W, np.float64)
@@ -364,6 +382,8 @@ def kl_hidden_fwd_bwd(h, W, g, U, b=None, scale=None, block=256):
         t1 = min(T, t0 + block)
         z = h[t0:t1] @ W.T
         zt = g[t0:t1] @ U.T
+        if g_scale is not None:
+            zt = zt * np.asarray(g_scale, np.float64)[t0:t1, None]
         if b is not None:
             zt = zt + np.asarray(b, np.float64)[None, :]
         for r in range(t1 - t0):

@@ -609,3 +609,32 @@ def test_reverse_tt_sample_inside_support_or_absent_adds_nothing():
         kl, grad = _reverse_kl_torch(z[t], logq[t])
         assert abs(Lf[t] - kl) < 1e-12
         np.testing.assert_allclose(df[t], grad, atol=1e-13)
+
+
+def test_int8_hidden_cache_codes():
+    """Codes within [-127, 127], the largest magnitude hits 127, every value
+    is reconstructed within half a step, and zero rows stay zero."""
+    r = np.random.default_rng(31)
+    g = (r.standard_normal((9, 70)) * np.array([0.1, 1, 5, 30, 1e-3, 2, 2, 2, 2])[:, None]).astype(np.float32)
+    g[3, 5] = -g[3].__abs__().max() * 1.5  # a negative extreme
+    g[8] = 0.0
+    q, s = oracle.quantize_hidden_int8(g)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert np.all(np.abs(q.astype(np.int32)) <= 127)
+    assert s[8] == 0 and np.all(q[8] == 0)
+    for t in range(8):
+        assert np.abs(q[t].astype(np.int32)).max() == 127
+        err = np.abs(g[t].astype(np.float64) - s[t] * q[t].astype(np.float64))
+        assert err.max() <= 0.5 * s[t] * (1 + 1e-6)
+
+
+def test_kl_hidden_int8_equals_dequantized_teacher():
+    """The int8 path (codes + per-position scale) is the float path on the
+    dequantized hidden states s * codes."""
+    h, W, g, U, b = _hidden_problem(8, T=6, d=5, dt=9, V=29)
+    q, s = oracle.quantize_hidden_int8(g)
+    a = oracle.kl_hidden_fwd_bwd(h, W, q.astype(np.float64), U, b, g_scale=s)
+    ref = oracle.kl_hidden_fwd_bwd(h, W, q.astype(np.float64) * s.astype(np.float64)[:, None], U, b)
+    assert abs(a["loss"] - ref["loss"]) < 1e-13
+    np.testing.assert_allclose(a["dh"], ref["dh"], atol=1e-14)
+    np.testing.assert_allclose(a["lse_t"], ref["lse_t"], atol=1e-13)
