@@ -195,6 +195,29 @@ kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const kd_bf16
                                float* dh, float* dW,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* int8 hidden-state cache [TG Table A2: d + 4 bytes per position]: per
+ * position t, scale[t] = max_j |g[t][j]| / 127 and codes[t][j] =
+ * rint(g[t][j] / scale[t]) clamped to [-127, 127], computed in fp32 with
+ * IEEE division and round-half-even (a zero row: scale 0, zero codes).
+ * In: g [T, d] bf16.  Out: codes [T, d] int8, scale [T] fp32.  No workspace. */
+kd_status kd_hidden_quantize_int8(const kd_bf16* g, int64_t T, int64_t d, int8_t* codes, float* scale,
+                                  void* stream);
+
+/* Bytes of device workspace kd_kl_hidden_int8_fwd_bwd needs (0 for invalid
+ * sizes): kd_kl_hidden_workspace plus 2 * T * dt. */
+size_t kd_kl_hidden_int8_workspace(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk);
+
+/* kd_kl_hidden_fwd_bwd with the teacher hidden states cached as int8 codes
+ * and a per-position scale (kd_hidden_quantize_int8): the teacher logits are
+ * scale[t] * (U codes[t]) + b, exact for the quantized states.  Arguments,
+ * outputs and errors otherwise as kd_kl_hidden_fwd_bwd. */
+kd_status kd_kl_hidden_int8_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int8_t* codes,
+                                    const float* scale_g, const kd_bf16* U, const float* b,
+                                    int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk, float scale,
+                                    float* loss, float* loss_tok, float* lse, float* lse_t,
+                                    float* dh, float* dW,
+                                    void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace kd_topk_cache_build needs.  Returns 0 for
  * invalid sizes. */
 size_t kd_topk_cache_build_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho);

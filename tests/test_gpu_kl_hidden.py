@@ -92,3 +92,37 @@ def test_kl_hidden_full_width_qwen3_8b_teacher_1p7b_student():
                                  b.double().numpy(), block=32)
     e = _check(gout, r, "full width")
     print(f"kl_hidden full width: loss={float(gout['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
+def test_int8_quantize_codes_bit_exact():
+    """GPU codes and scales equal the oracle's on identical bf16 inputs
+    (fp32 decisions on both sides), including a zero row and ties at .5."""
+    T, dt = 37, 320
+    g, _, _ = synth.teacher_head(T, dt, 64, seed=11)
+    g = g.clone()
+    g[3] = 0
+    g[5, :8] = torch.tensor([127.0, 0.5, 1.5, -2.5, 63.5, -63.5, 3.0, -126.5], dtype=torch.bfloat16)
+    codes, sc = kd.hidden_quantize_int8(g.to(DEV))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_hidden_int8(g.float().numpy())
+    np.testing.assert_array_equal(codes.cpu().numpy(), rq)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", ["tiny", "ragged"])
+def test_kl_hidden_int8_cache(shape):
+    if shape == "tiny":
+        T, d, dt, V, chunk, seed = 64, 64, 128, 1024, 8192, 0
+    else:
+        T, d, dt, V, chunk, seed = 300, 128, 64, 2500, 700, 3
+    h, W, g, U, b = _inputs(T, d, dt, V, seed)
+    # the cache comes from the oracle's quantizer (the GPU's is checked bit-exactly above)
+    rq, rs = oracle.quantize_hidden_int8(g.float().numpy())
+    o = kd.kl_hidden_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(rq).to(DEV), U.to(DEV), b.to(DEV), chunk=chunk,
+                             g_scale=torch.from_numpy(rs).to(DEV))
+    torch.cuda.synchronize()
+    gout = {k: getattr(o, k).cpu().numpy() for k in o._fields}
+    r = oracle.kl_hidden_fwd_bwd(synth.as_f64(h), synth.as_f64(W), rq.astype(np.float64), synth.as_f64(U),
+                                 b.double().numpy(), g_scale=rs)
+    e = _check(gout, r, "int8 " + shape)
+    print(f"kl_hidden int8 {shape}: loss={float(gout['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")

@@ -40,6 +40,10 @@ _SIGS = {
                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_loss_fwd_bwd_tt": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32,
                                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_hidden_quantize_int8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "kd_kl_hidden_int8_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32]),
+    "kd_kl_hidden_int8_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _f32,
+                                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -188,26 +192,46 @@ class KlOut(NamedTuple):
     lse_t: torch.Tensor
 
 
+def hidden_quantize_int8(g: torch.Tensor):
+    """int8 hidden-state cache of g [T, d] bf16: (codes int8 [T, d], scale fp32 [T])
+    (kd_hidden_quantize_int8)."""
+    T, d = g.shape
+    _need(g, "g", torch.bfloat16, (T, d), g.device)
+    codes = torch.empty((T, d), dtype=torch.int8, device=g.device)
+    sc = torch.empty(T, dtype=torch.float32, device=g.device)
+    with torch.cuda.device(g.device):
+        _check(lib().kd_hidden_quantize_int8(_ptr(g), T, d, _ptr(codes), _ptr(sc), _stream(g.device)),
+               "kd_hidden_quantize_int8")
+    return codes, sc
+
+
 def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torch.Tensor,
                       b: Optional[torch.Tensor] = None, chunk: int = 8192, scale: Optional[float] = None,
-                      workspace: Optional[torch.Tensor] = None, out: Optional[KlOut] = None) -> KlOut:
+                      workspace: Optional[torch.Tensor] = None, out: Optional[KlOut] = None,
+                      g_scale: Optional[torch.Tensor] = None) -> KlOut:
     """Exact full-vocabulary KL(softmax(U g + b) || softmax(W h)), forward and
     backward, with the teacher rebuilt from its cached hidden state g
-    (kd_kl_hidden_fwd_bwd)."""
+    (kd_kl_hidden_fwd_bwd); g int8 codes with g_scale [T] take the int8 cache
+    (kd_kl_hidden_int8_fwd_bwd)."""
     dev = h.device
     T, d = h.shape
     V = W.shape[0]
     dt = g.shape[1]
+    int8 = g.dtype == torch.int8
     _need(h, "h", torch.bfloat16, (T, d), dev)
     _need(W, "W", torch.bfloat16, (V, d), dev)
-    _need(g, "g", torch.bfloat16, (T, dt), dev)
+    _need(g, "g", torch.int8 if int8 else torch.bfloat16, (T, dt), dev)
     _need(U, "U", torch.bfloat16, (V, dt), dev)
+    if int8:
+        if g_scale is None:
+            raise ValueError("int8 hidden states need g_scale")
+        _need(g_scale, "g_scale", torch.float32, (T,), dev)
     if b is not None:
         _need(b, "b", torch.float32, (V,), dev)
     if scale is None:
         scale = 1.0 / max(T, 1)
     L = lib()
-    ws_bytes = int(L.kd_kl_hidden_workspace(T, d, dt, V, chunk))
+    ws_bytes = int((L.kd_kl_hidden_int8_workspace if int8 else L.kd_kl_hidden_workspace)(T, d, dt, V, chunk))
     if ws_bytes == 0:
         _check(L.kd_kl_hidden_fwd_bwd(None, None, None, None, None, T, d, dt, V, chunk, scale,
                                       None, None, None, None, None, None, None, 0, None), "kd_kl_hidden_fwd_bwd")
@@ -218,10 +242,17 @@ def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torc
             f32 = dict(dtype=torch.float32, device=dev)
             out = KlOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
                         torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
-        st = L.kd_kl_hidden_fwd_bwd(_ptr(h), _ptr(W), _ptr(g), _ptr(U), _ptr(b), T, d, dt, V, chunk, scale,
-                                    _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.lse_t),
-                                    _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(), _stream(dev))
-    _check(st, "kd_kl_hidden_fwd_bwd")
+        if int8:
+            st = L.kd_kl_hidden_int8_fwd_bwd(_ptr(h), _ptr(W), _ptr(g), _ptr(g_scale), _ptr(U), _ptr(b), T, d, dt,
+                                             V, chunk, scale, _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse),
+                                             _ptr(out.lse_t), _ptr(out.dh), _ptr(out.dW), _ptr(workspace),
+                                             workspace.numel(), _stream(dev))
+        else:
+            st = L.kd_kl_hidden_fwd_bwd(_ptr(h), _ptr(W), _ptr(g), _ptr(U), _ptr(b), T, d, dt, V, chunk, scale,
+                                        _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.lse_t),
+                                        _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
+                                        _stream(dev))
+    _check(st, "kd_kl_hidden_int8_fwd_bwd" if int8 else "kd_kl_hidden_fwd_bwd")
     return out
 
 

@@ -756,11 +756,13 @@ __device__ __forceinline__ void add_row_bias(Acc<TC>& acc, const float* bl, int 
     }
 }
 
+// Teacher tiles of an int8 cache (gscale != NULL) scale each token column by
+// its position's scale before the bias.
 template <bool TEACHER, bool MASK>
 __device__ __forceinline__ void lse_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, int64_t K,
-                                         int64_t T, int64_t V, const float* __restrict__ bias, int vt, int tt,
-                                         int64_t Tp, float2* __restrict__ part, float4* __restrict__ partT,
-                                         bf16_t* lds) {
+                                         int64_t T, int64_t V, const float* __restrict__ bias,
+                                         const float* __restrict__ gscale, int vt, int tt, int64_t Tp,
+                                         float2* __restrict__ part, float4* __restrict__ partT, bf16_t* lds) {
   const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
@@ -769,6 +771,15 @@ __device__ __forceinline__ void lse_tile(const bf16_t* __restrict__ A, const bf1
   __syncthreads();  // every wavefront is done with the operand stages
   float* red = (float*)lds;
   if (TEACHER) {
+    if (gscale != nullptr) {
+#pragma unroll
+      for (int fn = 0; fn < TC::FN; ++fn) {
+        const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
+        const float sc = t < T ? gscale[t] : 1.f;
+#pragma unroll
+        for (int fm = 0; fm < TC::FM; ++fm) acc.v[fm][fn] *= sc;
+      }
+    }
     float* bl = (float*)((char*)lds + LP_RED);
     for (int i = threadIdx.x; i < VT; i += TC::NT) bl[i] = (bias != nullptr && m0 + i < V) ? bias[m0 + i] : 0.f;
     __syncthreads();
@@ -831,15 +842,15 @@ __device__ __forceinline__ void lse_tile(const bf16_t* __restrict__ A, const bf1
 template <bool TEACHER>
 __global__ __launch_bounds__(256, 1) void k_lse_pass(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
                                                      int64_t K, int64_t T, int64_t V, const float* __restrict__ bias,
-                                                     int nVT, int nTT, int64_t Tp, float2* __restrict__ part,
-                                                     float4* __restrict__ partT) {
+                                                     const float* __restrict__ gscale, int nVT, int nTT, int64_t Tp,
+                                                     float2* __restrict__ part, float4* __restrict__ partT) {
   extern __shared__ __align__(16) bf16_t lds[];
   int vt, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 8, vt, tt)) return;
   if ((int64_t)(vt + 1) * VT > V)
-    lse_tile<TEACHER, true>(A, B, K, T, V, bias, vt, tt, Tp, part, partT, lds);
+    lse_tile<TEACHER, true>(A, B, K, T, V, bias, gscale, vt, tt, Tp, part, partT, lds);
   else
-    lse_tile<TEACHER, false>(A, B, K, T, V, bias, vt, tt, Tp, part, partT, lds);
+    lse_tile<TEACHER, false>(A, B, K, T, V, bias, gscale, vt, tt, Tp, part, partT, lds);
 }
 
 // Per token (one wavefront): student lse; teacher lse_t and H_t = E_q[zt] -
@@ -896,7 +907,8 @@ constexpr int TQ_LDS = (TC::BN / 2) * TC::BM * 4;  // 128 tokens x 256 vocabular
 static_assert(TQ_LDS >= TC::LDS_BYTES, "q staging reuses the operand stages");
 
 __global__ __launch_bounds__(256, 1) void k_teacher_q(const bf16_t* __restrict__ U, const bf16_t* __restrict__ g,
-                                                      const float* __restrict__ bias, int64_t T, int64_t dt,
+                                                      const float* __restrict__ bias,
+                                                      const float* __restrict__ gscale, int64_t T, int64_t dt,
                                                       int64_t Cp, int64_t c0, int64_t c1, int nCT, int nTT,
                                                       const float* __restrict__ tok, float* __restrict__ qbuf) {
   extern __shared__ __align__(16) bf16_t lds[];
@@ -944,8 +956,10 @@ __global__ __launch_bounds__(256, 1) void k_teacher_q(const bf16_t* __restrict__
       f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
       if (t < T) {
         const float nl = -tok[t * TOKF + TK_LSEQ] * KD_LOG2E;
+        const float sc = gscale != nullptr ? gscale[t] : 1.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = in[e] ? __builtin_amdgcn_exp2f(fmaf(x[e] + bv[e], KD_LOG2E, nl)) : 0.f;
+        for (int e = 0; e < 4; ++e)
+          q[e] = in[e] ? __builtin_amdgcn_exp2f(fmaf(x[e] * sc + bv[e], KD_LOG2E, nl)) : 0.f;
       }
       if (m0 + 4 * c < c0 + Cp) *(f32x4*)(qbuf + t * Cp + (v - c0)) = q;
     }
@@ -1054,6 +1068,35 @@ __global__ __launch_bounds__(256) void k_kl_finish(int64_t T, int nVT, int64_t T
   if (loss_tok) loss_tok[t] = L;
   if (lse_out) lse_out[t] = tk[TK_LSE];
   if (lset_out) lset_out[t] = tk[TK_LSEQ];
+}
+
+// int8 hidden-state cache: per position s = max|g| / 127 and codes rint(g / s)
+// clamped to [-127, 127], in fp32 with IEEE division (a zero row: s = 0, zero
+// codes).  One workgroup per position.
+__global__ __launch_bounds__(256) void k_quantize_int8(const bf16_t* __restrict__ g, int64_t d,
+                                                       int8_t* __restrict__ codes, float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const bf16_t* gr = g + t * d;
+  float amax = 0.f;
+  for (int64_t j = threadIdx.x; j < d; j += 256) amax = fmaxf(amax, fabsf(bf16_to_f32(gr[j])));
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 127.f);
+  for (int64_t j = threadIdx.x; j < d; j += 256) {
+    float q = 0.f;
+    if (s > 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(bf16_to_f32(gr[j]), s)), -127.f), 127.f);
+    codes[t * d + j] = (int8_t)q;
+  }
+  if (threadIdx.x == 0) scale[t] = s;
+}
+
+// int8 codes -> bf16 (exact: |code| <= 127 fits bf16's 8 significant bits).
+__global__ void k_codes_to_bf16(const int8_t* __restrict__ codes, int64_t n, bf16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = (bf16_t)(__float_as_uint((float)codes[i]) >> 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -1454,10 +1497,11 @@ namespace {
 struct KlPlan {
   int64_t Tp, C, Cp;
   int nVT, nTT, nDT, nchunks;
-  size_t o_tok, o_part, o_partT, o_partQZ, o_q, o_dz, total;
+  size_t o_tok, o_part, o_partT, o_partQZ, o_q, o_dz, o_g, total;
 };
 
-static bool plan_kl(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk, KlPlan& p) {
+// int8: room for the bf16 copy of the codes.
+static bool plan_kl(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk, bool int8, KlPlan& p) {
   if (T < 0 || d <= 0 || dt <= 0 || V <= 0 || d % 64 != 0 || dt % 64 != 0 || d > 16384 || dt > 16384 || chunk <= 0)
     return false;
   if (V > (int64_t)1 << 30 || T > (int64_t)1 << 26) return false;
@@ -1480,6 +1524,10 @@ static bool plan_kl(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk, 
   p.o_partQZ = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
   p.o_q = o; o = align_up(o + (size_t)p.Tp * p.Cp * 4);
   p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
+  p.o_g = 0;
+  if (int8) {
+    p.o_g = o; o = align_up(o + (size_t)(T > 0 ? T : 1) * dt * 2);
+  }
   p.total = o;
   return true;
 }
@@ -1488,20 +1536,42 @@ static bool plan_kl(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk, 
 
 extern "C" size_t kd_kl_hidden_workspace(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk) {
   KlPlan p;
-  if (!plan_kl(T, d, dt, V, chunk, p)) return 0;
+  if (!plan_kl(T, d, dt, V, chunk, false, p)) return 0;
   return p.total;
 }
 
-extern "C" kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, const kd_bf16* U,
-                                          const float* b, int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk,
-                                          float scale, float* loss, float* loss_tok, float* lse, float* lse_t,
-                                          float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
+extern "C" size_t kd_kl_hidden_int8_workspace(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk) {
   KlPlan p;
-  if (!plan_kl(T, d, dt, V, chunk, p))
+  if (!plan_kl(T, d, dt, V, chunk, true, p)) return 0;
+  return p.total;
+}
+
+extern "C" kd_status kd_hidden_quantize_int8(const kd_bf16* g, int64_t T, int64_t d, int8_t* codes, float* scale,
+                                             void* stream) {
+  if (T < 0 || d <= 0) return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld", (long long)T, (long long)d);
+  if (T == 0) return KD_OK;
+  if (!g || !codes || !scale) return kd_fail(KD_EINVAL, "null required pointer");
+  if (T > 0x7fffffffLL) return kd_fail(KD_EINVAL, "T too large");
+  hipStream_t s = (hipStream_t)stream;
+  KD_LAUNCH(k_quantize_int8, dim3((unsigned)T), dim3(256), 0, s, (const bf16_t*)g, d, codes, scale);
+  KD_LAUNCH_CHECK();
+  return KD_OK;
+}
+
+// The KL with the teacher hidden states as bf16 (g) or as int8 codes with a
+// per-position scale (codes8, gscale).
+static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, const int8_t* codes8,
+                         const float* gscale, const kd_bf16* U, const float* b, int64_t T, int64_t d, int64_t dt,
+                         int64_t V, int32_t chunk, float scale, float* loss, float* loss_tok, float* lse,
+                         float* lse_t, float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
+  KlPlan p;
+  const bool int8 = codes8 != nullptr || gscale != nullptr;
+  if (!plan_kl(T, d, dt, V, chunk, int8, p))
     return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld dt=%lld V=%lld chunk=%d (need d%%64==0, dt%%64==0, d,dt<=16384, chunk>0, and chunk*d, T*d bf16 and T*chunk fp32 each < 4 GiB)",
                    (long long)T, (long long)d, (long long)dt, (long long)V, (int)chunk);
   if (!loss || !dW || !W || !U) return kd_fail(KD_EINVAL, "null required pointer (loss, W, U, dW)");
-  if (T > 0 && (!h || !g || !dh)) return kd_fail(KD_EINVAL, "null required pointer (h, g, dh)");
+  if (T > 0 && (!h || !dh || (!int8 && !g) || (int8 && (!codes8 || !gscale))))
+    return kd_fail(KD_EINVAL, "null required pointer (h, dh and g, or the int8 codes and their scales)");
   if (!ws || ws_bytes < p.total)
     return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
@@ -1517,11 +1587,16 @@ extern "C" kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   float* partQZ = at<float>(ws, p.o_partQZ);
   float* qbuf = at<float>(ws, p.o_q);
   bf16_t* dz = at<bf16_t>(ws, p.o_dz);
+  if (int8) {
+    bf16_t* gb = at<bf16_t>(ws, p.o_g);
+    KD_LAUNCH(k_codes_to_bf16, dim3(1024), dim3(256), 0, s, codes8, T * dt, gb);
+    g = (const kd_bf16*)gb;
+  }
   const int g1 = grid_of(p.nVT * p.nTT);
   KD_LAUNCH(k_lse_pass<false>, dim3(g1), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)W, (const bf16_t*)h, d, T, V,
-                     (const float*)nullptr, p.nVT, p.nTT, p.Tp, part, (float4*)nullptr);
+                     (const float*)nullptr, (const float*)nullptr, p.nVT, p.nTT, p.Tp, part, (float4*)nullptr);
   KD_LAUNCH(k_lse_pass<true>, dim3(g1), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)U, (const bf16_t*)g, dt, T, V,
-                     b, p.nVT, p.nTT, p.Tp, (float2*)nullptr, partT);
+                     b, gscale, p.nVT, p.nTT, p.Tp, (float2*)nullptr, partT);
   KD_LAUNCH_CHECK();
   KD_LAUNCH(k_kl_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, p.nVT, p.Tp, scale, part, partT, tok);
   KD_LAUNCH_CHECK();
@@ -1531,7 +1606,7 @@ extern "C" kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
     const int64_t clen = c1 - c0;
     const int nCT = (int)kd_ceil_div(clen, VT);
     const int gz = grid_of(nCT * p.nTT);
-    KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), TQ_LDS, s, (const bf16_t*)U, (const bf16_t*)g, b, T, dt, p.Cp, c0,
+    KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), TQ_LDS, s, (const bf16_t*)U, (const bf16_t*)g, b, gscale, T, dt, p.Cp, c0,
                        c1, nCT, p.nTT, (const float*)tok, qbuf);
     KD_LAUNCH(k_zdz_kl, dim3(gz), dim3(TC::NT), ZK_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0,
                        c1, nCT, p.nTT, (const float*)tok, (const float*)qbuf, partQZ, dz);
@@ -1550,4 +1625,21 @@ extern "C" kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
   KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, (const float*)tok, (const int32_t*)nullptr, loss);
   KD_LAUNCH_CHECK();
   return KD_OK;
+}
+
+extern "C" kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, const kd_bf16* U,
+                                          const float* b, int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk,
+                                          float scale, float* loss, float* loss_tok, float* lse, float* lse_t,
+                                          float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
+  return kl_impl(h, W, g, nullptr, nullptr, U, b, T, d, dt, V, chunk, scale, loss, loss_tok, lse, lse_t, dh, dW, ws,
+                 ws_bytes, stream);
+}
+
+extern "C" kd_status kd_kl_hidden_int8_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int8_t* codes,
+                                               const float* gscale, const kd_bf16* U, const float* b, int64_t T,
+                                               int64_t d, int64_t dt, int64_t V, int32_t chunk, float scale,
+                                               float* loss, float* loss_tok, float* lse, float* lse_t, float* dh,
+                                               float* dW, void* ws, size_t ws_bytes, void* stream) {
+  return kl_impl(h, W, nullptr, codes, gscale, U, b, T, d, dt, V, chunk, scale, loss, loss_tok, lse, lse_t, dh, dW,
+                 ws, ws_bytes, stream);
 }
