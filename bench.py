@@ -240,7 +240,9 @@ def main():
         res["other_mode"] = {"mode": {kd.RENORM: "renorm", kd.TAIL: "tail"}[other], "ms_per_step": ms2,
                              "tokens_per_s": T / (ms2 * 1e-3), "mfma_frac_step": cr2 / (ms2 * 1e-3) / PEAK_BF16}
         log(f"[bench] other mode: {ms2:.3f} ms/step")
-        res["kl_hidden"] = bench_kl_hidden(torch, kd, synth, dev, hd, Wd, max(3, args.steps // 2))
+        res["more_modes"] = bench_more_modes(torch, kd, synth, dev, hd, Wd, idx, tlp, mq, max(3, args.steps // 4))
+        log(f"[bench] more modes: {res['more_modes']}")
+        res["kl_hidden"] = bench_kl_hidden(torch, kd, synth, dev, hd, Wd, max(3, args.steps // 4))
         log(f"[bench] kl_hidden: {res['kl_hidden']}")
         del hd, Wd
         torch.cuda.empty_cache()
@@ -257,6 +259,33 @@ def main():
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def bench_more_modes(torch, kd, synth, dev, hd, Wd, idx, tlp, mq, steps):
+    """Step time of the other objectives on the same workload: the tail-token
+    reverse KL, the tail-corrected reverse KL (synthetic sampled tokens and
+    teacher log-probs at them), and the tail-aware loss plus a 0.1-weighted
+    hard-label cross-entropy term (synthetic labels)."""
+    T, d, V, K, chunk = CFG["T"], CFG["d"], CFG["V"], CFG["K"], CFG["chunk"]
+    y = torch.from_numpy(synth.token_labels(T, V, seed=5)).to(dev)
+    tly = torch.full((T,), -12.0, dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = kd.LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
+                     torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
+    cases = {
+        "tail_reverse": (kd.TAIL_REVERSE, {}),
+        "reverse_tt": (kd.REVERSE_TT, {"labels": y, "labels_teacher_logp": tly}),
+        "tail+ce0.1": (kd.TAIL, {"labels": y, "ce_weight": 0.1}),
+    }
+    res = {}
+    for name, (md, kw) in cases.items():
+        ws = torch.empty(kd.loss_workspace_bytes(T, d, V, K, md, chunk, kw.get("ce_weight", 0.0)),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: kd.loss_fwd_bwd(hd, Wd, idx, tlp, mq, mode=md, chunk=chunk, workspace=ws, out=out, **kw)
+        ms = time_steps(torch, fn, steps, 1)
+        res[name] = {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3)}
+        del ws
+    return res
 
 
 def bench_kl_hidden(torch, kd, synth, dev, hd, Wd, steps):
