@@ -33,6 +33,8 @@ Sources (cited by title and section, figure or equation):
 * "The Gradient That Top-k Distillation Never Computes", Figure 3 (bottom):
   the hidden-state teacher cache, whose head reconstruction gives the exact
   full-vocabulary KL.
+* "The Gradient That Top-k Distillation Never Computes", abstract and
+  Table 1: the teacher is recoverable from k >= d + 1 cached log-probs.
 * The hard-label cross-entropy term that "The Gradient That Top-k
   Distillation Never Computes" (abstract) trains with or without, added
   with a weight to any of the four distillation losses.
@@ -45,5 +47,5 @@ from .kd_oracle import (  # noqa: F401
     RENORM, TAIL, FULL, REVERSE, TAIL_REVERSE, REVERSE_TT, MODES, MODE_NAMES,
     logsumexp, student_logits, loss_rows_from_logits, loss_fwd_bwd,
     topk_row, cache_from_logits, cache_build, teacher_logp, adaptive_k_row, kl_hidden_fwd_bwd,
-    quantize_hidden_int8,
+    quantize_hidden_int8, recover_teacher_hidden,
 )

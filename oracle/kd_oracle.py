@@ -397,3 +397,29 @@ def kl_hidden_fwd_bwd(h, W, g, U, b=None, scale=None, block=256, g_scale=None):
         dh[t0:t1] = scale * (dz @ W)
         dW += scale * (dz.T @ h[t0:t1])
     return {"loss": scale * float(np.sum(L)), "loss_tok": L, "lse": lse, "lse_t": lse_t, "dh": dh, "dW": dW}
+
+
+def recover_teacher_hidden(idx, tlp, U, b=None):
+    """Teacher hidden state and log-normalizer from k cached log-probabilities
+    ("The Gradient That Top-k Distillation Never Computes", abstract and
+    Table 1: the retained set determines the teacher's distribution once
+    k >= d + 1).  Cached log q_v = U_v g + b_v - c on S, with c the teacher's
+    logsumexp, is linear in (g, c): the least-squares solution of
+    [U_S, -1] (g; c) = log q_S - b_S (numpy's lstsq, the minimum-norm one
+    when k < d + 1, where it is not unique).  Returns (g_hat [T, d],
+    c_hat [T]) in float64.
+    """
+    idx = np.asarray(idx)
+    tlp = np.asarray(tlp, np.float64)
+    U = np.asarray(U, np.float64)
+    T, k = idx.shape
+    d = U.shape[1]
+    g_hat = np.zeros((T, d))
+    c_hat = np.zeros(T)
+    for t in range(T):
+        S = idx[t].astype(np.int64)
+        A = np.concatenate([U[S], -np.ones((k, 1))], axis=1)
+        y = tlp[t] - (np.asarray(b, np.float64)[S] if b is not None else 0.0)
+        x = np.linalg.lstsq(A, y, rcond=None)[0]
+        g_hat[t], c_hat[t] = x[:d], x[d]
+    return g_hat, c_hat

@@ -638,3 +638,33 @@ def test_kl_hidden_int8_equals_dequantized_teacher():
     assert abs(a["loss"] - ref["loss"]) < 1e-13
     np.testing.assert_allclose(a["dh"], ref["dh"], atol=1e-14)
     np.testing.assert_allclose(a["lse_t"], ref["lse_t"], atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Teacher recovery from k cached log-probabilities ("The Gradient That Top-k
+# Distillation Never Computes", abstract and Table 1: exact from k = d + 1)
+# --------------------------------------------------------------------------
+
+def test_teacher_recovery_transition_at_d_plus_1():
+    r = np.random.default_rng(41)
+    T, d, V = 4, 12, 200
+    U = r.standard_normal((V, d)) / np.sqrt(d)
+    b = 0.3 * r.standard_normal(V)
+    g = r.standard_normal((T, d))
+    z = g @ U.T + b[None, :]
+    logq = z - scipy.special.logsumexp(z, axis=1)[:, None]
+    order = np.argsort(-z, axis=1)
+    for k, exact in ((d - 1, False), (d, False), (d + 1, True), (3 * d, True)):
+        idx = order[:, :k]
+        tl = np.take_along_axis(logq, idx, 1)
+        gh, ch = oracle.recover_teacher_hidden(idx, tl, U, b)
+        zh = gh @ U.T + b[None, :]
+        logqh = zh - scipy.special.logsumexp(zh, axis=1)[:, None]
+        kl = np.sum(np.exp(logq) * (logq - logqh), axis=1)
+        if exact:
+            np.testing.assert_allclose(gh, g, atol=1e-9)
+            np.testing.assert_allclose(ch, scipy.special.logsumexp(z, axis=1), atol=1e-9)
+            assert kl.max() < 1e-15
+        else:
+            # below d + 1 the retained set does not determine the teacher
+            assert kl.min() > 1e-6, (k, kl)
