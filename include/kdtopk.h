@@ -257,6 +257,24 @@ kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K,
                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Teacher hidden-state recovery from k cached log-probabilities [TG abstract
+ * and Table 1: the retained set determines the teacher's distribution from
+ * k = d + 1 on].  Per position t, the least-squares solution of
+ *   [U_S, -1] (g; c) = teacher_logp_S - b_S,   S = idx[t, :]
+ * in fp64 (Householder QR), g the teacher's final hidden state and c its
+ * logsumexp; softmax(U g + b) is then the full teacher distribution.
+ *
+ * In:  idx          [T, k] int32  cached indices (distinct, in [0, V))
+ *      teacher_logp [T, k] fp32   cached teacher log-probabilities at idx
+ *      U            [V, d] bf16   teacher LM-head rows;  b [V] fp32 or NULL
+ *      d + 1 <= k <= V and (d + 2) * (k rounded up to odd) <= 19968
+ *      (KD_EUNSUPPORTED otherwise: one workgroup holds the system in LDS)
+ * Out: g_hat [T, d] fp32, c_hat [T] fp32; NaN for a position whose indices
+ *      are out of range (and non-finite values when [U_S, -1] is singular). */
+kd_status kd_teacher_recover(const int32_t* idx, const float* teacher_logp, const kd_bf16* U, const float* b,
+                             int64_t T, int64_t d, int64_t V, int32_t k, float* g_hat, float* c_hat,
+                             void* stream);
+
 /* Message describing the last non-KD_OK status returned on this thread. */
 const char* kd_last_error(void);
 

@@ -44,6 +44,7 @@ _SIGS = {
     "kd_kl_hidden_int8_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "kd_kl_hidden_int8_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _f32,
                                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_teacher_recover": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -254,6 +255,26 @@ def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torc
                                         _stream(dev))
     _check(st, "kd_kl_hidden_int8_fwd_bwd" if int8 else "kd_kl_hidden_fwd_bwd")
     return out
+
+
+def teacher_recover(idx: torch.Tensor, teacher_logp: torch.Tensor, U: torch.Tensor,
+                    b: Optional[torch.Tensor] = None):
+    """Teacher hidden state and logsumexp from k >= d + 1 cached log-probs
+    (kd_teacher_recover): returns (g_hat [T, d] fp32, c_hat [T] fp32)."""
+    dev = idx.device
+    T, k = idx.shape
+    V, d = U.shape
+    _need(idx, "idx", torch.int32, (T, k), dev)
+    _need(teacher_logp, "teacher_logp", torch.float32, (T, k), dev)
+    _need(U, "U", torch.bfloat16, (V, d), dev)
+    if b is not None:
+        _need(b, "b", torch.float32, (V,), dev)
+    g_hat = torch.empty((T, d), dtype=torch.float32, device=dev)
+    c_hat = torch.empty(T, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().kd_teacher_recover(_ptr(idx), _ptr(teacher_logp), _ptr(U), _ptr(b), T, d, V, k,
+                                        _ptr(g_hat), _ptr(c_hat), _stream(dev)), "kd_teacher_recover")
+    return g_hat, c_hat
 
 
 class CacheOut(NamedTuple):

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkdtopk.so")
-SOURCES = ["loss.hip", "cache.hip", "abi_common.cpp"]
+SOURCES = ["loss.hip", "cache.hip", "recover.hip", "abi_common.cpp"]
 ARCH = "gfx950"
 
 
