@@ -158,7 +158,8 @@ def main():
     ap.add_argument("--mode", default="tail", choices=["renorm", "tail", "full", "reverse"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the RENORM line and the cache-build line")
-    ap.add_argument("--memscan", action="store_true", help="peak memory vs T at d=2560, K=64 (4K..32K)")
+    ap.add_argument("--no-memscan", action="store_true",
+                    help="skip the long-context line (peak memory and tokens/s vs T at d=2560, K=64, 4K..32K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device copies of 1 GiB (fp32) for HBM counter calibration")
     args = ap.parse_args()
@@ -249,7 +250,7 @@ def main():
         res["cache_build"] = bench_cache_build(torch, kd, synth, dev)
         log(f"[bench] cache build: {res['cache_build']}")
 
-    if args.memscan:
+    if not args.no_memscan and not args.no_extras:
         res["memscan"] = memscan(torch, kd, dev)
 
     if not args.no_cpu_baseline:
@@ -335,7 +336,8 @@ def bench_cache_build(torch, kd, synth, dev, steps=3):
 
 
 def memscan(torch, kd, dev):
-    """Peak allocated memory of one fused step vs T (d=2560, V=151,936, K=64, tail mode)."""
+    """Long-context, Qwen3-4B-shaped head (d=2560, V=151,936, K=64, tail mode):
+    peak allocated memory of one fused step and its tokens/s vs T."""
     d, V, K = 2560, 151936, 64
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
@@ -352,8 +354,12 @@ def memscan(torch, kd, dev):
         t0 = time.time()
         kd.loss_fwd_bwd(h, W, idx, tlp, mq, mode=kd.TAIL, chunk=8192)
         torch.cuda.synchronize()
-        out[str(T)] = {"peak_bytes_above_W": torch.cuda.max_memory_allocated() - base,
-                       "seconds": time.time() - t0}
+        first = time.time() - t0
+        peak = torch.cuda.max_memory_allocated() - base
+        ms = time_steps(torch, lambda: kd.loss_fwd_bwd(h, W, idx, tlp, mq, mode=kd.TAIL, chunk=8192), 2, 0)
+        out[str(T)] = {"peak_bytes_above_W": peak, "first_call_s": first, "ms_per_step": ms,
+                       "tokens_per_s": T / (ms * 1e-3),
+                       "mfma_frac_step": 6 * T * d * V / (ms * 1e-3) / PEAK_BF16}
         log(f"[bench] memscan T={T}: {out[str(T)]}")
         del h, idx, tlp, mq
     return out

@@ -10,7 +10,8 @@ import numpy as np
 import oracle
 
 
-def sampled_reference(h64, W64, idx, tlp, mq, mode, tok_rows, vocab_rows, scale=None, block=256, log=None):
+def sampled_reference(h64, W64, idx, tlp, mq, mode, tok_rows, vocab_rows, scale=None, block=256, log=None,
+                      labels=None, ce_weight=0.0, tlp_labels=None):
     T, d = h64.shape
     if scale is None:
         scale = 1.0 / T
@@ -24,7 +25,10 @@ def sampled_reference(h64, W64, idx, tlp, mq, mode, tok_rows, vocab_rows, scale=
     for t0 in range(0, T, block):
         t1 = min(T, t0 + block)
         z = oracle.student_logits(h64[t0:t1], W64)
-        Lb, dz, lb, mb = oracle.loss_rows_from_logits(z, idx[t0:t1], tlp[t0:t1], None if mq is None else mq[t0:t1], mode)
+        Lb, dz, lb, mb = oracle.loss_rows_from_logits(
+            z, idx[t0:t1], tlp[t0:t1], None if mq is None else mq[t0:t1], mode,
+            None if labels is None else labels[t0:t1], ce_weight,
+            None if tlp_labels is None else tlp_labels[t0:t1])
         L[t0:t1], lse[t0:t1], mp[t0:t1] = Lb, lb, mb
         dW += scale * (dz[:, vocab_rows].T @ h64[t0:t1])
         for j, t in enumerate(tok_rows):

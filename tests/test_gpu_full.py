@@ -84,6 +84,32 @@ def test_qwen3_1p7b_head_full_size(qwen17_head, mode):
         assert np.all(g["dW"][free] == 0.0)
 
 
+@pytest.mark.timeout(400)
+def test_qwen3_1p7b_head_label_term_and_sampled_token_correction(qwen17_head):
+    """The cross-entropy term (weight 0.2) on the tail-aware loss, and the
+    tail-corrected reverse KL with synthetic sampled tokens, at full size."""
+    T, d, V, K, h, W, idx, tlp, mq, h64, W64 = qwen17_head
+    y = synth.token_labels(T, V, seed=9)
+    toks, voc = _sample_rows(T, V, idx, np.random.default_rng(2))
+    out = kd.loss_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV),
+                          torch.from_numpy(mq).to(DEV), mode=kd.TAIL, chunk=CHUNK,
+                          labels=torch.from_numpy(y).to(DEV), ce_weight=0.2)
+    torch.cuda.synchronize()
+    g = {k: getattr(out, k).cpu().numpy() for k in out._fields}
+    r = sampled_reference(h64, W64, idx, tlp, mq, kd.TAIL, toks, voc, log=say, labels=y, ce_weight=0.2)
+    _check(g, r, toks, voc, "T=4096 V=151936 K=15 tail + 0.2 CE")
+    # sampled tokens and a stand-in teacher log-prob at them (-14: far in the tail, so the
+    # per-token correction log p_y - log q_y is mostly positive and the mean loss is not near 0)
+    tly = np.full(T, -14.0, np.float32)
+    out = kd.loss_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV), None,
+                          mode=kd.REVERSE_TT, chunk=CHUNK, labels=torch.from_numpy(y).to(DEV),
+                          labels_teacher_logp=torch.from_numpy(tly).to(DEV))
+    torch.cuda.synchronize()
+    g = {k: getattr(out, k).cpu().numpy() for k in out._fields}
+    r = sampled_reference(h64, W64, idx, tlp, None, oracle.REVERSE_TT, toks, voc, log=say, labels=y, tlp_labels=tly)
+    _check(g, r, toks, voc, "T=4096 V=151936 K=15 reverse_tt")
+
+
 @pytest.mark.timeout(500)
 def test_llama_1b_head_full_mode_k256():
     T, d, V, K = 8192, 2048, 128256, 256

@@ -1053,15 +1053,23 @@ __global__ __launch_bounds__(256, 1) void k_zdz_kl(const bf16_t* __restrict__ W,
     zdz_kl_tile<false>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, ct, tt, lds);
 }
 
-// L_t = H_t - sum_v q_v z_v + lse, one thread per token (partials summed in
-// vocabulary-tile order).
-__global__ __launch_bounds__(256) void k_kl_finish(int64_t T, int nVT, int64_t Tp, const float* __restrict__ partQZ,
-                                                   float* __restrict__ tok, float* __restrict__ loss_tok,
-                                                   float* __restrict__ lse_out, float* __restrict__ lset_out) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
+// L_t = H_t - sum_v q_v z_v + lse.  A workgroup covers 32 tokens; its 32
+// groups of 32 threads each sum every 32nd vocabulary tile (coalesced across
+// tokens), and the group sums are added in group order (deterministic).
+__global__ __launch_bounds__(1024) void k_kl_finish(int64_t T, int nVT, int64_t Tp, const float* __restrict__ partQZ,
+                                                    float* __restrict__ tok, float* __restrict__ loss_tok,
+                                                    float* __restrict__ lse_out, float* __restrict__ lset_out) {
+  __shared__ double red[32][33];
+  const int tl = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int64_t t = (int64_t)blockIdx.x * 32 + tl;
+  double part = 0.0;
+  if (t < T)
+    for (int vt = grp; vt < nVT; vt += 32) part += (double)partQZ[(int64_t)vt * Tp + t];
+  red[grp][tl] = part;
+  __syncthreads();
+  if (grp != 0 || t >= T) return;
   double qz = 0.0;
-  for (int vt = 0; vt < nVT; ++vt) qz += (double)partQZ[(int64_t)vt * Tp + t];
+  for (int g = 0; g < 32; ++g) qz += red[g][tl];
   float* tk = tok + t * TOKF;
   const float L = (float)((double)tk[TK_L] - qz + (double)tk[TK_LSE]);
   tk[TK_L] = L;
@@ -1620,7 +1628,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
                        dh, dW);
     KD_LAUNCH_CHECK();
   }
-  KD_LAUNCH(k_kl_finish, dim3((unsigned)kd_ceil_div(T, 256)), dim3(256), 0, s, T, p.nVT, p.Tp, (const float*)partQZ,
+  KD_LAUNCH(k_kl_finish, dim3((unsigned)kd_ceil_div(T, 32)), dim3(1024), 0, s, T, p.nVT, p.Tp, (const float*)partQZ,
                      tok, loss_tok, lse, lse_t);
   KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, (const float*)tok, (const int32_t*)nullptr, loss);
   KD_LAUNCH_CHECK();
