@@ -899,71 +899,59 @@ __global__ __launch_bounds__(256) void k_kl_combine(int64_t T, int nVT, int64_t 
   }
 }
 
-// Teacher tile of one chunk -> q = exp(U g + b - lse_t) as fp32 token rows
-// qbuf [Tp][Cp] (0 past the chunk end and for padding tokens).  The tile is
-// staged half its tokens at a time in LDS (1 KB rows, 16-byte chunks
-// XOR-swizzled by token) and leaves as whole token rows.
-constexpr int TQ_LDS = (TC::BN / 2) * TC::BM * 4;  // 128 tokens x 256 vocabulary fp32
-static_assert(TQ_LDS >= TC::LDS_BYTES, "q staging reuses the operand stages");
+// q workspace layout: fragment-major per 256x256 (vocabulary x token) tile of
+// a chunk, in the order (tile = tt * nCT + ct, wavefront, fn, fm, g, lane) with
+// four fp32 per lane: element r of entry (fm, fn, g) is vocabulary row
+// wm*128 + fm*32 + 8g + 4(lane/32) + r and token wn*128 + fn*32 + lane%32 of
+// the tile, which is where the matrix-core accumulators of both heads hold
+// them.  Each wavefront then writes and reads 1 KB contiguous per access.
+__device__ __forceinline__ int64_t qfrag_index(int64_t tile, int wave, int fn, int fm, int g, int lane) {
+  return ((((tile * (TC::WM * TC::WN) + wave) * TC::FN + fn) * TC::FM + fm) * 4 + g) * 64 + lane;
+}
 
+// Teacher tile of one chunk -> q = exp(U g + b - lse_t) (0 past the chunk end
+// and for padding tokens), written straight from the accumulators.
 __global__ __launch_bounds__(256, 1) void k_teacher_q(const bf16_t* __restrict__ U, const bf16_t* __restrict__ g,
                                                       const float* __restrict__ bias,
                                                       const float* __restrict__ gscale, int64_t T, int64_t dt,
-                                                      int64_t Cp, int64_t c0, int64_t c1, int nCT, int nTT,
-                                                      const float* __restrict__ tok, float* __restrict__ qbuf) {
+                                                      int64_t c0, int64_t c1, int nCT, int nTT,
+                                                      const float* __restrict__ tok, f32x4* __restrict__ qbuf) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
   const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
   Acc<TC> acc;
   gemm_tile_pipe<TC>(U, dt, m0, c1, g, dt, n0, T, (int)dt, lds, acc);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
-  float* E = (float*)lds;
-  const int c = tid & 63;  // this thread's 16-byte chunk of a token row: vocabulary m0 + 4c .. +3
-  const int64_t v = m0 + 4 * c;
-  float bv[4];
-  bool in[4];
+  const int64_t rbase = m0 + wm * TC::TM + 4 * (lane >> 5);
+  const int64_t tile = (int64_t)tt * nCT + ct;
+  float bv[TC::FM][4][4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    in[e] = v + e < c1;
-    bv[e] = (bias != nullptr && in[e]) ? bias[v + e] : 0.f;
-  }
-  __syncthreads();  // every wavefront is done with the operand stages
+  for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (wn == half) {
+    for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
-      for (int fn = 0; fn < TC::FN; ++fn) {
-        const int tl = fn * 32 + (lane & 31);
-        float* row = E + tl * TC::BM;
-#pragma unroll
-        for (int fm = 0; fm < TC::FM; ++fm)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int cv = (wm * TC::TM + fm * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
-            *(f32x4*)(row + ((cv ^ ((tl & 31) << 1)) << 2)) =
-                f32x4{acc.v[fm][fn][4 * q], acc.v[fm][fn][4 * q + 1], acc.v[fm][fn][4 * q + 2], acc.v[fm][fn][4 * q + 3]};
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int64_t v = rbase + fm * 32 + 8 * gi + r;
+        bv[fm][gi][r] = v < c1 ? (bias != nullptr ? bias[v] : 0.f) : -KD_INF;
       }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int i = 0; i < TC::BN / 2 / 4; ++i) {
-      const int tl = wave + 4 * i;
-      const int64_t t = n0 + half * (TC::BN / 2) + tl;
-      const f32x4 x = *(const f32x4*)(E + tl * TC::BM + ((c ^ ((tl & 31) << 1)) << 2));
-      f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < T) {
-        const float nl = -tok[t * TOKF + TK_LSEQ] * KD_LOG2E;
-        const float sc = gscale != nullptr ? gscale[t] : 1.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          q[e] = in[e] ? __builtin_amdgcn_exp2f(fmaf(x[e] * sc + bv[e], KD_LOG2E, nl)) : 0.f;
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
+    const bool tok_ok = t < T;
+    const float nl = tok_ok ? -tok[t * TOKF + TK_LSEQ] * KD_LOG2E : -KD_INF;
+    const float sc = (tok_ok && gscale != nullptr) ? gscale[t] : 1.f;
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        f32x4 q;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          q[r] = __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][gi * 4 + r] * sc + bv[fm][gi][r], KD_LOG2E, nl));
+        qbuf[qfrag_index(tile, wave, fn, fm, gi, lane)] = q;
       }
-      if (m0 + 4 * c < c0 + Cp) *(f32x4*)(qbuf + t * Cp + (v - c0)) = q;
-    }
-    __syncthreads();
   }
 }
 
@@ -975,16 +963,31 @@ constexpr int ZK_LDS = ZDZ_LDS + TC::WM * TT * 4;
 template <bool MASK>
 __device__ __forceinline__ void zdz_kl_tile(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h, int64_t T,
                                             int64_t d, int64_t Tp, int64_t Cp, int64_t c0, int64_t c1,
-                                            const float* __restrict__ tok, const float* __restrict__ qbuf,
-                                            float* __restrict__ partQZ, bf16_t* __restrict__ dz, int ct, int tt,
-                                            bf16_t* lds) {
+                                            const float* __restrict__ tok, const f32x4* __restrict__ qbuf,
+                                            float* __restrict__ partQZ, bf16_t* __restrict__ dz, int nCT, int ct,
+                                            int tt, bf16_t* lds) {
   const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
   const int vt = (int)(m0 / VT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
+  const int64_t tile = (int64_t)tt * nCT + ct;
   Acc<TC> acc;
   gemm_tile_pipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
   if (MASK) mask_rows(acc, (int)(c1 - m0), wm, lane);
+  // Per-token constants and the q of the first token column are loaded before
+  // the barrier; each column's loop then loads the next column's q.
+  float nlv[TC::FN], av[TC::FN];
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
+    nlv[fn] = t < T ? -tok[t * TOKF + TK_LSE] * KD_LOG2E : -KD_INF;
+    av[fn] = t < T ? tok[t * TOKF + TK_ALPHA] : 0.f;
+  }
+  f32x4 qv[2][TC::FM][4];
+#pragma unroll
+  for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) qv[0][fm][g] = qbuf[qfrag_index(tile, wave, 0, fm, g, lane)];  // 0 for padding tokens
   __syncthreads();  // every wavefront is done with the operand stages
   char* E = (char*)lds;
   float* red = (float*)((char*)lds + ZDZ_LDS);
@@ -992,20 +995,22 @@ __device__ __forceinline__ void zdz_kl_tile(const bf16_t* __restrict__ W, const 
 #pragma unroll
   for (int fn = 0; fn < TC::FN; ++fn) {
     const int tl = acc_col<TC>(wn, fn, lane);
-    const int64_t t = n0 + tl;
-    const bool tok_ok = t < T;
-    const float nl = tok_ok ? -tok[t * TOKF + TK_LSE] * KD_LOG2E : -KD_INF;
-    const float a = tok_ok ? tok[t * TOKF + TK_ALPHA] : 0.f;
-    const float* qrow = qbuf + (tok_ok ? t : 0) * Cp + (m0 - c0);
+    const float nl = nlv[fn], a = av[fn];
     char* row = E + tl * (VT * 2);
     const int sw = zdz_swz(tl);
     float qz = 0.f;
+    if (fn + 1 < TC::FN) {
+#pragma unroll
+      for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) qv[(fn + 1) & 1][fm][g] = qbuf[qfrag_index(tile, wave, fn + 1, fm, g, lane)];
+    }
 #pragma unroll
     for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int vl = rbase + fm * 32 + 8 * g;  // multiple of 4
-        const f32x4 q = tok_ok ? *(const f32x4*)(qrow + vl) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 q = qv[fn & 1][fm][g];
         float x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1042,15 +1047,15 @@ __device__ __forceinline__ void zdz_kl_tile(const bf16_t* __restrict__ W, const 
 __global__ __launch_bounds__(256, 1) void k_zdz_kl(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                    int64_t T, int64_t d, int64_t Tp, int64_t Cp, int64_t c0,
                                                    int64_t c1, int nCT, int nTT, const float* __restrict__ tok,
-                                                   const float* __restrict__ qbuf, float* __restrict__ partQZ,
+                                                   const f32x4* __restrict__ qbuf, float* __restrict__ partQZ,
                                                    bf16_t* __restrict__ dz) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
   if (c0 + (int64_t)(ct + 1) * VT > c1)
-    zdz_kl_tile<true>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, ct, tt, lds);
+    zdz_kl_tile<true>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, nCT, ct, tt, lds);
   else
-    zdz_kl_tile<false>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, ct, tt, lds);
+    zdz_kl_tile<false>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, nCT, ct, tt, lds);
 }
 
 // L_t = H_t - sum_v q_v z_v + lse.  A workgroup covers 32 tokens; its 32
@@ -1593,7 +1598,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
   float2* part = at<float2>(ws, p.o_part);
   float4* partT = at<float4>(ws, p.o_partT);
   float* partQZ = at<float>(ws, p.o_partQZ);
-  float* qbuf = at<float>(ws, p.o_q);
+  f32x4* qbuf = at<f32x4>(ws, p.o_q);
   bf16_t* dz = at<bf16_t>(ws, p.o_dz);
   if (int8) {
     bf16_t* gb = at<bf16_t>(ws, p.o_g);
@@ -1614,10 +1619,10 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     const int64_t clen = c1 - c0;
     const int nCT = (int)kd_ceil_div(clen, VT);
     const int gz = grid_of(nCT * p.nTT);
-    KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), TQ_LDS, s, (const bf16_t*)U, (const bf16_t*)g, b, gscale, T, dt, p.Cp, c0,
-                       c1, nCT, p.nTT, (const float*)tok, qbuf);
+    KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)U, (const bf16_t*)g, b, gscale, T,
+                       dt, c0, c1, nCT, p.nTT, (const float*)tok, qbuf);
     KD_LAUNCH(k_zdz_kl, dim3(gz), dim3(TC::NT), ZK_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0,
-                       c1, nCT, p.nTT, (const float*)tok, (const float*)qbuf, partQZ, dz);
+                       c1, nCT, p.nTT, (const float*)tok, (const f32x4*)qbuf, partQZ, dz);
     KD_LAUNCH_CHECK();
     const int kdh = (int)kd_round_up(clen, 64);
     const int gdh = grid_of(p.nTT * p.nDT);
