@@ -94,6 +94,20 @@ def test_kl_hidden_full_width_qwen3_8b_teacher_1p7b_student():
     print(f"kl_hidden full width: loss={float(gout['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
 
 
+def test_kl_hidden_bench_size_every_output():
+    """The benchmarked workload itself: T = 4096 tokens, student d = 2048,
+    teacher d = 4096, V = 151,936, chunk 8192 (16 token tiles x 19 chunks),
+    every output against the fp64 oracle (about 13 TFLOP on the host)."""
+    T, d, dt, V = 4096, 2048, 4096, 151936
+    h, W = synth.student_head(T, d, V, seed=0)
+    g, U, b = synth.teacher_head(T, dt, V, seed=1)
+    gout = _gpu(h, W, g, U, b, 8192)
+    r = oracle.kl_hidden_fwd_bwd(synth.as_f64(h), synth.as_f64(W), synth.as_f64(g), synth.as_f64(U),
+                                 b.double().numpy())
+    e = _check(gout, r, "bench size")
+    print(f"kl_hidden bench size: loss={float(gout['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
 def test_int8_quantize_codes_bit_exact():
     """GPU codes and scales equal the oracle's on identical bf16 inputs
     (fp32 decisions on both sides), including a zero row and ties at .5."""
