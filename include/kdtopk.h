@@ -36,6 +36,10 @@
  *    reproducible from run to run on the same device.
  *  - Shape limits: 1 <= K <= min(V, 1024); d % 64 == 0; d <= 16384;
  *    T >= 0; V >= 1.
+ *  - The matrices h, W, g, U, dh, dW and the workspace are accessed with
+ *    16-byte vector loads and stores and must be 16-byte aligned (hipMalloc
+ *    and PyTorch's allocator return 256-byte aligned blocks); a misaligned
+ *    one is refused with KD_EINVAL.
  */
 #ifndef KDTOPK_H
 #define KDTOPK_H

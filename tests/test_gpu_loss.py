@@ -185,6 +185,12 @@ def test_argument_errors():
         kd.loss_fwd_bwd(h[:, :32].contiguous(), W[:, :32].contiguous(), idx, tlp, None, mode=kd.RENORM)
     with pytest.raises(ValueError):
         kd.loss_fwd_bwd(h.cpu(), W, idx, tlp, None, mode=kd.RENORM)
+    # a contiguous view 8 bytes into a buffer: refused on the host, nothing launched
+    hbuf = torch.zeros(T * d + 4, dtype=torch.bfloat16, device=DEV)
+    h_off = hbuf[4:].view(T, d)
+    assert h_off.data_ptr() % 16 == 8
+    with pytest.raises(kd.KDError, match="16-byte aligned"):
+        kd.loss_fwd_bwd(h_off, W, idx, tlp, None, mode=kd.RENORM)
 
 
 # --------------------------------------------------------------------------

@@ -1186,6 +1186,8 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
   if (!g || !U || !idx || !val || !lse || !m_q || (n_rho > 0 && !k_rho))
     return kd_fail(KD_EINVAL, "null required pointer");
   if (!ws || ws_bytes < p.total) return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
+  if (!kd_aligned16(g) || !kd_aligned16(U) || !kd_aligned16(ws))
+    return kd_fail(KD_EINVAL, "g, U and ws must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   float* z = (float*)ws;
   for (int64_t t0 = 0; t0 < T; t0 += p.Tb) {

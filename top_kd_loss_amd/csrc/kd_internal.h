@@ -7,6 +7,10 @@
 // Record a formatted message for kd_last_error() and return `code`.
 kd_status kd_fail(kd_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
+// Arrays that the kernels read or write with 16-byte vector accesses (the
+// GEMM operands, dh, dW and the workspace) must be 16-byte aligned.
+static inline bool kd_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 // Launch profiler: while kd_profile_begin() is active on this thread, each
 // scope records a pair of HIP events around one kernel launch on `stream`.
 bool kd_prof_active();

@@ -1228,34 +1228,55 @@ __global__ void k_csr_fill(int64_t T, int K, const int32_t* __restrict__ sidx, c
 // fp64; they are summed as 64-bit fixed point with a per-column exponent
 // chosen from the largest product, so the result is independent of the
 // bucket order (deterministic) and exact to ~2^-60 of the column's scale.
-__global__ __launch_bounds__(256) void k_sparse_dw(const bf16_t* __restrict__ h, int64_t d,
+// dW rows of the sparse backward, SDW_ROWS vocabulary rows per workgroup and
+// four consecutive features per thread (d % 64 == 0): rows without entries
+// are written as zeros, a single entry as its product, several entries as an
+// exact fixed-point sum (order-independent, hence deterministic).
+constexpr int SDW_ROWS = 4;
+
+__device__ __forceinline__ float sparse_dw_elem(const bf16_t* __restrict__ h, int64_t d, int64_t j,
+                                                const int32_t* __restrict__ ent_t, const float* __restrict__ ent_r,
+                                                int b, int n) {
+  double amax = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double p = (double)ent_r[b + i] * (double)bf16_to_f32(h[(int64_t)ent_t[b + i] * d + j]);
+    amax = fmax(amax, fabs(p));
+  }
+  if (amax == 0.0) return 0.f;
+  int ex;
+  frexp(amax * (double)n, &ex);  // amax*n < 2^ex
+  const int sh = 61 - ex;
+  long long acc = 0;
+  for (int i = 0; i < n; ++i) {
+    const double p = (double)ent_r[b + i] * (double)bf16_to_f32(h[(int64_t)ent_t[b + i] * d + j]);
+    acc += llrint(ldexp(p, sh));
+  }
+  return (float)ldexp((double)acc, -sh);
+}
+
+__global__ __launch_bounds__(256) void k_sparse_dw(const bf16_t* __restrict__ h, int64_t d, int64_t V,
                                                    const int32_t* __restrict__ off, const int32_t* __restrict__ ent_t,
                                                    const float* __restrict__ ent_r, float* __restrict__ dW) {
-  const int64_t v = blockIdx.x;
-  const int b = off[v], n = off[v + 1] - b;
-  for (int64_t j = threadIdx.x; j < d; j += 256) {
-    float out = 0.f;
-    if (n == 1) {
-      out = ent_r[b] * bf16_to_f32(h[(int64_t)ent_t[b] * d + j]);
-    } else if (n > 1) {
-      double amax = 0.0;
-      for (int i = 0; i < n; ++i) {
-        const double p = (double)ent_r[b + i] * (double)bf16_to_f32(h[(int64_t)ent_t[b + i] * d + j]);
-        amax = fmax(amax, fabs(p));
+  const int64_t d4 = d >> 2;
+#pragma unroll 1
+  for (int r = 0; r < SDW_ROWS; ++r) {
+    const int64_t v = (int64_t)blockIdx.x * SDW_ROWS + r;
+    if (v >= V) return;
+    const int b = off[v], n = off[v + 1] - b;
+    f32x4* row = (f32x4*)(dW + v * d);
+    for (int64_t j4 = threadIdx.x; j4 < d4; j4 += 256) {
+      f32x4 out = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (n == 1) {
+        const float rr = ent_r[b];
+        const uint2 hv = *(const uint2*)(h + (int64_t)ent_t[b] * d + 4 * j4);
+        out = f32x4{rr * __uint_as_float(hv.x << 16), rr * __uint_as_float(hv.x & 0xffff0000u),
+                    rr * __uint_as_float(hv.y << 16), rr * __uint_as_float(hv.y & 0xffff0000u)};
+      } else if (n > 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = sparse_dw_elem(h, d, 4 * j4 + e, ent_t, ent_r, b, n);
       }
-      if (amax > 0.0) {
-        int ex;
-        frexp(amax * (double)n, &ex);  // amax*n < 2^ex
-        const int sh = 61 - ex;
-        long long acc = 0;
-        for (int i = 0; i < n; ++i) {
-          const double p = (double)ent_r[b + i] * (double)bf16_to_f32(h[(int64_t)ent_t[b + i] * d + j]);
-          acc += llrint(ldexp(p, sh));
-        }
-        out = (float)ldexp((double)acc, -sh);
-      }
+      row[j4] = out;
     }
-    dW[v * d + j] = out;
   }
 }
 
@@ -1388,6 +1409,8 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
     return kd_fail(KD_EINVAL, "KD_TAIL and KD_TAIL_REVERSE need m_q");
   if (!ws || ws_bytes < p.total)
     return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
+  if (!kd_aligned16(W) || !kd_aligned16(dW) || !kd_aligned16(ws) || (T > 0 && (!kd_aligned16(h) || !kd_aligned16(dh))))
+    return kd_fail(KD_EINVAL, "h, W, dh, dW and ws must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
 
   int32_t* err = at<int32_t>(ws, p.o_err);
@@ -1466,7 +1489,8 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
     KD_LAUNCH(k_seg_sum, dim3(nseg), dim3(256), 0, s, cnt, V, segsum);
     KD_LAUNCH(k_seg_scan, dim3(nseg), dim3(256), 0, s, cnt, V, segsum, nseg, off);
     KD_LAUNCH(k_csr_fill, dim3(ge), dim3(256), 0, s, T, (int)K, sidx, coef, tok, off, fillc, ent_t, ent_r);
-    KD_LAUNCH(k_sparse_dw, dim3((unsigned)V), dim3(256), 0, s, (const bf16_t*)h, d, off, ent_t, ent_r, dW);
+    KD_LAUNCH(k_sparse_dw, dim3((unsigned)kd_ceil_div(V, SDW_ROWS)), dim3(256), 0, s, (const bf16_t*)h, d, V, off,
+              ent_t, ent_r, dW);
     KD_LAUNCH_CHECK();
   }
   return KD_OK;
@@ -1587,6 +1611,9 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     return kd_fail(KD_EINVAL, "null required pointer (h, dh and g, or the int8 codes and their scales)");
   if (!ws || ws_bytes < p.total)
     return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
+  if (!kd_aligned16(W) || !kd_aligned16(U) || !kd_aligned16(dW) || !kd_aligned16(ws) ||
+      (T > 0 && (!kd_aligned16(h) || !kd_aligned16(dh) || (!int8 && !kd_aligned16(g)))))
+    return kd_fail(KD_EINVAL, "h, W, g, U, dh, dW and ws must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   float* tok = at<float>(ws, p.o_tok);
   if (T == 0) {
