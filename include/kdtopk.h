@@ -222,6 +222,29 @@ kd_status kd_kl_hidden_int8_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const in
                                     float* dh, float* dW,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/* The hidden-state KL with the teacher's logsumexp read from the cache
+ * instead of recomputed.  [TG Fig. 3] prices the rebuild of the teacher's
+ * full distribution from a cached hidden state at one head evaluation
+ * (2 dt V FLOP) per token; without a cached normalizer the chunked loss has
+ * to evaluate the teacher head twice (once for its logsumexp, once for q).
+ * Here it is evaluated once:
+ *   teacher_lse [T] fp32  logsumexp_v (U g_t + b)_v, as written to lse_t by an
+ *                         earlier kd_kl_hidden_fwd_bwd / _int8_fwd_bwd call on
+ *                         the same cached states, U and b (q is formed as
+ *                         exp(U g_t + b - teacher_lse_t); a different value
+ *                         leaves q unnormalized and the result is not the KL)
+ * The teacher states are given either as g [T, dt] bf16 (codes, scale_g
+ * NULL; workspace kd_kl_hidden_workspace) or as int8 codes [T, dt] with
+ * scale_g [T] (g NULL; workspace kd_kl_hidden_int8_workspace).  lse_t, if not
+ * NULL, receives teacher_lse.  Other arguments, outputs and errors as
+ * kd_kl_hidden_fwd_bwd. */
+kd_status kd_kl_hidden_cached_lse_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g,
+                                          const int8_t* codes, const float* scale_g, const kd_bf16* U,
+                                          const float* b, const float* teacher_lse, int64_t T, int64_t d,
+                                          int64_t dt, int64_t V, int32_t chunk, float scale,
+                                          float* loss, float* loss_tok, float* lse, float* lse_t,
+                                          float* dh, float* dW, void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace kd_topk_cache_build needs.  Returns 0 for
  * invalid sizes. */
 size_t kd_topk_cache_build_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho);

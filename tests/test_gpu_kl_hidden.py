@@ -140,3 +140,77 @@ def test_kl_hidden_int8_cache(shape):
                                  b.double().numpy(), g_scale=rs)
     e = _check(gout, r, "int8 " + shape)
     print(f"kl_hidden int8 {shape}: loss={float(gout['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
+# --------------------------------------------------------------------------
+# Cached teacher logsumexp (kd_kl_hidden_cached_lse_fwd_bwd)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", ["tiny", "ragged", "ragged_int8"])
+def test_kl_hidden_cached_lse_matches_oracle(shape):
+    """The teacher's logsumexp given as an input (the oracle's, in fp32):
+    same bar as the recomputing call."""
+    if shape == "tiny":
+        T, d, dt, V, chunk, seed = 64, 64, 128, 1024, 8192, 0
+    else:
+        T, d, dt, V, chunk, seed = 300, 128, 64, 2500, 700, 3
+    h, W, g, U, b = _inputs(T, d, dt, V, seed)
+    if shape.endswith("int8"):
+        rq, rs = oracle.quantize_hidden_int8(g.float().numpy())
+        r = oracle.kl_hidden_fwd_bwd(synth.as_f64(h), synth.as_f64(W), rq.astype(np.float64), synth.as_f64(U),
+                                     b.double().numpy(), g_scale=rs)
+        gq, gs = torch.from_numpy(rq).to(DEV), torch.from_numpy(rs).to(DEV)
+    else:
+        r = oracle.kl_hidden_fwd_bwd(synth.as_f64(h), synth.as_f64(W), synth.as_f64(g), synth.as_f64(U),
+                                     b.double().numpy())
+        gq, gs = g.to(DEV), None
+    lse_t = torch.from_numpy(r["lse_t"].astype(np.float32)).to(DEV)
+    o = kd.kl_hidden_fwd_bwd(h.to(DEV), W.to(DEV), gq, U.to(DEV), b.to(DEV), chunk=chunk, g_scale=gs,
+                             teacher_lse=lse_t)
+    torch.cuda.synchronize()
+    gout = {k: getattr(o, k).cpu().numpy() for k in o._fields}
+    e = _check(gout, r, "cached lse " + shape)
+    print(f"kl_hidden cached lse {shape}: loss={float(gout['loss']):.6f} ref={r['loss']:.6f} "
+          f"dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
+def test_kl_hidden_cached_lse_reuses_the_recomputed_normalizer():
+    """Feeding back the lse_t of a recomputing call: q is formed from the same
+    fp32 normalizer, so dh and dW are bitwise those of that call; the loss
+    (entropy from per-tile sums instead of the online partials) agrees to
+    fp32 rounding."""
+    T, d, dt, V, chunk = 300, 128, 64, 2500, 700
+    h, W, g, U, b = _inputs(T, d, dt, V, 9)
+    args = (h.to(DEV), W.to(DEV), g.to(DEV), U.to(DEV), b.to(DEV))
+    full = kd.kl_hidden_fwd_bwd(*args, chunk=chunk)
+    cached = kd.kl_hidden_fwd_bwd(*args, chunk=chunk, teacher_lse=full.lse_t.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(full.dh, cached.dh) and torch.equal(full.dW, cached.dW)
+    assert torch.equal(full.lse, cached.lse) and torch.equal(full.lse_t, cached.lse_t)
+    assert rel_err(float(cached.loss), float(full.loss)) <= 1e-5
+    np.testing.assert_allclose(cached.loss_tok.cpu().numpy(), full.loss_tok.cpu().numpy(), atol=2e-5, rtol=0)
+
+
+def test_kl_hidden_cached_lse_argument_errors():
+    import ctypes
+    T, d, dt, V = 8, 64, 64, 300
+    z = lambda *s, dt_=torch.bfloat16: torch.zeros(s, dtype=dt_, device=DEV)
+    h, W, g, U = z(T, d), z(V, d), z(T, dt), z(V, dt)
+    codes, gs = z(T, dt, dt_=torch.int8), z(T, dt_=torch.float32)
+    f32 = lambda *s: z(*s, dt_=torch.float32)
+    loss, dh, dW, lse_t = f32(), f32(T, d), f32(V, d), f32(T)
+    L = kd.lib()
+    ws = torch.empty(int(L.kd_kl_hidden_int8_workspace(T, d, dt, V, 512)), dtype=torch.uint8, device=DEV)
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call(g_, codes_, gs_, lse_):
+        return L.kd_kl_hidden_cached_lse_fwd_bwd(p(h), p(W), p(g_), p(codes_), p(gs_), p(U), None, p(lse_), T, d, dt,
+                                                 V, 512, 1.0 / T, p(loss), None, None, None, p(dh), p(dW), p(ws),
+                                                 ws.numel(), s)
+
+    assert call(g, None, None, None) == 1 and b"teacher_lse" in L.kd_last_error()
+    assert call(g, codes, gs, lse_t) == 1 and b"not both" in L.kd_last_error()
+    assert call(None, codes, None, lse_t) == 1
+    assert call(g, None, None, lse_t) == 0
+    torch.cuda.synchronize()

@@ -44,6 +44,8 @@ _SIGS = {
     "kd_kl_hidden_int8_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "kd_kl_hidden_int8_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _f32,
                                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_kl_hidden_cached_lse_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                       _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_teacher_recover": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
@@ -209,11 +211,14 @@ def hidden_quantize_int8(g: torch.Tensor):
 def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torch.Tensor,
                       b: Optional[torch.Tensor] = None, chunk: int = 8192, scale: Optional[float] = None,
                       workspace: Optional[torch.Tensor] = None, out: Optional[KlOut] = None,
-                      g_scale: Optional[torch.Tensor] = None) -> KlOut:
+                      g_scale: Optional[torch.Tensor] = None,
+                      teacher_lse: Optional[torch.Tensor] = None) -> KlOut:
     """Exact full-vocabulary KL(softmax(U g + b) || softmax(W h)), forward and
     backward, with the teacher rebuilt from its cached hidden state g
     (kd_kl_hidden_fwd_bwd); g int8 codes with g_scale [T] take the int8 cache
-    (kd_kl_hidden_int8_fwd_bwd)."""
+    (kd_kl_hidden_int8_fwd_bwd).  teacher_lse [T] (the lse_t output of an
+    earlier call on the same cache) skips the teacher's logsumexp pass
+    (kd_kl_hidden_cached_lse_fwd_bwd)."""
     dev = h.device
     T, d = h.shape
     V = W.shape[0]
@@ -229,6 +234,8 @@ def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torc
         _need(g_scale, "g_scale", torch.float32, (T,), dev)
     if b is not None:
         _need(b, "b", torch.float32, (V,), dev)
+    if teacher_lse is not None:
+        _need(teacher_lse, "teacher_lse", torch.float32, (T,), dev)
     if scale is None:
         scale = 1.0 / max(T, 1)
     L = lib()
@@ -243,7 +250,13 @@ def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torc
             f32 = dict(dtype=torch.float32, device=dev)
             out = KlOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
                         torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
-        if int8:
+        if teacher_lse is not None:
+            st = L.kd_kl_hidden_cached_lse_fwd_bwd(_ptr(h), _ptr(W), None if int8 else _ptr(g), _ptr(g) if int8 else None,
+                                                   _ptr(g_scale) if int8 else None, _ptr(U), _ptr(b), _ptr(teacher_lse),
+                                                   T, d, dt, V, chunk, scale, _ptr(out.loss), _ptr(out.loss_tok),
+                                                   _ptr(out.lse), _ptr(out.lse_t), _ptr(out.dh), _ptr(out.dW),
+                                                   _ptr(workspace), workspace.numel(), _stream(dev))
+        elif int8:
             st = L.kd_kl_hidden_int8_fwd_bwd(_ptr(h), _ptr(W), _ptr(g), _ptr(g_scale), _ptr(U), _ptr(b), T, d, dt,
                                              V, chunk, scale, _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse),
                                              _ptr(out.lse_t), _ptr(out.dh), _ptr(out.dW), _ptr(workspace),
@@ -253,7 +266,8 @@ def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torc
                                         _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.lse_t),
                                         _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
                                         _stream(dev))
-    _check(st, "kd_kl_hidden_int8_fwd_bwd" if int8 else "kd_kl_hidden_fwd_bwd")
+    _check(st, "kd_kl_hidden_cached_lse_fwd_bwd" if teacher_lse is not None
+           else "kd_kl_hidden_int8_fwd_bwd" if int8 else "kd_kl_hidden_fwd_bwd")
     return out
 
 

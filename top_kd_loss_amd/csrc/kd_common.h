@@ -32,6 +32,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 #define KD_LOG2E 1.4426950408889634f
+#define KD_LN2 0.6931471805599453f
 
 // D = A(32x16) * B(16x32) + C on the matrix cores, bf16 in, fp32 accumulate.
 // Lane l holds A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; the

@@ -855,9 +855,12 @@ __global__ __launch_bounds__(256, 1) void k_lse_pass(const bf16_t* __restrict__ 
 
 // Per token (one wavefront): student lse; teacher lse_t and H_t = E_q[zt] -
 // lse_t from the (m, s, u) partials, merged in fp64.
+// partT == nullptr: the teacher's logsumexp comes from lse_t_in, and its
+// entropy term from the per-tile sums of k_teacher_q (added in k_kl_finish).
 __global__ __launch_bounds__(256) void k_kl_combine(int64_t T, int nVT, int64_t Tp, float scale,
                                                     const float2* __restrict__ part,
-                                                    const float4* __restrict__ partT, float* __restrict__ tok) {
+                                                    const float4* __restrict__ partT,
+                                                    const float* __restrict__ lse_t_in, float* __restrict__ tok) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -869,7 +872,7 @@ __global__ __launch_bounds__(256) void k_kl_combine(int64_t T, int nVT, int64_t 
       s = (m == -INFINITY ? 0.0 : s * exp(m - mn)) + (double)p.y * exp((double)p.x - mn);
       m = mn;
     }
-    const float4 q = partT[(int64_t)vt * Tp + t];
+    const float4 q = partT != nullptr ? partT[(int64_t)vt * Tp + t] : float4{-INFINITY, 0.f, 0.f, 0.f};
     if (q.x != -INFINITY) {
       const double mn = fmax(mt, (double)q.x);
       const double fo = (mt == -INFINITY) ? 0.0 : exp(mt - mn), fp = exp((double)q.x - mn);
@@ -891,11 +894,15 @@ __global__ __launch_bounds__(256) void k_kl_combine(int64_t T, int nVT, int64_t 
   ut = wave_sum_f64(ut_l);
   if (lane == 0) {
     float* tk = tok + t * TOKF;
-    const double lse_t = Mt + log(st);
     tk[TK_LSE] = (float)(M + log(s));
-    tk[TK_LSEQ] = (float)lse_t;
     tk[TK_ALPHA] = scale;
-    tk[TK_L] = (float)(ut / st - log(st));  // H_t = E_q[zt] - lse_t
+    if (partT != nullptr) {
+      tk[TK_LSEQ] = (float)(Mt + log(st));
+      tk[TK_L] = (float)(ut / st - log(st));  // H_t = E_q[zt] - lse_t
+    } else {
+      tk[TK_LSEQ] = lse_t_in[t];
+      tk[TK_L] = 0.f;
+    }
   }
 }
 
@@ -914,8 +921,9 @@ __device__ __forceinline__ int64_t qfrag_index(int64_t tile, int wave, int fn, i
 __global__ __launch_bounds__(256, 1) void k_teacher_q(const bf16_t* __restrict__ U, const bf16_t* __restrict__ g,
                                                       const float* __restrict__ bias,
                                                       const float* __restrict__ gscale, int64_t T, int64_t dt,
-                                                      int64_t c0, int64_t c1, int nCT, int nTT,
-                                                      const float* __restrict__ tok, f32x4* __restrict__ qbuf) {
+                                                      int64_t c0, int64_t c1, int nCT, int nTT, int64_t Tp,
+                                                      const float* __restrict__ tok, f32x4* __restrict__ qbuf,
+                                                      float* __restrict__ partH) {
   extern __shared__ __align__(16) bf16_t lds[];
   int ct, tt;
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
@@ -926,32 +934,53 @@ __global__ __launch_bounds__(256, 1) void k_teacher_q(const bf16_t* __restrict__
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   const int64_t rbase = m0 + wm * TC::TM + 4 * (lane >> 5);
   const int64_t tile = (int64_t)tt * nCT + ct;
-  float bv[TC::FM][4][4];
-#pragma unroll
-  for (int fm = 0; fm < TC::FM; ++fm)
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t v = rbase + fm * 32 + 8 * gi + r;
-        bv[fm][gi][r] = v < c1 ? (bias != nullptr ? bias[v] : 0.f) : -KD_INF;
-      }
+  float nl[TC::FN], sc[TC::FN], hq[TC::FN];  // per token column; hq: sum of q log2 q over this lane's rows
 #pragma unroll
   for (int fn = 0; fn < TC::FN; ++fn) {
     const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
     const bool tok_ok = t < T;
-    const float nl = tok_ok ? -tok[t * TOKF + TK_LSEQ] * KD_LOG2E : -KD_INF;
-    const float sc = (tok_ok && gscale != nullptr) ? gscale[t] : 1.f;
+    nl[fn] = tok_ok ? -tok[t * TOKF + TK_LSEQ] * KD_LOG2E : -KD_INF;
+    sc[fn] = (tok_ok && gscale != nullptr) ? gscale[t] : 1.f;
+    hq[fn] = 0.f;
+  }
 #pragma unroll
-    for (int fm = 0; fm < TC::FM; ++fm)
+  for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
+    for (int gi = 0; gi < 4; ++gi) {
+      float bv[4];  // bias of this lane's 4 rows; -inf past the chunk end
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t v = rbase + fm * 32 + 8 * gi + r;
+        bv[r] = v < c1 ? (bias != nullptr ? bias[v] : 0.f) : -KD_INF;
+      }
+#pragma unroll
+      for (int fn = 0; fn < TC::FN; ++fn) {
         f32x4 q;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          q[r] = __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][gi * 4 + r] * sc + bv[fm][gi][r], KD_LOG2E, nl));
+        for (int r = 0; r < 4; ++r) {
+          const float y = fmaf(acc.v[fm][fn][gi * 4 + r] * sc[fn] + bv[r], KD_LOG2E, nl[fn]);  // log2 q
+          q[r] = __builtin_amdgcn_exp2f(y);
+          hq[fn] += (q[r] != 0.f) ? q[r] * y : 0.f;
+        }
         qbuf[qfrag_index(tile, wave, fn, fm, gi, lane)] = q;
       }
+    }
+  if (partH != nullptr) {
+    // sum_v q_v log q_v of this tile per token, merged over the wavefront rows
+    float* red = (float*)lds;
+    __syncthreads();  // every wavefront is done with the operand stages
+#pragma unroll
+    for (int fn = 0; fn < TC::FN; ++fn) {
+      const float hs = hq[fn] + __shfl_xor(hq[fn], 32, 64);
+      if (lane < 32) red[wm * TT + acc_col<TC>(wn, fn, lane)] = hs;
+    }
+    __syncthreads();
+    static_assert(TT == TC::NT, "one thread per token column");
+    const int col = threadIdx.x;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < TC::WM; ++w) sum += red[w * TT + col];
+    if (n0 + col < T) partH[(m0 / VT) * Tp + n0 + col] = sum * KD_LN2;
   }
 }
 
@@ -1058,25 +1087,31 @@ __global__ __launch_bounds__(256, 1) void k_zdz_kl(const bf16_t* __restrict__ W,
     zdz_kl_tile<false>(W, h, T, d, Tp, Cp, c0, c1, tok, qbuf, partQZ, dz, nCT, ct, tt, lds);
 }
 
-// L_t = H_t - sum_v q_v z_v + lse.  A workgroup covers 32 tokens; its 32
+// L_t = H_t - sum_v q_v z_v + lse, with H_t = sum_v q_v log q_v from the
+// teacher partials (k_kl_combine) or, with a cached teacher logsumexp, from
+// the per-tile sums partH.  A workgroup covers 32 tokens; its 32
 // groups of 32 threads each sum every 32nd vocabulary tile (coalesced across
 // tokens), and the group sums are added in group order (deterministic).
 __global__ __launch_bounds__(1024) void k_kl_finish(int64_t T, int nVT, int64_t Tp, const float* __restrict__ partQZ,
-                                                    float* __restrict__ tok, float* __restrict__ loss_tok,
-                                                    float* __restrict__ lse_out, float* __restrict__ lset_out) {
+                                                    const float* __restrict__ partH, float* __restrict__ tok,
+                                                    float* __restrict__ loss_tok, float* __restrict__ lse_out,
+                                                    float* __restrict__ lset_out) {
   __shared__ double red[32][33];
   const int tl = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int64_t t = (int64_t)blockIdx.x * 32 + tl;
-  double part = 0.0;
+  double part = 0.0;  // sum over tiles of (sum q log q, when given) - sum q z
   if (t < T)
-    for (int vt = grp; vt < nVT; vt += 32) part += (double)partQZ[(int64_t)vt * Tp + t];
+    for (int vt = grp; vt < nVT; vt += 32) {
+      part -= (double)partQZ[(int64_t)vt * Tp + t];
+      if (partH != nullptr) part += (double)partH[(int64_t)vt * Tp + t];
+    }
   red[grp][tl] = part;
   __syncthreads();
   if (grp != 0 || t >= T) return;
-  double qz = 0.0;
-  for (int g = 0; g < 32; ++g) qz += red[g][tl];
+  double acc = 0.0;
+  for (int g = 0; g < 32; ++g) acc += red[g][tl];
   float* tk = tok + t * TOKF;
-  const float L = (float)((double)tk[TK_L] - qz + (double)tk[TK_LSE]);
+  const float L = (float)((double)tk[TK_L] + acc + (double)tk[TK_LSE]);
   tk[TK_L] = L;
   if (loss_tok) loss_tok[t] = L;
   if (lse_out) lse_out[t] = tk[TK_LSE];
@@ -1534,7 +1569,7 @@ namespace {
 struct KlPlan {
   int64_t Tp, C, Cp;
   int nVT, nTT, nDT, nchunks;
-  size_t o_tok, o_part, o_partT, o_partQZ, o_q, o_dz, o_g, total;
+  size_t o_tok, o_part, o_partT, o_partQZ, o_partH, o_q, o_dz, o_g, total;
 };
 
 // int8: room for the bf16 copy of the codes.
@@ -1559,6 +1594,7 @@ static bool plan_kl(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk, 
   p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_partT = o; o = align_up(o + (size_t)p.nVT * p.Tp * 16);
   p.o_partQZ = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
+  p.o_partH = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
   p.o_q = o; o = align_up(o + (size_t)p.Tp * p.Cp * 4);
   p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
   p.o_g = 0;
@@ -1597,10 +1633,12 @@ extern "C" kd_status kd_hidden_quantize_int8(const kd_bf16* g, int64_t T, int64_
 
 // The KL with the teacher hidden states as bf16 (g) or as int8 codes with a
 // per-position scale (codes8, gscale).
+// teacher_lse != nullptr: the teacher's logsumexp is given (cached), and the
+// teacher head is evaluated once instead of twice.
 static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, const int8_t* codes8,
-                         const float* gscale, const kd_bf16* U, const float* b, int64_t T, int64_t d, int64_t dt,
-                         int64_t V, int32_t chunk, float scale, float* loss, float* loss_tok, float* lse,
-                         float* lse_t, float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
+                         const float* gscale, const kd_bf16* U, const float* b, const float* teacher_lse, int64_t T,
+                         int64_t d, int64_t dt, int64_t V, int32_t chunk, float scale, float* loss, float* loss_tok,
+                         float* lse, float* lse_t, float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
   KlPlan p;
   const bool int8 = codes8 != nullptr || gscale != nullptr;
   if (!plan_kl(T, d, dt, V, chunk, int8, p))
@@ -1609,6 +1647,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
   if (!loss || !dW || !W || !U) return kd_fail(KD_EINVAL, "null required pointer (loss, W, U, dW)");
   if (T > 0 && (!h || !dh || (!int8 && !g) || (int8 && (!codes8 || !gscale))))
     return kd_fail(KD_EINVAL, "null required pointer (h, dh and g, or the int8 codes and their scales)");
+  if (int8 && g != nullptr) return kd_fail(KD_EINVAL, "give either g or the int8 codes and their scales, not both");
   if (!ws || ws_bytes < p.total)
     return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", p.total, ws_bytes);
   if (!kd_aligned16(W) || !kd_aligned16(U) || !kd_aligned16(dW) || !kd_aligned16(ws) ||
@@ -1625,6 +1664,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
   float2* part = at<float2>(ws, p.o_part);
   float4* partT = at<float4>(ws, p.o_partT);
   float* partQZ = at<float>(ws, p.o_partQZ);
+  float* partH = teacher_lse != nullptr ? at<float>(ws, p.o_partH) : nullptr;
   f32x4* qbuf = at<f32x4>(ws, p.o_q);
   bf16_t* dz = at<bf16_t>(ws, p.o_dz);
   if (int8) {
@@ -1635,10 +1675,12 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
   const int g1 = grid_of(p.nVT * p.nTT);
   KD_LAUNCH(k_lse_pass<false>, dim3(g1), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)W, (const bf16_t*)h, d, T, V,
                      (const float*)nullptr, (const float*)nullptr, p.nVT, p.nTT, p.Tp, part, (float4*)nullptr);
-  KD_LAUNCH(k_lse_pass<true>, dim3(g1), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)U, (const bf16_t*)g, dt, T, V,
-                     b, gscale, p.nVT, p.nTT, p.Tp, (float2*)nullptr, partT);
+  if (teacher_lse == nullptr)
+    KD_LAUNCH(k_lse_pass<true>, dim3(g1), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)U, (const bf16_t*)g, dt, T,
+              V, b, gscale, p.nVT, p.nTT, p.Tp, (float2*)nullptr, partT);
   KD_LAUNCH_CHECK();
-  KD_LAUNCH(k_kl_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, p.nVT, p.Tp, scale, part, partT, tok);
+  KD_LAUNCH(k_kl_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, p.nVT, p.Tp, scale, part,
+            teacher_lse != nullptr ? (const float4*)nullptr : (const float4*)partT, teacher_lse, tok);
   KD_LAUNCH_CHECK();
   for (int c = 0; c < p.nchunks; ++c) {
     const int64_t c0 = (int64_t)c * p.C;
@@ -1647,7 +1689,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     const int nCT = (int)kd_ceil_div(clen, VT);
     const int gz = grid_of(nCT * p.nTT);
     KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)U, (const bf16_t*)g, b, gscale, T,
-                       dt, c0, c1, nCT, p.nTT, (const float*)tok, qbuf);
+                       dt, c0, c1, nCT, p.nTT, p.Tp, (const float*)tok, qbuf, partH);
     KD_LAUNCH(k_zdz_kl, dim3(gz), dim3(TC::NT), ZK_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0,
                        c1, nCT, p.nTT, (const float*)tok, (const f32x4*)qbuf, partQZ, dz);
     KD_LAUNCH_CHECK();
@@ -1661,7 +1703,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     KD_LAUNCH_CHECK();
   }
   KD_LAUNCH(k_kl_finish, dim3((unsigned)kd_ceil_div(T, 32)), dim3(1024), 0, s, T, p.nVT, p.Tp, (const float*)partQZ,
-                     tok, loss_tok, lse, lse_t);
+                     (const float*)partH, tok, loss_tok, lse, lse_t);
   KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, (const float*)tok, (const int32_t*)nullptr, loss);
   KD_LAUNCH_CHECK();
   return KD_OK;
@@ -1671,8 +1713,8 @@ extern "C" kd_status kd_kl_hidden_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
                                           const float* b, int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk,
                                           float scale, float* loss, float* loss_tok, float* lse, float* lse_t,
                                           float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
-  return kl_impl(h, W, g, nullptr, nullptr, U, b, T, d, dt, V, chunk, scale, loss, loss_tok, lse, lse_t, dh, dW, ws,
-                 ws_bytes, stream);
+  return kl_impl(h, W, g, nullptr, nullptr, U, b, nullptr, T, d, dt, V, chunk, scale, loss, loss_tok, lse, lse_t, dh,
+                 dW, ws, ws_bytes, stream);
 }
 
 extern "C" kd_status kd_kl_hidden_int8_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int8_t* codes,
@@ -1680,6 +1722,17 @@ extern "C" kd_status kd_kl_hidden_int8_fwd_bwd(const kd_bf16* h, const kd_bf16* 
                                                int64_t d, int64_t dt, int64_t V, int32_t chunk, float scale,
                                                float* loss, float* loss_tok, float* lse, float* lse_t, float* dh,
                                                float* dW, void* ws, size_t ws_bytes, void* stream) {
-  return kl_impl(h, W, nullptr, codes, gscale, U, b, T, d, dt, V, chunk, scale, loss, loss_tok, lse, lse_t, dh, dW,
-                 ws, ws_bytes, stream);
+  return kl_impl(h, W, nullptr, codes, gscale, U, b, nullptr, T, d, dt, V, chunk, scale, loss, loss_tok, lse, lse_t,
+                 dh, dW, ws, ws_bytes, stream);
+}
+
+extern "C" kd_status kd_kl_hidden_cached_lse_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g,
+                                                     const int8_t* codes, const float* gscale, const kd_bf16* U,
+                                                     const float* b, const float* teacher_lse, int64_t T, int64_t d,
+                                                     int64_t dt, int64_t V, int32_t chunk, float scale, float* loss,
+                                                     float* loss_tok, float* lse, float* lse_t, float* dh, float* dW,
+                                                     void* ws, size_t ws_bytes, void* stream) {
+  if (T > 0 && teacher_lse == nullptr) return kd_fail(KD_EINVAL, "null required pointer (teacher_lse)");
+  return kl_impl(h, W, g, codes, gscale, U, b, teacher_lse, T, d, dt, V, chunk, scale, loss, loss_tok, lse, lse_t, dh,
+                 dW, ws, ws_bytes, stream);
 }
