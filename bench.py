@@ -33,6 +33,7 @@ PEAK_HBM = 8.0e12       # MI355X HBM3E, bytes/s
 METRIC = "fused top-K KD loss fwd+bwd tokens/s incl. LM head; % bf16 MFMA peak"
 CFG = dict(T=4096, d=2048, V=151936, K=15, chunk=8192)
 CACHE_CFG = dict(T=16384, d=4096, V=151936, K=256, rho=(0.9, 0.95))
+LLAMA_CFG = dict(T=8192, d=2048, V=128256, K=256, K_rev=16, chunk=8192)
 GEMM_KERNELS = {"k_pass1": 2, "k_zdz": 2, "k_dhdw": 4, "k_cache_gemm": 2}  # x T*d*V FLOP per step
 
 
@@ -157,7 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--mode", default="tail", choices=["renorm", "tail", "full", "reverse"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the RENORM line and the cache-build line")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other modes, the hidden-state KL, the T=8192 K=256 line and the cache build")
     ap.add_argument("--no-memscan", action="store_true",
                     help="skip the long-context line (peak memory and tokens/s vs T at d=2560, K=64, 4K..32K)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -247,6 +249,8 @@ def main():
         log(f"[bench] kl_hidden: {res['kl_hidden']}")
         del hd, Wd
         torch.cuda.empty_cache()
+        res["llama_k256"] = bench_llama_k256(torch, kd, synth, dev, max(3, args.steps // 4))
+        log(f"[bench] llama k256: {res['llama_k256']}")
         res["cache_build"] = bench_cache_build(torch, kd, synth, dev)
         log(f"[bench] cache build: {res['cache_build']}")
 
@@ -322,6 +326,57 @@ def bench_kl_hidden(torch, kd, synth, dev, hd, Wd, steps):
             "cached_teacher_lse": {"ms_per_step": ms_c, "tokens_per_s": T / (ms_c * 1e-3),
                                    "mfma_frac_credited": credited / (ms_c * 1e-3) / PEAK_BF16,
                                    "mfma_frac_executed": executed_c / (ms_c * 1e-3) / PEAK_BF16}}
+
+
+def bench_llama_k256(torch, kd, synth, dev, steps):
+    """Llama-3.2-1B-shaped student head, T=8192, V=128,256: the teacher cache
+    keeps K=256 (renorm, tail, full); reverse KL runs on the student's own
+    top-16, selected by the cache build on (h, W), with the teacher's
+    log-probs gathered from the same synthetic teacher rows."""
+    c = LLAMA_CFG
+    T, d, V, K, Kr, chunk = c["T"], c["d"], c["V"], c["K"], c["K_rev"], c["chunk"]
+    h, W = synth.student_head(T, d, V, seed=2)
+    hd, Wd = h.to(dev), W.to(dev)
+    del h, W
+    sel = kd.cache_build(hd, Wd, None, Kr)                 # student top-16 (the REVERSE support)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    tlp = torch.empty((T, K), dtype=torch.float32, device=dev)
+    mq = torch.empty(T, dtype=torch.float32, device=dev)
+    tlp_rev = torch.empty((T, Kr), dtype=torch.float32, device=dev)
+    rows = 1024
+    for r0 in range(0, T, rows):
+        r1 = min(T, r0 + rows)
+        b0, nb = r0 // synth.BLOCK, (r1 - r0 + synth.BLOCK - 1) // synth.BLOCK
+        zt = torch.from_numpy(synth.zipf_teacher_logits(T, V, seed=2, first_block=b0, n_blocks=nb)).to(dev)
+        o = kd.topk_rows(zt, K)
+        idx[r0:r1], tlp[r0:r1], mq[r0:r1] = o.idx, o.val - o.lse[:, None], o.m_q
+        tlp_rev[r0:r1] = torch.gather(zt, 1, sel.idx[r0:r1].long()) - o.lse[:, None]
+        del zt
+    torch.cuda.synchronize()
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = kd.LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
+                     torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
+    tdv = T * d * V
+    res = {"workload": "Llama-3.2-1B-shaped student head", "T": T, "d": d, "V": V, "K": K, "chunk": chunk}
+    for name, md in (("renorm", kd.RENORM), ("tail", kd.TAIL), ("full", kd.FULL)):
+        ws = torch.empty(kd.loss_workspace_bytes(T, d, V, K, md, chunk), dtype=torch.uint8, device=dev)
+        ms = time_steps(torch, lambda: kd.loss_fwd_bwd(hd, Wd, idx, tlp, mq, mode=md, chunk=chunk, workspace=ws,
+                                                       out=out), steps, 2)
+        cr = 6 * tdv if md in (kd.TAIL, kd.FULL) else 2 * tdv + 4 * T * K * d
+        res[name] = {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "mfma_frac_step": cr / (ms * 1e-3) / PEAK_BF16}
+        del ws
+    wsc = torch.empty(kd.lib().kd_topk_cache_build_workspace(T, d, V, Kr, 0), dtype=torch.uint8, device=dev)
+    ms_sel = time_steps(torch, lambda: kd.cache_build(hd, Wd, None, Kr, workspace=wsc), steps, 1)
+    del wsc
+    ws = torch.empty(kd.loss_workspace_bytes(T, d, V, Kr, kd.REVERSE, chunk), dtype=torch.uint8, device=dev)
+    ridx = sel.idx
+    ms_rev = time_steps(torch, lambda: kd.loss_fwd_bwd(hd, Wd, ridx, tlp_rev, None, mode=kd.REVERSE, chunk=chunk,
+                                                       workspace=ws, out=out), steps, 2)
+    res["reverse_student_top16"] = {"selection_ms": ms_sel, "loss_ms": ms_rev,
+                                    "tokens_per_s": T / ((ms_sel + ms_rev) * 1e-3)}
+    del hd, Wd, idx, tlp, mq, tlp_rev, sel, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_cache_build(torch, kd, synth, dev, steps=3):

@@ -161,6 +161,39 @@ def test_bitwise_deterministic():
             assert np.array_equal(a[key].view(np.uint32), b[key].view(np.uint32)), (mode, key)
 
 
+@pytest.mark.parametrize("mode", [kd.RENORM, kd.REVERSE])
+def test_sparse_backward_shared_supports(mode):
+    """Vocabulary rows shared by many tokens: 1,100 tokens share one support
+    (those 8 dW rows gather 1,100 entries each, past the 1,024 that the
+    kernel ranks by token in LDS), 200 more share 4 indices (200 entries per
+    row) plus 4 of their own.  Parity with the oracle and bitwise
+    repeatability (the CSR fill's entry order does not reach dW)."""
+    T, d, V, K = 1300, 64, 3000, 8
+    rng = np.random.default_rng(21)
+    h, W = synth.student_head(T, d, V, seed=21)
+    idx = np.zeros((T, K), np.int32)
+    s0 = np.array([5, 17, 300, 1024, 2047, 2500, 2999, 0], np.int32)
+    idx[:1100] = s0
+    s1 = np.array([7, 1500, 2222, 64], np.int32)
+    pool = np.setdiff1d(np.arange(V, dtype=np.int32), np.concatenate([s0, s1]))
+    for t in range(1100, T):
+        idx[t, :4] = s1
+        idx[t, 4:] = rng.choice(pool, 4, replace=False)
+    zt = synth.zipf_teacher_logits(T, V, seed=21).astype(np.float64)
+    lse_t = np.array([oracle.logsumexp(zt[t]) for t in range(T)])
+    tlp = (np.take_along_axis(zt, idx.astype(np.int64), axis=1) - lse_t[:, None]).astype(np.float32)
+    mq = np.zeros(T, np.float32)
+    g = _run(h, W, idx, tlp, mq, mode, chunk=1024)
+    g2 = _run(h, W, idx, tlp, mq, mode, chunk=1024)
+    for key in ("loss", "dh", "dW"):
+        assert np.array_equal(g[key].view(np.uint32), g2[key].view(np.uint32)), (mode, key)
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    e = _compare(g, r, f"shared supports mode={mode}")
+    hot = np.concatenate([s0, s1])
+    assert rel_fro(g["dW"][hot], r["dW"][hot]) <= GRAD_RTOL, rel_fro(g["dW"][hot], r["dW"][hot])
+    print(f"shared supports mode={mode}: dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
 def test_empty_tokens():
     V, d, K = 300, 64, 4
     W = synth.to_bf16(synth.normal_f32(V, d, 0.1, 0, 2)).to(DEV)

@@ -1264,10 +1264,14 @@ __global__ void k_csr_fill(int64_t T, int K, const int32_t* __restrict__ sidx, c
 // chosen from the largest product, so the result is independent of the
 // bucket order (deterministic) and exact to ~2^-60 of the column's scale.
 // dW rows of the sparse backward, SDW_ROWS vocabulary rows per workgroup and
-// four consecutive features per thread (d % 64 == 0): rows without entries
-// are written as zeros, a single entry as its product, several entries as an
-// exact fixed-point sum (order-independent, hence deterministic).
+// four consecutive features per thread (d % 64 == 0).  A row without entries
+// is written as zeros, one entry as its product.  A row with 2..SDW_SORT
+// entries (the tokens of a row are distinct) has them ranked by token in LDS
+// and summed in fp32 in token order; a longer one (a vocabulary row shared by
+// more than SDW_SORT tokens) takes an exact fixed-point sum.  Both orders are
+// fixed, so dW does not depend on the order the CSR fill wrote the entries.
 constexpr int SDW_ROWS = 4;
+constexpr int SDW_SORT = 1024;
 
 __device__ __forceinline__ float sparse_dw_elem(const bf16_t* __restrict__ h, int64_t d, int64_t j,
                                                 const int32_t* __restrict__ ent_t, const float* __restrict__ ent_r,
@@ -1289,28 +1293,61 @@ __device__ __forceinline__ float sparse_dw_elem(const bf16_t* __restrict__ h, in
   return (float)ldexp((double)acc, -sh);
 }
 
+__device__ __forceinline__ f32x4 bf16x4_scaled(const bf16_t* p, float r) {
+  const uint2 hv = *(const uint2*)p;
+  return f32x4{r * __uint_as_float(hv.x << 16), r * __uint_as_float(hv.x & 0xffff0000u),
+               r * __uint_as_float(hv.y << 16), r * __uint_as_float(hv.y & 0xffff0000u)};
+}
+
 __global__ __launch_bounds__(256) void k_sparse_dw(const bf16_t* __restrict__ h, int64_t d, int64_t V,
                                                    const int32_t* __restrict__ off, const int32_t* __restrict__ ent_t,
                                                    const float* __restrict__ ent_r, float* __restrict__ dW) {
+  __shared__ int32_t tin[SDW_SORT], ts[SDW_SORT];
+  __shared__ float rs[SDW_SORT];
   const int64_t d4 = d >> 2;
+  const int tid = threadIdx.x;
 #pragma unroll 1
   for (int r = 0; r < SDW_ROWS; ++r) {
     const int64_t v = (int64_t)blockIdx.x * SDW_ROWS + r;
     if (v >= V) return;
     const int b = off[v], n = off[v + 1] - b;
     f32x4* row = (f32x4*)(dW + v * d);
-    for (int64_t j4 = threadIdx.x; j4 < d4; j4 += 256) {
-      f32x4 out = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (n == 1) {
-        const float rr = ent_r[b];
-        const uint2 hv = *(const uint2*)(h + (int64_t)ent_t[b] * d + 4 * j4);
-        out = f32x4{rr * __uint_as_float(hv.x << 16), rr * __uint_as_float(hv.x & 0xffff0000u),
-                    rr * __uint_as_float(hv.y << 16), rr * __uint_as_float(hv.y & 0xffff0000u)};
-      } else if (n > 1) {
+    if (n == 0) {
+      for (int64_t j4 = tid; j4 < d4; j4 += 256) row[j4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if (n == 1) {
+      const float rr = ent_r[b];
+      const bf16_t* hr = h + (int64_t)ent_t[b] * d;
+      for (int64_t j4 = tid; j4 < d4; j4 += 256) row[j4] = bf16x4_scaled(hr + 4 * j4, rr);
+    } else if (n <= SDW_SORT) {
+      for (int i = tid; i < n; i += 256) tin[i] = ent_t[b + i];
+      __syncthreads();
+      for (int i = tid; i < n; i += 256) {
+        const int ti = tin[i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) rank += tin[j] < ti;
+        ts[rank] = ti;
+        rs[rank] = ent_r[b + i];
+      }
+      __syncthreads();
+      for (int64_t j4 = tid; j4 < d4; j4 += 256) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < n; ++i) {
+          const f32x4 x = bf16x4_scaled(h + (int64_t)ts[i] * d + 4 * j4, 1.f);
+          acc[0] = fmaf(rs[i], x[0], acc[0]);
+          acc[1] = fmaf(rs[i], x[1], acc[1]);
+          acc[2] = fmaf(rs[i], x[2], acc[2]);
+          acc[3] = fmaf(rs[i], x[3], acc[3]);
+        }
+        row[j4] = acc;
+      }
+      __syncthreads();  // the next row reuses tin, ts, rs
+    } else {
+      for (int64_t j4 = tid; j4 < d4; j4 += 256) {
+        f32x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = sparse_dw_elem(h, d, 4 * j4 + e, ent_t, ent_r, b, n);
+        row[j4] = out;
       }
-      row[j4] = out;
     }
   }
 }
