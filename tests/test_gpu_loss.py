@@ -77,6 +77,30 @@ def test_ragged_multi_chunk(mode):
     _compare(g, r, f"ragged mode={mode}")
 
 
+EDGE_SIZES = {
+    "one_token": (1, 64, 300, 5, 8192),
+    "k_max_1024": (257, 64, 2049, 1024, 512),
+    "d_max_16384": (3, 16384, 700, 4, 8192),
+    "vocab_7_k_eq_v": (5, 64, 7, 7, 8192),
+}
+
+
+@pytest.mark.parametrize("mode", ALL_MODES)
+@pytest.mark.parametrize("case", sorted(EDGE_SIZES))
+def test_edge_sizes(case, mode):
+    """A single token; the largest K (1,024) over several chunks; the largest
+    d (16,384); a 7-word vocabulary with K = V (one partial tile)."""
+    T, d, V, K, chunk = EDGE_SIZES[case]
+    h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=17)
+    g = _run(h, W, idx, tlp, mq, mode, chunk=chunk)
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    # K = V (and the REVERSE support covering the whole vocabulary) makes the
+    # renormalised losses exactly 0 up to rounding: compare absolutely there
+    floor = 1e-4 if case == "vocab_7_k_eq_v" else 1e-6
+    e = _compare(g, r, f"{case} mode={mode}", loss_floor=floor)
+    print(f"{case} mode={mode}: loss={float(g['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
 def test_worked_example_fig2():
     """The twelve-token, k=4 example of "The Gradient That Top-k Distillation
     Never Computes" (Figure 2), embedded with d=64: column 0 of W holds the
