@@ -152,3 +152,43 @@ def test_rows_bitwise_deterministic():
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x,
                            y.view(torch.int32) if y.dtype == torch.float32 else y)
+
+
+def test_rows_single_pass_collection_no_rho():
+    """Without k_rho targets the candidates are collected during the
+    histogram pass above a bound from the threads' maxima (K <= 512) or by
+    the separate pass (K > 512); ties, signed zeros, -inf and a tie larger
+    than the candidate buffer go through both."""
+    z = synth.tie_heavy_logits(12, 40000, seed=7, step=1.0 / 64.0, span=3.0)
+    for K in (1, 5, 256, 512, 513, 1000):
+        _check_rows(z, K, rho=())
+    h = np.full((3, 10000), 0.7, np.float32)
+    h[1, 5000:] = -0.0
+    h[1, :5000] = 0.0
+    h[2, 9000:] = 3.0
+    h[2, :100] = -np.inf
+    for K in (1, 300, 1024):
+        _check_rows(h, K, rho=())
+
+
+@pytest.mark.parametrize("rho", [(), RHO])
+def test_cache_build_integer_logits_bit_exact(rho):
+    """Small-integer hidden states and head rows make every logit an exact
+    integer in fp32 (|z| < 2^24), so the cache build's top-K (through the
+    GEMM's per-tile maxima) must equal the oracle's bit for bit, with heavy
+    ties resolved to the lower index."""
+    T, d, V = 50, 64, 5000
+    r = np.random.default_rng(31)
+    g = r.integers(-2, 3, size=(T, d)).astype(np.float32)
+    U = r.integers(-2, 3, size=(V, d)).astype(np.float32)
+    b = r.integers(-3, 4, size=V).astype(np.float32)
+    z = g.astype(np.float64) @ U.astype(np.float64).T + b[None, :]
+    for K in (1, 16, 300):
+        o = kd.cache_build(torch.from_numpy(g).to(torch.bfloat16).to(DEV),
+                           torch.from_numpy(U).to(torch.bfloat16).to(DEV), torch.from_numpy(b).to(DEV), K, rho)
+        torch.cuda.synchronize()
+        ri, rv, rlse, rmq, rk = oracle.cache_from_logits(z.astype(np.float32), K, rho)
+        np.testing.assert_array_equal(o.idx.cpu().numpy(), ri)
+        np.testing.assert_array_equal(o.val.cpu().numpy().view(np.uint32), rv.view(np.uint32))
+        np.testing.assert_allclose(o.lse.cpu().numpy(), rlse, atol=1e-5, rtol=0)
+        np.testing.assert_allclose(o.m_q.cpu().numpy(), rmq, atol=1e-5, rtol=0)

@@ -521,10 +521,13 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
   const float* zr = z + row * ldz;
   const int tid = threadIdx.x;
   const bool vec = ((V & 3) == 0) && ((((uintptr_t)zr) & 15) == 0);
-  // fixed point: a mass term exp(z - edge) <= 1 is stored as round(term * 2^31)
-  // (32 bits); sums over a bin are exact 64-bit integers for V < 2^32
-  const float fxs = 2147483648.0f;
-  const double fxs_inv = 1.0 / 2147483648.0;
+  // fixed point: a mass term exp(z - edge) <= 1 is stored as round(term * 2^F)
+  // with F = 62 - bits(V), so the sums over a bin stay exact 64-bit integers;
+  // a wide level-0 bin (width 16 for values in [64, 128)) puts its largest
+  // element far below the edge, whose mass then keeps 2^-F * e^16 precision
+  const int fx_bits = 62 - (64 - __clzll((unsigned long long)V));
+  const double fxs = ldexp(1.0, fx_bits);
+  const double fxs_inv = ldexp(1.0, -fx_bits);
 
   for (int i = tid; i < NB * NCOPY; i += RT) {
     (&S.u.copies.cnt[0][0])[i] = 0;
@@ -541,7 +544,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
     row_loop<RT>(zr, V, vec, [&](int64_t, float x) {
       const int b = (int)(fkey(x) >> 21);
       const float ex = __expf(x - S.ref0[b]);
-      run.add(b, (unsigned long long)(uint32_t)fmaf(ex, fxs, 0.5f), S.u.copies.cnt[cp], S.u.copies.mass[cp]);
+      run.add(b, __double2ull_rn((double)ex * fxs), S.u.copies.cnt[cp], S.u.copies.mass[cp]);
     });
     run.flush(S.u.copies.cnt[cp], S.u.copies.mass[cp]);
   }
@@ -663,7 +666,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
           if (act[j] && (k >> (32 - pb)) == pj[j]) {
             const int dg = (int)((k >> sh) & ((1u << dbits) - 1u));
             const float ex = __expf(x - bin_upper((pj[j] << dbits) | (uint32_t)dg, pb + dbits));
-            run[j].add(dg, (unsigned long long)(uint32_t)fmaf(ex, fxs, 0.5f), S.u.late.cntR[j], S.u.late.massR[j]);
+            run[j].add(dg, __double2ull_rn((double)ex * fxs), S.u.late.cntR[j], S.u.late.massR[j]);
           }
         }
       });
@@ -787,6 +790,8 @@ struct FastShared {
   float red_f[RF / 64];
   int red_i[RF / 64];
   unsigned long long total_q;
+  float tau;                       // lower bound of the K-th largest value (single-pass collection)
+  int tau_ok;
   int bK, aboveK, nbK, fillK;
   int bR[RHO_MAX], cntAboveR[RHO_MAX], nR[RHO_MAX], fillR[RHO_MAX], segR[RHO_MAX];
   unsigned long long massAboveR[RHO_MAX];
@@ -881,6 +886,30 @@ __device__ __forceinline__ float cand_value(unsigned long long c) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Lower bound of the K-th largest value of a row from n partial maxima a[]
+// (each the maximum of a disjoint part of the row): the partial maximum of
+// rank K - 1 in (value desc, position asc) order.  K distinct elements of the
+// row are >= it, so it is <= the K-th largest element.  a[] is in LDS;
+// S.tau_ok stays 0 when n < K or no value has that rank (NaN present).
+__device__ __forceinline__ void fast_tau(const float* a, int n, int K, FastShared& S) {
+  if (threadIdx.x == 0) S.tau_ok = 0;
+  __syncthreads();
+  if (n >= K)
+    for (int p = threadIdx.x; p < n; p += RF) {
+      const float x = a[p];
+      int r = 0;
+      for (int q = 0; q < n; ++q) {
+        const float y = a[q];
+        r += (y > x || (y == x && q < p)) ? 1 : 0;
+      }
+      if (r == K - 1) {
+        S.tau = x;
+        S.tau_ok = 1;
+      }
+    }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
                                                   int n_rho, float rho0, float rho1, float rho2, float rho3,
                                                   float rho4, float rho5, float rho6, float rho7,
@@ -907,20 +936,61 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     if (tid == 0) flags[row] = 1;
     return;
   }
+  // Without k_rho targets the top-K candidates can be collected during pass B
+  // already: every element >= tau (a lower bound of the K-th largest value,
+  // from the producer's tile maxima or the threads' maxima of pass A).
+  bool onepass = false;
+  float tau = 0.f;
+  if (n_rho == 0) {
+    float* a = (float*)S.u.hist;
+    int n;
+    if (tmax != nullptr) {
+      n = n_tmax <= NBL * 2 ? n_tmax : 0;
+      for (int p = tid; p < n; p += RF) a[p] = tmax[row * n_tmax + p];
+    } else {
+      n = RF;
+      a[tid] = mx;
+    }
+    __syncthreads();
+    fast_tau(a, n, K, S);
+    onepass = S.tau_ok != 0;
+    tau = S.tau;
+    __syncthreads();  // a[] is overwritten by the histogram below
+  }
 
   // ---- B: packed (count, fixed-point mass) histogram of the value bins
   for (int i = tid; i < NBL; i += RF) S.u.hist[i] = 0ull;
+  if (tid == 0) S.fillK = 0;
   __syncthreads();
-  row_loop_pipe<RF>(
-      zr, V, vec,
-      [&](int64_t, float x, int) {
-        const int b = vbin(x, zmax);
-        const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
-        const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
-        atomicAdd(&S.u.hist[b], w);
-      },
-      [](int64_t, bool) {});
+  if (onepass)
+    row_loop_pipe<RF>(
+        zr, V, vec,
+        [&](int64_t i, float x, int) {
+          const int b = vbin(x, zmax);
+          const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
+          const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
+          atomicAdd(&S.u.hist[b], w);
+          if (x >= tau) {
+            const int slot = atomicAdd(&S.fillK, 1);
+            if (slot < CAPK) S.poolK[slot] = cand_key(x, i);
+          }
+        },
+        [](int64_t, bool) {});
+  else
+    row_loop_pipe<RF>(
+        zr, V, vec,
+        [&](int64_t, float x, int) {
+          const int b = vbin(x, zmax);
+          const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
+          const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
+          atomicAdd(&S.u.hist[b], w);
+        },
+        [](int64_t, bool) {});
   __syncthreads();
+  // the single-pass collection holds the top K when it neither overflowed nor
+  // came up short (it cannot, for a valid tau)
+  const int nOne = S.fillK;
+  const bool doneK = onepass && nOne >= K && nOne <= CAPK;
 
   // bins [tid*BPT, tid*BPT + BPT) per thread: masses in 2^-44 units of exp(zmax)
   unsigned long long bm[BPT];
@@ -988,7 +1058,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
   // candidate segments: one per distinct crossing bin; fall back when the
   // candidates do not fit or a crossing lies in the last (unbounded) bin
   const int bK = S.bK;
-  const int nKc = S.aboveK + S.nbK;
+  const int nKc = doneK ? nOne : S.aboveK + S.nbK;
   int bR[RHO_MAX], seg[RHO_MAX];
   bool own[RHO_MAX];
   int used = 0;
@@ -1026,8 +1096,8 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
   __syncthreads();
 
   // ---- C: collect the candidates (rare: the LDS slot atomics run only for
-  // the lanes holding one)
-  row_loop_pipe<RF>(
+  // the lanes holding one); skipped when pass B collected the top K
+  if (!doneK) row_loop_pipe<RF>(
       zr, V, vec,
       [&](int64_t i, float x, int) {
         const int b = vbin(x, zmax);
