@@ -253,6 +253,8 @@ def main():
         log(f"[bench] llama k256: {res['llama_k256']}")
         res["cache_build"] = bench_cache_build(torch, kd, synth, dev)
         log(f"[bench] cache build: {res['cache_build']}")
+        res["topk_rows"] = bench_topk_rows(torch, kd, dev)
+        log(f"[bench] standalone row pass: {res['topk_rows']}")
 
     if not args.no_memscan and not args.no_extras:
         res["memscan"] = memscan(torch, kd, dev)
@@ -375,6 +377,27 @@ def bench_llama_k256(torch, kd, synth, dev, steps):
     res["reverse_student_top16"] = {"selection_ms": ms_sel, "loss_ms": ms_rev,
                                     "tokens_per_s": T / ((ms_sel + ms_rev) * 1e-3)}
     del hd, Wd, idx, tlp, mq, tlp_rev, sel, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_topk_rows(torch, kd, dev, steps=5):
+    """The standalone row pass (kd_topk_rows) on 2048 fp32 rows shaped like the
+    cache build's teacher logits (V = 151,936, N(0, 1.1)), K = 256, with and
+    without the two k_rho targets: algorithmic bytes = the row read once plus
+    the outputs."""
+    T, V, K = 2048, CACHE_CFG["V"], CACHE_CFG["K"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    z = torch.randn((T, V), generator=gen, device=dev, dtype=torch.float32) * 1.1
+    res = {"workload": "teacher-logit rows, N(0, 1.1)", "rows": T, "V": V, "K": K}
+    for name, rho in (("no_rho", ()), ("rho", CACHE_CFG["rho"])):
+        ws = torch.empty(max(1, kd.lib().kd_topk_rows_workspace(T, V, K, len(rho))), dtype=torch.uint8, device=dev)
+        ms = time_steps(torch, lambda: kd.topk_rows(z, K, rho, workspace=ws), steps, 2)
+        alg = T * (4 * V) + T * (8 * K + 8 + 4 * len(rho))
+        gbps = alg / (ms * 1e-3) / 1e9
+        res[name] = {"rho": list(rho), "ms_per_call": ms, "algorithmic_GBps": gbps, "hbm_frac": gbps * 1e9 / PEAK_HBM}
+    del z
     torch.cuda.empty_cache()
     return res
 
