@@ -746,8 +746,10 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Fast row pass: one workgroup of RF threads per row, three streaming reads
-// of the row (the second and third are served by the last-level cache).
+// Fast row pass: one workgroup of RF threads per row, up to three streaming
+// reads of the row.  Without k_rho targets and with a lower bound tau of the
+// K-th largest value (from the partial maxima of A), B and C collapse into
+// one read that sums exp(z - zmax) and collects the elements >= tau.
 //   A  the row maximum zmax;
 //   B  a histogram over NBL value bins below zmax, bin b holding the values
 //      with floor(128 (zmax - z)) = b (the last bin also everything lower).
@@ -886,6 +888,36 @@ __device__ __forceinline__ float cand_value(unsigned long long c) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Top K of the nKc candidates in S.poolK (every element ranked above a
+// candidate is a candidate): rank by key, write idx / val, and lse and the
+// tail mass 1 - sum over the top K of exp(z - lse).
+__device__ __forceinline__ void fast_emit_topk(FastShared& S, int nKc, int K, const float* zr, int64_t row,
+                                               double lse, int32_t* idx_out, float* val_out, float* lse_out,
+                                               float* mq_out) {
+  const int tid = threadIdx.x;
+  for (int p = tid; p < nKc; p += RF) {
+    const unsigned long long mine = S.poolK[p];
+    int r = 0;
+#pragma unroll 8
+    for (int q = 0; q < nKc; ++q) r += (S.poolK[q] < mine) ? 1 : 0;
+    if (r < K) {
+      const int64_t i = (int64_t)(mine & 0xffffffffull);
+      const float x = zr[i];  // the stored value keeps its bits (-0.0)
+      idx_out[row * K + r] = (int32_t)i;
+      val_out[row * K + r] = x;
+      S.u.m[r] = exp((double)x - lse);
+    }
+  }
+  __syncthreads();
+  double kept = 0.0;
+  for (int r = tid; r < K; r += RF) kept += S.u.m[r];
+  kept = fast_block_sum(kept, S);
+  if (tid == 0) {
+    lse_out[row] = (float)lse;
+    mq_out[row] = (float)(1.0 - kept);
+  }
+}
+
 // Lower bound of the K-th largest value of a row from n partial maxima a[]
 // (each the maximum of a disjoint part of the row): the partial maximum of
 // rank K - 1 in (value desc, position asc) order.  K distinct elements of the
@@ -958,39 +990,48 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     __syncthreads();  // a[] is overwritten by the histogram below
   }
 
-  // ---- B: packed (count, fixed-point mass) histogram of the value bins
-  for (int i = tid; i < NBL; i += RF) S.u.hist[i] = 0ull;
-  if (tid == 0) S.fillK = 0;
-  __syncthreads();
-  if (onepass)
+  if (onepass) {
+    // ---- B': one read: the exponential sum (fp64 per thread, then the fixed
+    // block order: deterministic) and the elements >= tau.  The top K are
+    // among them; more than CAPK of them (a huge tie) sends the row to the
+    // exact kernel.
+    if (tid == 0) S.fillK = 0;
+    __syncthreads();
+    double acc = 0.0;
     row_loop_pipe<RF>(
         zr, V, vec,
         [&](int64_t i, float x, int) {
-          const int b = vbin(x, zmax);
-          const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
-          const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
-          atomicAdd(&S.u.hist[b], w);
+          acc += (double)__builtin_amdgcn_exp2f((x - zmax) * KD_LOG2E);
           if (x >= tau) {
             const int slot = atomicAdd(&S.fillK, 1);
             if (slot < CAPK) S.poolK[slot] = cand_key(x, i);
           }
         },
         [](int64_t, bool) {});
-  else
-    row_loop_pipe<RF>(
-        zr, V, vec,
-        [&](int64_t, float x, int) {
-          const int b = vbin(x, zmax);
-          const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
-          const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
-          atomicAdd(&S.u.hist[b], w);
-        },
-        [](int64_t, bool) {});
+    const double total = fast_block_sum(acc, S);  // its barriers also complete the pool
+    const int nKc = S.fillK;
+    if (nKc < K || nKc > CAPK) {
+      if (tid == 0) flags[row] = 1;
+      return;
+    }
+    if (tid == 0) flags[row] = 0;
+    fast_emit_topk(S, nKc, K, zr, row, (double)zmax + log(total), idx_out, val_out, lse_out, mq_out);
+    return;
+  }
+
+  // ---- B: packed (count, fixed-point mass) histogram of the value bins
+  for (int i = tid; i < NBL; i += RF) S.u.hist[i] = 0ull;
   __syncthreads();
-  // the single-pass collection holds the top K when it neither overflowed nor
-  // came up short (it cannot, for a valid tau)
-  const int nOne = S.fillK;
-  const bool doneK = onepass && nOne >= K && nOne <= CAPK;
+  row_loop_pipe<RF>(
+      zr, V, vec,
+      [&](int64_t, float x, int) {
+        const int b = vbin(x, zmax);
+        const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
+        const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
+        atomicAdd(&S.u.hist[b], w);
+      },
+      [](int64_t, bool) {});
+  __syncthreads();
 
   // bins [tid*BPT, tid*BPT + BPT) per thread: masses in 2^-44 units of exp(zmax)
   unsigned long long bm[BPT];
@@ -1058,7 +1099,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
   // candidate segments: one per distinct crossing bin; fall back when the
   // candidates do not fit or a crossing lies in the last (unbounded) bin
   const int bK = S.bK;
-  const int nKc = doneK ? nOne : S.aboveK + S.nbK;
+  const int nKc = S.aboveK + S.nbK;
   int bR[RHO_MAX], seg[RHO_MAX];
   bool own[RHO_MAX];
   int used = 0;
@@ -1096,8 +1137,8 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
   __syncthreads();
 
   // ---- C: collect the candidates (rare: the LDS slot atomics run only for
-  // the lanes holding one); skipped when pass B collected the top K
-  if (!doneK) row_loop_pipe<RF>(
+  // the lanes holding one)
+  row_loop_pipe<RF>(
       zr, V, vec,
       [&](int64_t i, float x, int) {
         const int b = vbin(x, zmax);
@@ -1118,28 +1159,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
       [](int64_t, bool) {});
   __syncthreads();
 
-  // top-K: rank of each candidate among all of them (distinct keys)
-  for (int p = tid; p < nKc; p += RF) {
-    const unsigned long long mine = S.poolK[p];
-    int r = 0;
-#pragma unroll 8
-    for (int q = 0; q < nKc; ++q) r += (S.poolK[q] < mine) ? 1 : 0;
-    if (r < K) {
-      const int64_t i = (int64_t)(mine & 0xffffffffull);
-      const float x = zr[i];  // the stored value keeps its bits (-0.0)
-      idx_out[row * K + r] = (int32_t)i;
-      val_out[row * K + r] = x;
-      S.u.m[r] = exp((double)x - lse);
-    }
-  }
-  __syncthreads();
-  double kept = 0.0;
-  for (int r = tid; r < K; r += RF) kept += S.u.m[r];
-  kept = fast_block_sum(kept, S);
-  if (tid == 0) {
-    lse_out[row] = (float)lse;
-    mq_out[row] = (float)(1.0 - kept);
-  }
+  fast_emit_topk(S, nKc, K, zr, row, lse, idx_out, val_out, lse_out, mq_out);
 
   // k_rho: masses of the crossing bin's elements in rank order, then the
   // first rank where the mass from the top reaches rho
