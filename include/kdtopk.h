@@ -170,6 +170,33 @@ kd_status kd_topk_loss_fwd_bwd_tt(const kd_bf16* h, const kd_bf16* W, const int3
                                   float* dh, float* dW,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* kd_topk_loss_fwd_bwd (any mode) when the student's logsumexp and its
+ * logits at idx are already known, so the forward pass over the vocabulary
+ * is skipped.  The reverse modes choose S as the student's own top-k [TT
+ * abstract, Table 2]: kd_topk_cache_build(h, W, NULL, K) returns exactly
+ * idx, student_logits (its val) and student_lse (its lse), computed from the
+ * same fp32 logits this call would form, so a step that selects and then
+ * distils evaluates the student head once for the forward instead of twice.
+ *
+ * In:  student_lse    [T]    fp32  logsumexp of each token's student logits
+ *      student_logits [T, K] fp32  the student's logits at idx, same order
+ *                                  (padding slots ignored)
+ *      sampled, teacher_logp_sampled  as kd_topk_loss_fwd_bwd_tt (mode
+ *                                  KD_REVERSE_TT only), else NULL
+ * Everything else, the outputs (lse receives student_lse) and the
+ * workspace (kd_topk_loss_workspace) as kd_topk_loss_fwd_bwd.  Values that
+ * are not those of h and W give the loss of the values given, not of the
+ * model; the backward still uses h and W. */
+kd_status kd_topk_loss_fwd_bwd_selected(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                        const float* teacher_logp, const float* m_q,
+                                        const float* student_lse, const float* student_logits,
+                                        const int32_t* sampled, const float* teacher_logp_sampled,
+                                        int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                                        int32_t chunk, float scale,
+                                        float* loss, float* loss_tok, float* lse, float* m_p,
+                                        float* dh, float* dW,
+                                        void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace kd_kl_hidden_fwd_bwd needs (0 for invalid sizes).
  * Linear in T for fixed (d, dt, V, chunk). */
 size_t kd_kl_hidden_workspace(int64_t T, int64_t d, int64_t dt, int64_t V, int32_t chunk);

@@ -343,3 +343,49 @@ def test_reverse_tt_sampled_token_correction(shape):
                             tlp_labels=tly)
     e = _compare(g, r, f"reverse_tt {shape}")
     print(f"reverse_tt {shape} loss={float(g['loss']):.6f} ref={r['loss']:.6f} dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
+# --------------------------------------------------------------------------
+# Student logsumexp and logits at S given (kd_topk_loss_fwd_bwd_selected)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ALL_MODES)
+def test_given_student_logits_match_oracle(mode):
+    """The forward pass replaced by given values (the oracle's fp64 logsumexp
+    and logits at idx, rounded to fp32): same bar as the full call."""
+    T, d, V, K = 300, 128, 2500, 13
+    h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=23)
+    z = synth.as_f64(h) @ synth.as_f64(W).T
+    slse = np.array([oracle.logsumexp(z[t]) for t in range(T)]).astype(np.float32)
+    szl = np.take_along_axis(z, np.maximum(idx, 0).astype(np.int64), axis=1).astype(np.float32)
+    out = kd.loss_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV),
+                          torch.from_numpy(mq).to(DEV), mode=mode, chunk=700,
+                          student_lse=torch.from_numpy(slse).to(DEV), student_logits=torch.from_numpy(szl).to(DEV))
+    torch.cuda.synchronize()
+    g = {k: getattr(out, k).cpu().numpy() for k in out._fields}
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    e = _compare(g, r, f"given student logits mode={mode}")
+    np.testing.assert_array_equal(g["lse"], slse)
+    print(f"given student logits mode={mode}: dh={e[0]:.2e} dW={e[1]:.2e}")
+
+
+def test_given_selection_equals_recomputed_forward():
+    """Reverse KL on the student's own top-16: feeding the cache build's lse
+    and values (the selection step) gives the same result as recomputing the
+    forward pass (the two logsumexps agree to fp32 rounding)."""
+    T, d, V, K = 512, 256, 6000, 16
+    h, W = synth.student_head(T, d, V, seed=29)
+    hd, Wd = h.to(DEV), W.to(DEV)
+    sel = kd.cache_build(hd, Wd, None, K)
+    zt = torch.from_numpy(synth.zipf_teacher_logits(T, V, seed=29)).to(DEV)
+    tlp = torch.gather(zt, 1, sel.idx.long()) - torch.logsumexp(zt, 1, keepdim=True)
+    a = kd.loss_fwd_bwd(hd, Wd, sel.idx, tlp, None, mode=kd.REVERSE, chunk=2048)
+    b = kd.loss_fwd_bwd(hd, Wd, sel.idx, tlp, None, mode=kd.REVERSE, chunk=2048, student_lse=sel.lse,
+                        student_logits=sel.val)
+    torch.cuda.synchronize()
+    assert rel_err(float(b.loss), float(a.loss)) <= 1e-5, (float(b.loss), float(a.loss))
+    np.testing.assert_allclose(b.lse.cpu().numpy(), a.lse.cpu().numpy(), atol=2e-5, rtol=0)
+    assert rel_fro(b.dh.cpu().numpy(), a.dh.cpu().numpy()) <= 1e-5
+    assert rel_fro(b.dW.cpu().numpy(), a.dW.cpu().numpy()) <= 1e-5
+    with pytest.raises(ValueError):
+        kd.loss_fwd_bwd(hd, Wd, sel.idx, tlp, None, mode=kd.REVERSE, student_lse=sel.lse)

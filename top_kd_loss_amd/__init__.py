@@ -40,6 +40,9 @@ _SIGS = {
                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_loss_fwd_bwd_tt": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32,
                                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_topk_loss_fwd_bwd_selected": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                                     _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                                     _vp]),
     "kd_hidden_quantize_int8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "kd_kl_hidden_int8_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "kd_kl_hidden_int8_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _f32,
@@ -125,12 +128,16 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
                  m_q: Optional[torch.Tensor] = None, mode: int = TAIL, chunk: int = 8192,
                  scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                  out: Optional[LossOut] = None, labels: Optional[torch.Tensor] = None,
-                 ce_weight: float = 0.0, labels_teacher_logp: Optional[torch.Tensor] = None) -> LossOut:
+                 ce_weight: float = 0.0, labels_teacher_logp: Optional[torch.Tensor] = None,
+                 student_lse: Optional[torch.Tensor] = None,
+                 student_logits: Optional[torch.Tensor] = None) -> LossOut:
     """Fused LM head + top-K KD loss, forward and backward (kd_topk_loss_fwd_bwd;
     with labels [T] int32 (-1 = none) and ce_weight > 0, kd_topk_loss_fwd_bwd_ce
     adds the weighted hard-label cross-entropy term; with mode REVERSE_TT,
     labels are the sampled tokens and labels_teacher_logp [T] the teacher's
-    log-probabilities at them, kd_topk_loss_fwd_bwd_tt)."""
+    log-probabilities at them, kd_topk_loss_fwd_bwd_tt).  student_lse [T] and
+    student_logits [T, K] (e.g. lse and val of cache_build(h, W, None, K), the
+    selection of idx) skip the forward pass (kd_topk_loss_fwd_bwd_selected)."""
     if isinstance(mode, str):
         mode = MODE_BY_NAME[mode]
     dev = h.device
@@ -147,6 +154,14 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
         _need(labels, "labels", torch.int32, (T,), dev)
     if labels_teacher_logp is not None:
         _need(labels_teacher_logp, "labels_teacher_logp", torch.float32, (T,), dev)
+    sel = student_lse is not None or student_logits is not None
+    if sel:
+        if student_lse is None or student_logits is None:
+            raise ValueError("student_lse and student_logits come together")
+        if ce_weight != 0.0:
+            raise ValueError("the cross-entropy term is not available with given student logits")
+        _need(student_lse, "student_lse", torch.float32, (T,), dev)
+        _need(student_logits, "student_logits", torch.float32, (T, K), dev)
     ce = ce_weight != 0.0
     tt = mode == REVERSE_TT and labels is not None
     if scale is None:
@@ -164,7 +179,15 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
             f32 = dict(dtype=torch.float32, device=dev)
             out = LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
                           torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
-        if tt:
+        if sel:
+            st = L.kd_topk_loss_fwd_bwd_selected(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
+                                                 _ptr(student_lse), _ptr(student_logits),
+                                                 _ptr(labels) if tt else None,
+                                                 _ptr(labels_teacher_logp) if tt else None, T, d, V, K, mode, chunk,
+                                                 scale, _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse),
+                                                 _ptr(out.m_p), _ptr(out.dh), _ptr(out.dW), _ptr(workspace),
+                                                 workspace.numel(), _stream(dev))
+        elif tt:
             st = L.kd_topk_loss_fwd_bwd_tt(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(labels),
                                            _ptr(labels_teacher_logp), T, d, V, K, chunk, scale,
                                            _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
@@ -182,7 +205,8 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
                                         _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
                                         _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
                                         _stream(dev))
-    _check(st, "kd_topk_loss_fwd_bwd_tt" if tt else "kd_topk_loss_fwd_bwd_ce" if ce else "kd_topk_loss_fwd_bwd")
+    _check(st, "kd_topk_loss_fwd_bwd_selected" if sel else "kd_topk_loss_fwd_bwd_tt" if tt
+           else "kd_topk_loss_fwd_bwd_ce" if ce else "kd_topk_loss_fwd_bwd")
     return out
 
 

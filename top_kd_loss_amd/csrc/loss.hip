@@ -72,19 +72,23 @@ static inline int grid_of(int tiles) { return (int)kd_round_up(tiles, 8); }
 // with a bitonic network in LDS; padding slots (idx < 0) and indices >= V
 // sort last as SENT (the latter also raise the error flag).
 // ---------------------------------------------------------------------------
+// zin (optional): the student's logits at idx, already known; they are
+// sorted along into zout (0 at padding slots).
 __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, const float* __restrict__ tlp,
-                                             int64_t T, int64_t V, int K, int Kp2, int nVT, int64_t Tp,
-                                             int32_t* __restrict__ sidx, float* __restrict__ stlp,
+                                             const float* __restrict__ zin, int64_t T, int64_t V, int K, int Kp2,
+                                             int nVT, int64_t Tp, int32_t* __restrict__ sidx,
+                                             float* __restrict__ stlp, float* __restrict__ zout,
                                              int32_t* __restrict__ starts, float* __restrict__ tok,
                                              int32_t* __restrict__ err) {
   __shared__ int key[KMAX];
   __shared__ float val[KMAX];
+  __shared__ float zv[KMAX];
   const int lane = threadIdx.x;
   const int64_t t = blockIdx.x;
   bool bad = false;
   for (int k = lane; k < Kp2; k += 64) {
     int id = SENT;
-    float v = 0.f;
+    float v = 0.f, zz = 0.f;
     if (k < K) {
       const int raw = idx[t * K + k];
       if (raw >= V) {
@@ -92,10 +96,12 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
       } else if (raw >= 0) {
         id = raw;
         v = tlp[t * K + k];
+        if (zin != nullptr) zz = zin[t * K + k];
       }
     }
     key[k] = id;
     val[k] = v;
+    zv[k] = zz;
   }
   __syncthreads();
   for (int size = 2; size <= Kp2; size <<= 1) {
@@ -111,6 +117,9 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
           const float x = val[lo];
           val[lo] = val[hi];
           val[hi] = x;
+          const float y = zv[lo];
+          zv[lo] = zv[hi];
+          zv[hi] = y;
         }
       }
       __syncthreads();
@@ -122,6 +131,7 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
     const int id = key[k];
     sidx[t * K + k] = id;
     stlp[t * K + k] = val[k];
+    if (zout != nullptr) zout[t * K + k] = zv[k];
     if (id != SENT) {
       ++nv;
       mx = fmax(mx, (double)val[k]);
@@ -359,23 +369,28 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
                                                  float* __restrict__ tok,
                                                  float* __restrict__ coef, int32_t* __restrict__ ylab,
                                                  float* __restrict__ loss_tok, float* __restrict__ lse_out,
-                                                 float* __restrict__ mp_out) {
+                                                 float* __restrict__ mp_out, const float* __restrict__ lse_in) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
-  // logsumexp over the per-tile partials
-  double m = -INFINITY, s = 0.0;
-  for (int vt = lane; vt < nVT; vt += 64) {
-    const float2 p = part[(int64_t)vt * Tp + t];
-    const double mn = fmax(m, (double)p.x);
-    s = (m == -INFINITY ? 0.0 : s * exp(m - mn)) + (double)p.y * exp((double)p.x - mn);
-    m = mn;
+  // logsumexp over the per-tile partials (or given)
+  double lse;
+  if (lse_in != nullptr) {
+    lse = (double)lse_in[t];
+  } else {
+    double m = -INFINITY, s = 0.0;
+    for (int vt = lane; vt < nVT; vt += 64) {
+      const float2 p = part[(int64_t)vt * Tp + t];
+      const double mn = fmax(m, (double)p.x);
+      s = (m == -INFINITY ? 0.0 : s * exp(m - mn)) + (double)p.y * exp((double)p.x - mn);
+      m = mn;
+    }
+    double M = m;
+    for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
+    s = (m == -INFINITY) ? 0.0 : s * exp(m - M);
+    s = wave_sum_f64(s);
+    lse = M + log(s);
   }
-  double M = m;
-  for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
-  s = (m == -INFINITY) ? 0.0 : s * exp(m - M);
-  s = wave_sum_f64(s);
-  const double lse = M + log(s);
 
   const float* tk = tok + t * TOKF;
   const int nv = (int)tk[TK_NV];
@@ -1456,12 +1471,17 @@ extern "C" size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int
 
 // The loss with optional per-token tokens: labels + ce_weight (cross-entropy
 // term) or, for KD_REVERSE_TT, sampled tokens + their teacher log-probs tly.
+// st_lse / st_z (optional, together): the student's logsumexp [T] and its
+// logits at idx [T, K], already known; the forward GEMM (pass 1) is skipped.
 static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* idx, const float* teacher_logp,
                            const float* m_q, const int32_t* labels, float ce_weight, const float* tly, int64_t T,
                            int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale, float* loss,
                            float* loss_tok, float* lse, float* m_p, float* dh, float* dW, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           void* stream, const float* st_lse = nullptr, const float* st_z = nullptr) {
   LossPlan p;
+  const bool given = st_lse != nullptr || st_z != nullptr;
+  if (given && T > 0 && (st_lse == nullptr || st_z == nullptr))
+    return kd_fail(KD_EINVAL, "the student's logsumexp and its logits at idx come together");
   if (mode < KD_RENORM || mode > KD_REVERSE_TT) return kd_fail(KD_EINVAL, "unknown mode %d", (int)mode);
   if (mode == KD_REVERSE_TT && ce_weight != 0.f)
     return kd_fail(KD_EINVAL, "KD_REVERSE_TT takes no cross-entropy term");
@@ -1503,15 +1523,17 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   float2* part = at<float2>(ws, p.o_part);
   const int lds = TC::LDS_BYTES;
 
-  KD_LAUNCH(k_prep, dim3((unsigned)T), dim3(64), 0, s, idx, teacher_logp, T, V, (int)K,
-                     p.Kp2, p.nVT, p.Tp, sidx, stlp, starts, tok, err);
+  KD_LAUNCH(k_prep, dim3((unsigned)T), dim3(64), 0, s, idx, teacher_logp, given ? st_z : (const float*)nullptr, T, V,
+            (int)K, p.Kp2, p.nVT, p.Tp, sidx, stlp, given ? zS : (float*)nullptr, starts, tok, err);
   KD_LAUNCH_CHECK();
-  // zero the gathered logits so padding slots read as finite values
-  KD_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
-  const int g1 = grid_of(p.nVT * p.nTT);
-  KD_LAUNCH(k_pass1, dim3(g1), dim3(TC::NT), P1_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
-                     p.nVT, p.nTT, p.Tp, sidx, starts, zS, part);
-  KD_LAUNCH_CHECK();
+  if (!given) {
+    // zero the gathered logits so padding slots read as finite values
+    KD_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
+    const int g1 = grid_of(p.nVT * p.nTT);
+    KD_LAUNCH(k_pass1, dim3(g1), dim3(TC::NT), P1_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, V, (int)K,
+              p.nVT, p.nTT, p.Tp, sidx, starts, zS, part);
+    KD_LAUNCH_CHECK();
+  }
   int32_t* ylab = with_y ? at<int32_t>(ws, p.o_ylab) : nullptr;
   if (with_y) {
     KD_LAUNCH(k_label_logit, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, (const bf16_t*)h, (const bf16_t*)W,
@@ -1520,7 +1542,7 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   }
   KD_LAUNCH(k_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, (int)K, p.nVT, p.Tp, (int)mode,
                      scale, part, zS, sidx, stlp, m_q, with_y ? labels : nullptr, ce_weight, tly, V, tok, coef,
-                     ylab, loss_tok, lse, m_p);
+                     ylab, loss_tok, lse, m_p, given ? st_lse : (const float*)nullptr);
   KD_LAUNCH_CHECK();
   KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, tok, err, loss);
   KD_LAUNCH_CHECK();
@@ -1575,6 +1597,22 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
                                           float* dW, void* ws, size_t ws_bytes, void* stream) {
   return loss_impl(h, W, idx, teacher_logp, m_q, nullptr, 0.f, nullptr, T, d, V, K, mode, chunk, scale, loss, loss_tok,
                    lse, m_p, dh, dW, ws, ws_bytes, stream);
+}
+
+extern "C" kd_status kd_topk_loss_fwd_bwd_selected(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                                   const float* teacher_logp, const float* m_q,
+                                                   const float* student_lse, const float* student_logits,
+                                                   const int32_t* sampled, const float* teacher_logp_sampled,
+                                                   int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                                                   int32_t chunk, float scale, float* loss, float* loss_tok,
+                                                   float* lse, float* m_p, float* dh, float* dW, void* ws,
+                                                   size_t ws_bytes, void* stream) {
+  if (T > 0 && (student_lse == nullptr || student_logits == nullptr))
+    return kd_fail(KD_EINVAL, "null required pointer (student_lse, student_logits)");
+  if (sampled != nullptr && mode != KD_REVERSE_TT)
+    return kd_fail(KD_EINVAL, "sampled tokens belong to KD_REVERSE_TT");
+  return loss_impl(h, W, idx, teacher_logp, m_q, sampled, 0.f, teacher_logp_sampled, T, d, V, K, mode, chunk, scale,
+                   loss, loss_tok, lse, m_p, dh, dW, ws, ws_bytes, stream, student_lse, student_logits);
 }
 
 extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
