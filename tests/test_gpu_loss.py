@@ -175,6 +175,22 @@ def test_padding_and_invalid_indices():
     assert np.isnan(c["loss"])
 
 
+@pytest.mark.parametrize("mode", [kd.RENORM, kd.REVERSE])
+def test_duplicate_index_in_sparse_modes_gives_nan(mode):
+    """A duplicated index (invalid) reaches the sparse backward's per-row
+    ranking as two entries of one token: the call must still end normally
+    with a NaN loss."""
+    T, d, V, K = 50, 64, 777, 6
+    h, W, idx, tlp, mq = _case(T, d, V, K, kd.TAIL, seed=5)
+    bad = idx.copy()
+    bad[3, 2] = bad[3, 1]
+    bad[7, 0] = bad[7, 5]
+    c = _run(h, W, bad, tlp, mq, mode, chunk=8192)
+    assert np.isnan(c["loss"])
+    ok = _run(h, W, idx, tlp, mq, mode, chunk=8192)
+    assert np.isfinite(ok["loss"])
+
+
 def test_bitwise_deterministic():
     T, d, V, K = 200, 128, 3000, 9
     for mode in (kd.TAIL, kd.RENORM):

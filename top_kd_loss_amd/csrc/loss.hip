@@ -1274,14 +1274,10 @@ __global__ void k_csr_fill(int64_t T, int K, const int32_t* __restrict__ sidx, c
   ent_r[pos] = coef[i];
 }
 
-// dW[v][j] = sum over the bucket of r * h[t][j].  The products are exact in
-// fp64; they are summed as 64-bit fixed point with a per-column exponent
-// chosen from the largest product, so the result is independent of the
-// bucket order (deterministic) and exact to ~2^-60 of the column's scale.
 // dW rows of the sparse backward, SDW_ROWS vocabulary rows per workgroup and
 // four consecutive features per thread (d % 64 == 0).  A row without entries
 // is written as zeros, one entry as its product.  A row with 2..SDW_SORT
-// entries (the tokens of a row are distinct) has them ranked by token in LDS
+// entries (the tokens of a row are distinct for valid input) has them ranked by token in LDS
 // and summed in fp32 in token order; a longer one (a vocabulary row shared by
 // more than SDW_SORT tokens) takes an exact fixed-point sum.  Both orders are
 // fixed, so dW does not depend on the order the CSR fill wrote the entries.
@@ -1337,9 +1333,11 @@ __global__ __launch_bounds__(256) void k_sparse_dw(const bf16_t* __restrict__ h,
       for (int i = tid; i < n; i += 256) tin[i] = ent_t[b + i];
       __syncthreads();
       for (int i = tid; i < n; i += 256) {
+        // equal tokens (only from a duplicated index, an input error) are
+        // ranked by position, so the ranks stay a permutation of 0..n-1
         const int ti = tin[i];
         int rank = 0;
-        for (int j = 0; j < n; ++j) rank += tin[j] < ti;
+        for (int j = 0; j < n; ++j) rank += (tin[j] < ti) || (tin[j] == ti && j < i);
         ts[rank] = ti;
         rs[rank] = ent_r[b + i];
       }
