@@ -82,3 +82,44 @@ def test_cache_argument_errors():
     rho = (ctypes.c_float * 1)(1.5)
     st = L.kd_topk_rows(None, 4, 100, 4, rho, 1, None, None, None, None, None, None, 0, None)
     assert st == 1 and b"rho" in L.kd_last_error()
+
+
+def _host_ptrs(n, size=4096):
+    """Host buffers standing in for device arrays in calls that must be
+    rejected on the host before any launch."""
+    bufs = [ctypes.create_string_buffer(size + 16) for _ in range(n)]
+    return bufs, [ctypes.c_void_p((ctypes.addressof(b) + 15) & ~15) for b in bufs]
+
+
+def test_selected_entry_argument_errors():
+    L = kd.lib()
+    _, (h, W, idx, tlp, sl, sz, y, loss, dh, dW, ws) = _host_ptrs(11)
+    # the student's logsumexp and logits at idx come together
+    st = L.kd_topk_loss_fwd_bwd_selected(h, W, idx, tlp, None, sl, None, None, None, 8, 64, 100, 4, kd.REVERSE,
+                                         8192, 1.0, loss, None, None, None, dh, dW, ws, 1 << 40, None)
+    assert st == 1 and b"student_lse" in L.kd_last_error()
+    # sampled tokens only with the tail-corrected reverse mode
+    st = L.kd_topk_loss_fwd_bwd_selected(h, W, idx, tlp, None, sl, sz, y, None, 8, 64, 100, 4, kd.REVERSE,
+                                         8192, 1.0, loss, None, None, None, dh, dW, ws, 1 << 40, None)
+    assert st == 1 and b"KD_REVERSE_TT" in L.kd_last_error()
+
+
+def test_cached_lse_entry_argument_errors():
+    L = kd.lib()
+    _, (h, W, g, codes, gs, U, loss, dh, dW, ws) = _host_ptrs(10)
+    st = L.kd_kl_hidden_cached_lse_fwd_bwd(h, W, g, None, None, U, None, None, 8, 64, 64, 300, 512, 1.0, loss, None,
+                                           None, None, dh, dW, ws, 1 << 40, None)
+    assert st == 1 and b"teacher_lse" in L.kd_last_error()
+    _, (tl,) = _host_ptrs(1)
+    st = L.kd_kl_hidden_cached_lse_fwd_bwd(h, W, g, codes, gs, U, None, tl, 8, 64, 64, 300, 512, 1.0, loss, None,
+                                           None, None, dh, dW, ws, 1 << 40, None)
+    assert st == 1 and b"not both" in L.kd_last_error()
+
+
+def test_misaligned_matrix_rejected_before_launch():
+    L = kd.lib()
+    _, (h, W, idx, tlp, loss, dh, dW, ws) = _host_ptrs(8)
+    W_off = ctypes.c_void_p(W.value + 8)
+    st = L.kd_topk_loss_fwd_bwd(h, W_off, idx, tlp, None, 8, 64, 100, 4, kd.RENORM, 8192, 1.0,
+                                loss, None, None, None, dh, dW, ws, 1 << 40, None)
+    assert st == 1 and b"16-byte aligned" in L.kd_last_error()
