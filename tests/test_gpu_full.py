@@ -110,16 +110,25 @@ def test_qwen3_1p7b_head_label_term_and_sampled_token_correction(qwen17_head):
     _check(g, r, toks, voc, "T=4096 V=151936 K=15 reverse_tt")
 
 
-@pytest.mark.timeout(500)
-def test_llama_1b_head_full_mode_k256():
+@pytest.fixture(scope="module")
+def llama_head_k256():
     T, d, V, K = 8192, 2048, 128256, 256
     say("generating T=8192 d=2048 V=128256 K=256 inputs")
     h, W = synth.student_head(T, d, V, seed=2)
     idx, tlp, mq = teacher_cache(T, V, K, seed=2)
-    g = _gpu(h, W, idx, tlp, mq, kd.FULL)
+    return T, d, V, K, h, W, idx, tlp, mq
+
+
+@pytest.mark.timeout(500)
+@pytest.mark.parametrize("mode", [kd.FULL, kd.RENORM])
+def test_llama_1b_head_k256(llama_head_k256, mode):
+    """K=256 over V=128,256: the dense backward (full) and the sparse one
+    (renorm: ~16 tokens per dW row, the ranked per-row sums)."""
+    T, d, V, K, h, W, idx, tlp, mq = llama_head_k256
+    g = _gpu(h, W, idx, tlp, mq, mode)
     toks, voc = _sample_rows(T, V, idx, np.random.default_rng(2))
-    r = sampled_reference(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, kd.FULL, toks, voc, log=say)
-    _check(g, r, toks, voc, "T=8192 V=128256 K=256 mode=full")
+    r = sampled_reference(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode, toks, voc, log=say)
+    _check(g, r, toks, voc, f"T=8192 V=128256 K=256 mode={mode}")
 
 
 @pytest.mark.timeout(500)
