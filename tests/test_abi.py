@@ -123,3 +123,23 @@ def test_misaligned_matrix_rejected_before_launch():
     st = L.kd_topk_loss_fwd_bwd(h, W_off, idx, tlp, None, 8, 64, 100, 4, kd.RENORM, 8192, 1.0,
                                 loss, None, None, None, dh, dW, ws, 1 << 40, None)
     assert st == 1 and b"16-byte aligned" in L.kd_last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No CPU fallback: without the built library every call raises."""
+    monkeypatch.setattr(kd, "_lib", None)
+    monkeypatch.setattr(kd, "LIB_PATH", "/nonexistent/libkdtopk.so")
+    with pytest.raises(kd.KDError, match="not built"):
+        kd.lib()
+
+
+def test_cpu_tensors_are_refused():
+    import torch
+    h = torch.zeros((4, 64), dtype=torch.bfloat16)
+    W = torch.zeros((100, 64), dtype=torch.bfloat16)
+    idx = torch.zeros((4, 2), dtype=torch.int32)
+    tlp = torch.zeros((4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="no CPU path"):
+        kd.loss_fwd_bwd(h, W, idx, tlp, None, mode=kd.RENORM)
+    with pytest.raises(ValueError, match="no CPU path"):
+        kd.cache_build(h, W, None, 2)
