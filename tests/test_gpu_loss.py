@@ -405,3 +405,25 @@ def test_given_selection_equals_recomputed_forward():
     assert rel_fro(b.dW.cpu().numpy(), a.dW.cpu().numpy()) <= 1e-5
     with pytest.raises(ValueError):
         kd.loss_fwd_bwd(hd, Wd, sel.idx, tlp, None, mode=kd.REVERSE, student_lse=sel.lse)
+
+
+@pytest.mark.parametrize("mode", [kd.RENORM, kd.REVERSE])
+def test_sparse_modes_gradient_structure(mode):
+    """Properties of the renormalised objectives on the GPU outputs
+    themselves: dW is exactly zero on every vocabulary row outside all
+    supports, and each token's dh lies in span{W_i - W_j : i, j in S_t}
+    ("The Gradient That Top-k Distillation Never Computes", Theorem 1: the
+    renormalised gradient never leaves that span)."""
+    T, d, V, K = 300, 128, 2500, 13
+    h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=41)
+    g = _run(h, W, idx, tlp, mq, mode, chunk=700)
+    used = np.zeros(V, bool)
+    used[idx[idx >= 0]] = True
+    assert np.all(g["dW"][~used] == 0.0)
+    W64 = synth.as_f64(W)
+    for t in range(0, T, 17):
+        S = idx[t][idx[t] >= 0]
+        A = (W64[S[1:]] - W64[S[0]]).T
+        coef, *_ = np.linalg.lstsq(A, g["dh"][t].astype(np.float64), rcond=None)
+        resid = g["dh"][t] - A @ coef
+        assert np.linalg.norm(resid) <= 1e-2 * np.linalg.norm(g["dh"][t]) + 1e-12, (t, np.linalg.norm(resid))
