@@ -192,3 +192,19 @@ def test_cache_build_integer_logits_bit_exact(rho):
         np.testing.assert_array_equal(o.val.cpu().numpy().view(np.uint32), rv.view(np.uint32))
         np.testing.assert_allclose(o.lse.cpu().numpy(), rlse, atol=1e-5, rtol=0)
         np.testing.assert_allclose(o.m_q.cpu().numpy(), rmq, atol=1e-5, rtol=0)
+
+
+def test_rows_single_pass_degenerate_bounds():
+    """Single-read path with a bound of -inf (fewer finite partial maxima
+    than K): K = V on short rows, and wide rows that are mostly -inf (the
+    collection overflows and the exact kernel takes the row)."""
+    r = np.random.default_rng(43)
+    z = r.standard_normal((6, 300)).astype(np.float32)
+    _check_rows(z, 300, rho=())
+    _check_rows(z, 100, rho=())
+    w = np.full((4, 40000), -np.inf, np.float32)
+    for t in range(4):
+        pos = r.choice(40000, 300 + 400 * t, replace=False)
+        w[t, pos] = r.standard_normal(len(pos)).astype(np.float32)
+    for K in (50, 300, 450):
+        _check_rows(w, K, rho=())
