@@ -143,3 +143,13 @@ def test_cpu_tensors_are_refused():
         kd.loss_fwd_bwd(h, W, idx, tlp, None, mode=kd.RENORM)
     with pytest.raises(ValueError, match="no CPU path"):
         kd.cache_build(h, W, None, 2)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
