@@ -62,7 +62,8 @@ typedef enum {
 } kd_status;
 
 /* Loss modes.  Per token t, with z = W h_t, p = softmax(z), S = the cached
- * indices, q_v = exp(teacher_logp_v) on S, Q = sum_S q, m_p = 1 - sum_S p,
+ * indices, q_v = exp(teacher_logp_v) on S, Q = sum_S q, m_p = sum of p
+ * outside S (= 1 - sum_S p; computed as the sum over the tokens outside S),
  * p_hat / q_hat = p / q renormalized over S:
  *   KD_RENORM  L = KL(q_hat || p_hat)                    [TG abstract, Fig. 2]
  *   KD_TAIL    L = sum_S q log(q/p) + m_q log(m_q/m_p)   [TA abstract; the
@@ -74,7 +75,12 @@ typedef enum {
  *              reverse KL over the top-k tokens plus a tail token]
  *   KD_REVERSE_TT    L = sum_S p log(p/q) (+ the sampled-token tail correction of
  *              kd_topk_loss_fwd_bwd_tt) [TT abstract, Figure 1]
- * The gradient dL/dz is the exact derivative of L; for KD_FULL it is Eq. (3).
+ * For KD_RENORM, KD_TAIL, KD_FULL, KD_REVERSE and KD_TAIL_REVERSE the
+ * gradient dL/dz is the exact derivative of L (for KD_FULL it is Eq. (3)).
+ * KD_REVERSE_TT is an estimator: its dz is sum_S a_v grad p_v with
+ * a = log p - log q held fixed, i.e. the S-part of the full reverse-KL
+ * gradient, which leaves out the p (1_S - P_S) term that differentiating the
+ * reported L through a would add (see kd_topk_loss_fwd_bwd_tt).
  * Tail masses inside logarithms are floored at the smallest normal float. */
 typedef enum {
   KD_RENORM = 0, KD_TAIL = 1, KD_FULL = 2, KD_REVERSE = 3, KD_TAIL_REVERSE = 4, KD_REVERSE_TT = 5
@@ -82,7 +88,7 @@ typedef enum {
 
 /* Bytes of device workspace kd_topk_loss_fwd_bwd needs for these sizes.
  * Linear in T for fixed (d, V, K, chunk).  Returns 0 for invalid sizes. */
-size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk);
+size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode, int32_t chunk);
 
 /* Fused chunked LM head + top-K KD loss, forward and backward [FK sec. 3.2].
  *
@@ -116,7 +122,7 @@ size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_
  * into dh and dW. */
 kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
                                const float* teacher_logp, const float* m_q,
-                               int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                               int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode,
                                int32_t chunk, float scale,
                                float* loss, float* loss_tok, float* lse, float* m_p,
                                float* dh, float* dW,
@@ -124,7 +130,7 @@ kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t
 
 /* Bytes of device workspace kd_topk_loss_fwd_bwd_ce needs (0 for invalid
  * sizes).  A nonzero ce_weight sends every mode through the dense backward. */
-size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk,
+size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode, int32_t chunk,
                                  float ce_weight);
 
 /* kd_topk_loss_fwd_bwd plus a hard-label cross-entropy term [TG abstract:
@@ -141,7 +147,7 @@ size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int
 kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
                                   const float* teacher_logp, const float* m_q,
                                   const int32_t* labels, float ce_weight,
-                                  int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                                  int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode,
                                   int32_t chunk, float scale,
                                   float* loss, float* loss_tok, float* lse, float* m_p,
                                   float* dh, float* dW,
@@ -153,8 +159,10 @@ kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int3
  * with S the selected tokens (e.g. the student's top-k), a = log p - log q
  * on S, y the sampled token and l = log p_y - log q_y:
  *   L_t   = sum_S p a + [y not in S] l          (unbiased for KL(p || q))
- *   dL/dz = p (a [v in S] - sum_S p a) + [y not in S] l (e_y - p)
- * (the gradient of sum_S p a plus l log p_y with l held fixed).
+ *   dz    = p (a [v in S] - sum_S p a) + [y not in S] l (e_y - p)
+ * dz is the estimator's gradient, sum_S a_v grad p_v + l grad log p_y with
+ * a and l held fixed (stop-gradient), not the derivative of L_t: that would
+ * add p_u ([u in S] - sum_S p) from differentiating a = log p - log q.
  *
  * In:  idx, teacher_logp  [T, K]  S and log q on S, full-vocabulary normalised
  *      sampled            [T] int32  y per token, -1 for none (no correction);
@@ -191,7 +199,7 @@ kd_status kd_topk_loss_fwd_bwd_selected(const kd_bf16* h, const kd_bf16* W, cons
                                         const float* teacher_logp, const float* m_q,
                                         const float* student_lse, const float* student_logits,
                                         const int32_t* sampled, const float* teacher_logp_sampled,
-                                        int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                                        int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode,
                                         int32_t chunk, float scale,
                                         float* loss, float* loss_tok, float* lse, float* m_p,
                                         float* dh, float* dW,
@@ -292,24 +300,31 @@ size_t kd_topk_cache_build_workspace(int64_t T, int64_t d, int64_t V, int32_t K,
  *      m_q      [T]    fp32   1 - sum_{top-K} exp(val - lse), the tail mass
  *      k_rho    [T, n_rho] int32  smallest k whose top-k mass reaches rho[j]
  *               over the full row (may exceed K), or NULL when n_rho == 0
- * Teacher log-probabilities for the loss are val - lse. */
+ *      teacher_logp [T, K] fp32  the cached teacher log-probabilities
+ *               val - lse at idx, the loss's teacher_logp input, rounded to
+ *               fp32 from the fp64 difference with the row's fp64
+ *               logsumexp [TG Fig. 3: the top-k cache; FK sec. 3.2: the
+ *               cached top-K teacher values feed the loss]; or NULL (not
+ *               written) */
 kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, const float* b,
                               int64_t T, int64_t d, int64_t V, int32_t K,
                               const float* rho_host, int32_t n_rho,
                               int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
-                              void* ws, size_t ws_bytes, void* stream);
+                              float* teacher_logp, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of device workspace kd_topk_rows needs (4 bytes per row, rounded up
  * to 256; 0 for invalid sizes). */
 size_t kd_topk_rows_workspace(int64_t T, int64_t V, int32_t K, int32_t n_rho);
 
 /* The row pass of the cache build on caller-provided fp32 logits z [T, V]
- * (no NaN): same outputs and ordering rules as kd_topk_cache_build.  On
+ * (no NaN) [TG Fig. 3: keep the k largest teacher logits of each row, with
+ * the discarded tail mass; SS: the adaptive support k_rho]: same outputs
+ * (teacher_logp may be NULL) and ordering rules as kd_topk_cache_build.  On
  * identical fp32 inputs the selected indices and values are exact. */
 kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K,
                        const float* rho_host, int32_t n_rho,
                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
-                       void* ws, size_t ws_bytes, void* stream);
+                       float* teacher_logp, void* ws, size_t ws_bytes, void* stream);
 
 /* Teacher hidden-state recovery from k cached log-probabilities [TG abstract
  * and Table 1: the retained set determines the teacher's distribution from

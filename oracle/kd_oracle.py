@@ -118,10 +118,13 @@ def _loss_row(z: np.ndarray, S: np.ndarray, tl: np.ndarray, m_q: float, mode: in
     elif mode == REVERSE_TT:
         # Top-k part of the tail-corrected reverse-KL gradient estimator
         # ("Unbiased Top-k Estimation for On-Policy Distillation", abstract and
-        # Figure 1): the full-vocabulary reverse KL restricted to S,
-        # sum_S p_v (log p_v - log q_v), with its exact gradient
-        # dz_u = p_u (a_u [u in S] - sum_S p a), a = log p - log q.  The
-        # sampled-token correction is added by _sampled_tail_term.
+        # Figure 1): L is the full-vocabulary reverse KL restricted to S,
+        # sum_S p_v (log p_v - log q_v), and dz is the S-part of the full
+        # reverse-KL gradient, sum_S a_v grad p_v with a = log p - log q held
+        # fixed: dz_u = p_u (a_u [u in S] - sum_S p a).  It is not the
+        # derivative of this L, which would add p_u ([u in S] - sum_S p) from
+        # differentiating a.  The sampled-token correction is added by
+        # _sampled_tail_term.
         a = logp[S] - tl
         L = float(np.sum(p[S] * a))
         dz = -L * p

@@ -138,6 +138,36 @@ def zipf_teacher_logits(T: int, V: int, seed: int = 0, exponent: float = 1.2,
     return np.ascontiguousarray(np.concatenate(_map_blocks(_zipf_block, jobs), axis=0))
 
 
+def zipf_teacher_logits_device(rows: int, V: int, seed: int, device, first_row: int = 0, exponent: float = 1.2,
+                               noise: float = 0.3) -> torch.Tensor:
+    """The Zipf-like teacher recipe above drawn on a GPU with torch's
+    generator, float32 [rows, V] on ``device``: rows first_row .. are keyed by
+    (seed, row block of BLOCK rows) so any row range regenerates alone.  The
+    permutation of each row is the argsort of V iid float64 uniforms (a
+    uniform random permutation; ties have probability ~V^2 2^-54).  Same
+    distribution as zipf_teacher_logits, a different random stream: for
+    large benchmark inputs, where the CPU generator would take minutes."""
+    base = (-exponent * torch.log1p(torch.arange(V, dtype=torch.float64, device=device))).to(torch.float32)
+    out = torch.empty((rows, V), dtype=torch.float32, device=device)
+    gen = torch.Generator(device=device)
+    r = 0
+    while r < rows:
+        row = first_row + r
+        blk = row // BLOCK
+        r1 = min(rows, (blk + 1) * BLOCK - first_row)
+        gen.manual_seed(int(np.random.SeedSequence([int(seed), STREAM_TEACHER, int(blk)]).generate_state(1)[0]))
+        n_blk = min(BLOCK, (blk + 1) * BLOCK) - blk * BLOCK
+        keys = torch.rand((n_blk, V), dtype=torch.float64, device=device, generator=gen)
+        eps = torch.randn((n_blk, V), dtype=torch.float32, device=device, generator=gen)
+        perm = torch.argsort(keys, dim=1)
+        blk_rows = base[perm] + noise * eps
+        o0 = row - blk * BLOCK
+        out[r:r1] = blk_rows[o0:o0 + (r1 - r)]
+        del keys, eps, perm, blk_rows
+        r = r1
+    return out
+
+
 def tie_heavy_logits(rows: int, V: int, seed: int = 0, step: float = 0.25,
                      span: float = 4.0) -> np.ndarray:
     """float32 logits rounded to multiples of ``step`` in [-span, span]: many exact ties."""

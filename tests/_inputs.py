@@ -59,6 +59,17 @@ def student_topk_cache(h: torch.Tensor, W: torch.Tensor, K: int, T: int, V: int,
     return idx, tlp
 
 
+def gather_teacher_logp(idx: np.ndarray, T: int, V: int, seed: int = 0) -> np.ndarray:
+    """Teacher log-probabilities (oracle logsumexp of the full Zipf rows) at
+    the given indices [T, K] (any selection, e.g. the student's top-K)."""
+    out = np.zeros(idx.shape, np.float32)
+    nb = (T + synth.BLOCK - 1) // synth.BLOCK
+    jobs = [(T, V, seed, b, idx[b * synth.BLOCK:min(T, (b + 1) * synth.BLOCK)]) for b in range(nb)]
+    for b, tl in synth._map_blocks(_gather_block, jobs):
+        out[b * synth.BLOCK:b * synth.BLOCK + len(tl)] = tl
+    return out
+
+
 def rel_fro(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

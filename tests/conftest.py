@@ -12,11 +12,6 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
-def pytest_collection_modifyitems(config, items):
-    # Print the case name before each GPU test runs so a fault names its case.
-    pass
-
-
 @pytest.fixture(autouse=True)
 def _announce(request):
     if request.node.get_closest_marker("gpu") is not None:

@@ -80,7 +80,7 @@ def test_cache_argument_errors():
     assert L.kd_topk_cache_build_workspace(16, 64, 1000, 8, 2) > 0
     assert L.kd_topk_cache_build_workspace(16, 64, 1000, 8, 9) == 0
     rho = (ctypes.c_float * 1)(1.5)
-    st = L.kd_topk_rows(None, 4, 100, 4, rho, 1, None, None, None, None, None, None, 0, None)
+    st = L.kd_topk_rows(None, 4, 100, 4, rho, 1, None, None, None, None, None, None, None, 0, None)
     assert st == 1 and b"rho" in L.kd_last_error()
 
 

@@ -27,6 +27,19 @@ def _krho_ok(z_row64, lse, rho, k):
     return ck >= rho - 1e-5 and ckm1 < rho + 1e-5
 
 
+def _check_logp(glp, rv, rlse, rows_ok):
+    """teacher_logp = val - lse against the oracle's fp64 difference: within
+    one fp32 ulp of the value plus 1e-6 (the GPU logsumexp's own rounding)."""
+    ref = oracle.teacher_logp(rv, rlse)[rows_ok]
+    g = glp[rows_ok].astype(np.float64)
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(g[~fin], ref[~fin])
+    ulp = np.spacing(np.abs(ref[fin]).astype(np.float32)).astype(np.float64)
+    err = np.abs(g[fin] - ref[fin])
+    assert np.all(err <= ulp + 1e-6), float((err - ulp).max())
+    return float((err / ulp).max()) if err.size else 0.0
+
+
 def _check_rows(z, K, rho=RHO):
     zt = torch.from_numpy(z).to(DEV)
     o = kd.topk_rows(zt, K, rho)
@@ -39,6 +52,7 @@ def _check_rows(z, K, rho=RHO):
     fin = np.isfinite(rlse)
     np.testing.assert_allclose(glse[fin], rlse[fin], atol=1e-5, rtol=0)
     np.testing.assert_allclose(gmq[fin], rmq[fin], atol=1e-5, rtol=0)
+    _check_logp(o.teacher_logp.cpu().numpy(), rv, rlse, fin)
     exact = 0
     for t in range(z.shape[0]):
         if not fin[t]:
@@ -73,12 +87,17 @@ def test_rows_ties_signed_zero_neg_inf():
         _check_rows(zz, K, rho=(0.5,))
 
 
-def test_rows_gaussian_full_vocab_width():
-    """Rows as wide as the Qwen vocabulary (V = 151,936), Gaussian logits."""
+@pytest.mark.timeout(300)
+def test_rows_full_vocab_width_256_rows():
+    """256 rows as wide as the Qwen vocabulary (V = 151,936), K = 256 and both
+    k_rho targets: 128 Zipf-like teacher rows and 128 Gaussian rows
+    N(0, 1.1) (the cache-build workload's logit statistics)."""
     r = np.random.default_rng(3)
-    z = (r.standard_normal((6, 151936)) * 1.05).astype(np.float32)
-    frac = _check_rows(z, 256)
-    print(f"k_rho exact-match fraction {frac:.3f}")
+    zg = (r.standard_normal((128, 151936)) * np.sqrt(1.1)).astype(np.float32)
+    zz = synth.zipf_teacher_logits(128, 151936, seed=3)
+    for name, z in (("gaussian", zg), ("zipf", zz)):
+        frac = _check_rows(z, 256)
+        print(f"{name}: 128 rows bit-exact; k_rho exact-match fraction {frac:.3f}")
 
 
 def test_rows_k_equals_v_and_ragged():
@@ -107,6 +126,10 @@ def test_cache_build_small_with_bias():
         assert len(set(gi[t].tolist())) == K
     agree = np.mean([len(set(gi[t]) & set(ri[t])) / K for t in range(T)])
     assert agree > 0.99, agree
+    # teacher_logp: the fp64 log-probabilities at the returned entries, up to
+    # the fp32 accumulation of the logits
+    tl = o.teacher_logp.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(tl, np.take_along_axis(z, gi.astype(np.int64), 1) - rlse[:, None], atol=2e-4)
     gk = o.k_rho.cpu().numpy()
     for t in range(0, T, 7):
         for j, r in enumerate(RHO):

@@ -160,6 +160,41 @@ def test_full_vocab_k_equals_v_is_dense_kl():
         assert np.abs(g["m_p"]).max() < 1e-5
 
 
+@pytest.mark.parametrize("mode", [kd.TAIL, kd.TAIL_REVERSE, kd.FULL])
+def test_peaked_student_tail_mass(mode):
+    """A student concentrated on S (retained logits 30 above the rest, so
+    m_p ~ 1e-11) against a teacher with tail mass m_q = 0.3: the tail term
+    m_q log(m_q / m_p) needs m_p to relative accuracy, and the off-S
+    gradient -m_q p / m_p stays bounded only if the ratio never forms.
+    Column 0 of W carries the +30 on the shared support, h's column 0 is 1."""
+    T, d, V, K = 64, 64, 1024, 8
+    rng = np.random.default_rng(23)
+    S = np.array([5, 300, 517, 700, 701, 900, 1020, 1023], np.int32)
+    W = rng.standard_normal((V, d)).astype(np.float32) / 8.0
+    W[:, 0] = 0.0
+    W[S, 0] = 30.0
+    h = rng.standard_normal((T, d)).astype(np.float32)
+    h[:, 0] = 1.0
+    hb, Wb = synth.to_bf16(h), synth.to_bf16(W)
+    idx = np.tile(S, (T, 1))
+    mq = np.full(T, 0.3, np.float32)
+    head = rng.standard_normal((T, K))
+    head = np.exp(head) / np.exp(head).sum(1, keepdims=True)
+    tlp = np.log(0.7 * head).astype(np.float32)
+    g = _run(hb, Wb, idx, tlp, mq, mode, chunk=512)
+    r = oracle.loss_fwd_bwd(synth.as_f64(hb), synth.as_f64(Wb), idx, tlp, mq, mode)
+    assert r["m_p"].max() < 1e-9
+    assert np.isfinite(g["dh"]).all() and np.isfinite(g["dW"]).all()
+    np.testing.assert_allclose(g["m_p"], r["m_p"], rtol=1e-3, atol=0)
+    assert rel_err(g["loss"], r["loss"]) <= LOSS_RTOL, (float(g["loss"]), r["loss"])
+    lt = np.abs(g["loss_tok"] - r["loss_tok"]) / np.maximum(np.abs(r["loss_tok"]), 1e-3)
+    assert lt.max() <= 5e-3, float(lt.max())
+    e_dh, e_dw = rel_fro(g["dh"], r["dh"]), rel_fro(g["dW"], r["dW"])
+    print(f"peaked student mode={mode}: m_p~{float(np.median(r['m_p'])):.2e} loss={float(g['loss']):.5f} "
+          f"ref={r['loss']:.5f} dh={e_dh:.2e} dW={e_dw:.2e}")
+    assert e_dh <= GRAD_RTOL and e_dw <= GRAD_RTOL
+
+
 def test_padding_and_invalid_indices():
     T, d, V, K = 50, 64, 777, 6
     h, W, idx, tlp, mq = _case(T, d, V, K, kd.TAIL, seed=5)

@@ -52,9 +52,10 @@ _SIGS = {
     "kd_teacher_recover": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
-                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_rows_workspace": (_sz, [_i64, _i64, _i32, _i32]),
-    "kd_topk_rows": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kd_topk_rows": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                    _vp]),
     "kd_last_error": (ctypes.c_char_p, []),
     "kd_version": (ctypes.c_char_p, []),
     "kd_profile_begin": (ctypes.c_int, []),
@@ -316,11 +317,12 @@ def teacher_recover(idx: torch.Tensor, teacher_logp: torch.Tensor, U: torch.Tens
 
 
 class CacheOut(NamedTuple):
-    idx: torch.Tensor    # [T, K] int32
-    val: torch.Tensor    # [T, K] fp32
-    lse: torch.Tensor    # [T] fp32
-    m_q: torch.Tensor    # [T] fp32
-    k_rho: torch.Tensor  # [T, n_rho] int32
+    idx: torch.Tensor           # [T, K] int32
+    val: torch.Tensor           # [T, K] fp32
+    lse: torch.Tensor           # [T] fp32
+    m_q: torch.Tensor           # [T] fp32
+    k_rho: torch.Tensor         # [T, n_rho] int32
+    teacher_logp: torch.Tensor  # [T, K] fp32: val - lse, the loss's teacher_logp input
 
 
 def _rho_arr(rho: Sequence[float]):
@@ -329,9 +331,19 @@ def _rho_arr(rho: Sequence[float]):
     return arr, n
 
 
+def _cache_out(T: int, K: int, n: int, dev) -> CacheOut:
+    return CacheOut(torch.empty((T, K), dtype=torch.int32, device=dev),
+                    torch.empty((T, K), dtype=torch.float32, device=dev),
+                    torch.empty(T, dtype=torch.float32, device=dev),
+                    torch.empty(T, dtype=torch.float32, device=dev),
+                    torch.empty((T, n), dtype=torch.int32, device=dev),
+                    torch.empty((T, K), dtype=torch.float32, device=dev))
+
+
 def cache_build(g: torch.Tensor, U: torch.Tensor, b: Optional[torch.Tensor], K: int,
                 rho: Sequence[float] = (), workspace: Optional[torch.Tensor] = None) -> CacheOut:
-    """Teacher cache: top-K of z = U g + b per token, lse, m_q, k_rho (kd_topk_cache_build)."""
+    """Teacher cache: top-K of z = U g + b per token, lse, m_q, k_rho and the
+    teacher log-probabilities val - lse (kd_topk_cache_build)."""
     dev = g.device
     T, d = g.shape
     V = U.shape[0]
@@ -345,21 +357,19 @@ def cache_build(g: torch.Tensor, U: torch.Tensor, b: Optional[torch.Tensor], K: 
     with torch.cuda.device(dev):
         if workspace is None or workspace.numel() < ws_bytes:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-        o = CacheOut(torch.empty((T, K), dtype=torch.int32, device=dev),
-                     torch.empty((T, K), dtype=torch.float32, device=dev),
-                     torch.empty(T, dtype=torch.float32, device=dev),
-                     torch.empty(T, dtype=torch.float32, device=dev),
-                     torch.empty((T, n), dtype=torch.int32, device=dev))
+        o = _cache_out(T, K, n, dev)
         st = L.kd_topk_cache_build(_ptr(g), _ptr(U), _ptr(b), T, d, V, K, arr, n,
                                    _ptr(o.idx), _ptr(o.val), _ptr(o.lse), _ptr(o.m_q),
-                                   _ptr(o.k_rho) if n else None, _ptr(workspace), workspace.numel(), _stream(dev))
+                                   _ptr(o.k_rho) if n else None, _ptr(o.teacher_logp), _ptr(workspace),
+                                   workspace.numel(), _stream(dev))
     _check(st, "kd_topk_cache_build")
     return o
 
 
 def topk_rows(z: torch.Tensor, K: int, rho: Sequence[float] = (),
               workspace: Optional[torch.Tensor] = None) -> CacheOut:
-    """Row pass on fp32 logits z [T, V]: top-K, lse, tail mass, k_rho (kd_topk_rows)."""
+    """Row pass on fp32 logits z [T, V]: top-K, lse, tail mass, k_rho and
+    val - lse (kd_topk_rows)."""
     dev = z.device
     T, V = z.shape
     _need(z, "z", torch.float32, (T, V), dev)
@@ -369,13 +379,10 @@ def topk_rows(z: torch.Tensor, K: int, rho: Sequence[float] = (),
     with torch.cuda.device(dev):
         if workspace is None or workspace.numel() < ws_bytes:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-        o = CacheOut(torch.empty((T, K), dtype=torch.int32, device=dev),
-                     torch.empty((T, K), dtype=torch.float32, device=dev),
-                     torch.empty(T, dtype=torch.float32, device=dev),
-                     torch.empty(T, dtype=torch.float32, device=dev),
-                     torch.empty((T, n), dtype=torch.int32, device=dev))
+        o = _cache_out(T, K, n, dev)
         st = L.kd_topk_rows(_ptr(z), T, V, K, arr, n, _ptr(o.idx), _ptr(o.val), _ptr(o.lse), _ptr(o.m_q),
-                            _ptr(o.k_rho) if n else None, _ptr(workspace), workspace.numel(), _stream(dev))
+                            _ptr(o.k_rho) if n else None, _ptr(o.teacher_logp), _ptr(workspace),
+                            workspace.numel(), _stream(dev))
     _check(st, "kd_topk_rows")
     return o
 

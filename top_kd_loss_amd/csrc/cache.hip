@@ -514,7 +514,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
                                                         const int32_t* __restrict__ flags,
                                                         int32_t* __restrict__ idx_out, float* __restrict__ val_out,
                                                         float* __restrict__ lse_out, float* __restrict__ mq_out,
-                                                        int32_t* __restrict__ krho_out) {
+                                                        int32_t* __restrict__ krho_out, float* __restrict__ logp_out) {
   __shared__ RowShared S;
   const int64_t row = blockIdx.x;
   if (flags != nullptr && flags[row] == 0) return;
@@ -736,6 +736,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
     const float x = zr[i];
     idx_out[row * K + k] = (int32_t)i;
     val_out[row * K + k] = x;
+    if (logp_out != nullptr) logp_out[row * K + k] = (float)((double)x - lse);
     kept += exp((double)x - lse);
   }
   kept = block_sum_d(kept, S);
@@ -893,7 +894,7 @@ __device__ __forceinline__ float cand_value(unsigned long long c) {
 // tail mass 1 - sum over the top K of exp(z - lse).
 __device__ __forceinline__ void fast_emit_topk(FastShared& S, int nKc, int K, const float* zr, int64_t row,
                                                double lse, int32_t* idx_out, float* val_out, float* lse_out,
-                                               float* mq_out) {
+                                               float* mq_out, float* logp_out) {
   const int tid = threadIdx.x;
   for (int p = tid; p < nKc; p += RF) {
     const unsigned long long mine = S.poolK[p];
@@ -905,6 +906,7 @@ __device__ __forceinline__ void fast_emit_topk(FastShared& S, int nKc, int K, co
       const float x = zr[i];  // the stored value keeps its bits (-0.0)
       idx_out[row * K + r] = (int32_t)i;
       val_out[row * K + r] = x;
+      if (logp_out != nullptr) logp_out[row * K + r] = (float)((double)x - lse);
       S.u.m[r] = exp((double)x - lse);
     }
   }
@@ -948,7 +950,8 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
                                                   const float* __restrict__ tmax, int n_tmax,
                                                   int32_t* __restrict__ flags, int32_t* __restrict__ idx_out,
                                                   float* __restrict__ val_out, float* __restrict__ lse_out,
-                                                  float* __restrict__ mq_out, int32_t* __restrict__ krho_out) {
+                                                  float* __restrict__ mq_out, int32_t* __restrict__ krho_out,
+                                                  float* __restrict__ logp_out) {
   __shared__ FastShared S;
   const int64_t row = blockIdx.x;
   const float* zr = z + row * ldz;
@@ -1015,7 +1018,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
       return;
     }
     if (tid == 0) flags[row] = 0;
-    fast_emit_topk(S, nKc, K, zr, row, (double)zmax + log(total), idx_out, val_out, lse_out, mq_out);
+    fast_emit_topk(S, nKc, K, zr, row, (double)zmax + log(total), idx_out, val_out, lse_out, mq_out, logp_out);
     return;
   }
 
@@ -1159,7 +1162,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
       [](int64_t, bool) {});
   __syncthreads();
 
-  fast_emit_topk(S, nKc, K, zr, row, lse, idx_out, val_out, lse_out, mq_out);
+  fast_emit_topk(S, nKc, K, zr, row, lse, idx_out, val_out, lse_out, mq_out, logp_out);
 
   // k_rho: masses of the crossing bin's elements in rank order, then the
   // first rank where the mass from the top reaches rho
@@ -1242,16 +1245,17 @@ static kd_status check_rho(const float* rho_host, int32_t n_rho) {
 // (every row when V is beyond the fast pass's packed counts).  `flags` holds
 // `rows` int32; tmax (optional) the rows' maxima in n_tmax parts each.
 static void launch_rows(const float* z, int64_t ldz, int64_t rows, int64_t V, int K, const float* rho, int n_rho,
-                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho, int32_t* flags,
-                        const float* tmax, int n_tmax, hipStream_t s) {
+                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho, float* logp,
+                        int32_t* flags, const float* tmax, int n_tmax, hipStream_t s) {
   float r[RHO_MAX] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < n_rho; ++j) r[j] = rho[j];
   const bool fast = V <= VFAST_MAX;
   if (fast)
     KD_LAUNCH(k_topk_rows, dim3((unsigned)rows), dim3(RF), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
-                       r[4], r[5], r[6], r[7], tmax, n_tmax, flags, idx, val, lse, m_q, k_rho);
+                       r[4], r[5], r[6], r[7], tmax, n_tmax, flags, idx, val, lse, m_q, k_rho, logp);
   KD_LAUNCH(k_topk_rows_exact, dim3((unsigned)rows), dim3(RT), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
-                     r[4], r[5], r[6], r[7], fast ? (const int32_t*)flags : nullptr, idx, val, lse, m_q, k_rho);
+                     r[4], r[5], r[6], r[7], fast ? (const int32_t*)flags : nullptr, idx, val, lse, m_q, k_rho,
+                     logp);
 }
 
 }  // namespace
@@ -1264,8 +1268,8 @@ extern "C" size_t kd_topk_cache_build_workspace(int64_t T, int64_t d, int64_t V,
 
 extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, const float* b, int64_t T, int64_t d,
                                          int64_t V, int32_t K, const float* rho_host, int32_t n_rho, int32_t* idx,
-                                         float* val, float* lse, float* m_q, int32_t* k_rho, void* ws, size_t ws_bytes,
-                                         void* stream) {
+                                         float* val, float* lse, float* m_q, int32_t* k_rho, float* teacher_logp,
+                                         void* ws, size_t ws_bytes, void* stream) {
   CachePlan p;
   if (!plan_cache(T, d, V, K, n_rho, p))
     return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d n_rho=%d (need 1<=K<=min(V,1024), d%%64==0, 0<=n_rho<=8)",
@@ -1288,7 +1292,8 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
     KD_LAUNCH(k_cache_gemm, dim3(grid), dim3(CC::NT), CG_LDS, s, (const bf16_t*)g + t0 * d,
                        (const bf16_t*)U, b, tb, d, V, nTT, nVT, z, tmax);
     launch_rows(z, V, tb, V, K, rho_host, n_rho, idx + t0 * K, val + t0 * K, lse + t0, m_q + t0,
-                n_rho ? k_rho + t0 * n_rho : nullptr, (int32_t*)((char*)ws + p.o_flags), tmax, nVT, s);
+                n_rho ? k_rho + t0 * n_rho : nullptr, teacher_logp ? teacher_logp + t0 * K : nullptr,
+                (int32_t*)((char*)ws + p.o_flags), tmax, nVT, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
   }
@@ -1302,7 +1307,7 @@ extern "C" size_t kd_topk_rows_workspace(int64_t T, int64_t V, int32_t K, int32_
 
 extern "C" kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K, const float* rho_host,
                                   int32_t n_rho, int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
-                                  void* ws, size_t ws_bytes, void* stream) {
+                                  float* teacher_logp, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || V <= 0 || K < 1 || K > KMAX || K > V || n_rho < 0 || n_rho > RHO_MAX || V >= ((int64_t)1 << 31))
     return kd_fail(KD_EINVAL, "invalid sizes T=%lld V=%lld K=%d n_rho=%d", (long long)T, (long long)V, (int)K, (int)n_rho);
   kd_status st = check_rho(rho_host, n_rho);
@@ -1311,7 +1316,7 @@ extern "C" kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t 
   if (!z || !idx || !val || !lse || !m_q || (n_rho > 0 && !k_rho)) return kd_fail(KD_EINVAL, "null required pointer");
   const size_t need = (size_t)kd_round_up(T * 4, 256);
   if (!ws || ws_bytes < need) return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
-  launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, (int32_t*)ws, nullptr, 0,
+  launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, teacher_logp, (int32_t*)ws, nullptr, 0,
               (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));

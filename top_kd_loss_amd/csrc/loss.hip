@@ -41,7 +41,8 @@ constexpr int SENT = 0x7fffffff;  // sorted-index sentinel (padding)
 enum {
   TK_LSE = 0, TK_ALPHA = 1, TK_L = 2, TK_MP = 3, TK_Q = 4, TK_LSEQ = 5, TK_NV = 6,
   TK_ZY = 7,   // logit of the token's label / sampled token
-  TK_YR = 8,   // scaled dz residual at that token when it lies outside S
+  TK_YR = 8,   // scaled full dz at that token when it lies outside S
+  TK_B = 9,    // reference of the off-S dense term A e^(z - B) (A = TK_ALPHA)
   TOKF = 12
 };
 
@@ -163,16 +164,22 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
 
 // ---------------------------------------------------------------------------
 // pass 1: z^T tile (vocab x tokens) with the logsumexp / gather epilogue.
-// Per token column: (max, sum exp(z - max)) over the tile's vocabulary rows,
-// in-lane over the 64 accumulators plus one xor-32 exchange, merged across
-// the WM wavefront rows in LDS.  z at retained indices is gathered from an
-// fp32 copy of the tile staged in LDS, 128 vocabulary rows at a time, by
-// one thread per token walking its sorted index list.
+// Before the main loop the thread owning token n0 + tid walks the token's
+// sorted indices inside the tile and parks a 256-bit row mask (bit r = row
+// m0 + r is retained) with the sorted position of the first of them.  After
+// the main loop every lane takes, for each of its 4 token columns, the
+// retained rows among its own 64 accumulators: it writes their logits to z_S
+// and sets them to -inf.  The per-token (max, sum exp(z - max)) partials of
+// the tile then cover the vocabulary OUTSIDE S only (in-lane over the 64
+// accumulators plus one xor-32 exchange, merged across the WM wavefront
+// rows in LDS), so the student's tail mass m_p = sum_{v not in S} p_v comes
+// out as a sum of positive terms instead of 1 - sum_S p.
 // ---------------------------------------------------------------------------
 constexpr int P1_RED = TC::WM * TT * 2 * 4;           // (max, sum) per wavefront row and token
-constexpr int P1_Z = TT * TC::TM * 4;                 // fp32 z of 128 vocabulary rows x TT tokens
-constexpr int P1_LDS = P1_RED + P1_Z;
-static_assert(TC::LDS_BYTES + 2 * TC::NT * 4 <= P1_LDS, "pass-1 parking space");
+constexpr int P1_MASKW = VT / 32;                     // mask words per token
+constexpr int P1_PARK = (P1_MASKW + 1) * TC::NT * 4;  // masks + first positions
+constexpr int P1_LDS = TC::LDS_BYTES + P1_PARK;
+static_assert(P1_RED <= TC::LDS_BYTES, "pass-1 reduction space");
 
 // Tile rows at or past vlim (the vocabulary's end) are set to -inf in the
 // accumulators, so the epilogues below need no per-element row test: they
@@ -188,22 +195,32 @@ __device__ __forceinline__ void mask_rows(Acc<TC>& acc, int vlim, int wm, int la
         if (rbase + fm * 32 + 8 * (e >> 2) + (e & 3) >= vlim) acc.v[fm][fn][e] = -KD_INF;
 }
 
-// Row reductions of one wavefront's accumulators per token column.
-__device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, float* red, int wm, int wn, int lane) {
+// Row reductions of one wavefront's accumulators per token column, leaving
+// out the retained rows: bit 8g + r of sm[fn][fm] set = element 4g + r of
+// block (fm, fn) is retained.
+__device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, const uint32_t (&sm)[TC::FN][TC::FM], float* red,
+                                             int wm, int wn, int lane) {
 #pragma unroll
   for (int fn = 0; fn < TC::FN; ++fn) {
     float mx = -KD_INF;
 #pragma unroll
     for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc.v[fm][fn][e]);
+      for (int e = 0; e < 16; ++e) {
+        const bool ret = (sm[fn][fm] >> (8 * (e >> 2) + (e & 3))) & 1u;
+        mx = fmaxf(mx, ret ? -KD_INF : acc.v[fm][fn][e]);
+      }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float nm = (mx == -KD_INF) ? 0.f : -mx * KD_LOG2E;
     float s = 0.f;
 #pragma unroll
     for (int fm = 0; fm < TC::FM; ++fm)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][e], KD_LOG2E, nm));
+      for (int e = 0; e < 16; ++e) {
+        const bool ret = (sm[fn][fm] >> (8 * (e >> 2) + (e & 3))) & 1u;
+        const float x = __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][e], KD_LOG2E, nm));
+        s += ret ? 0.f : x;
+      }
     s += __shfl_xor(s, 32, 64);
     const int col = acc_col<TC>(wn, fn, lane);
     if (lane < 32) {
@@ -211,6 +228,69 @@ __device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, float* red, int
       red[(wm * TT + col) * 2 + 1] = s;
     }
     __builtin_amdgcn_sched_barrier(0);  // one token column's values live at a time
+  }
+}
+
+// Retained-row mask of token ts inside the tile [m0, m0 + VT): bit r of word
+// r / 32 is row m0 + r.  kc0 receives the sorted position of the first
+// retained index >= m0 (K if none).  Indices are read eight at a time.
+__device__ __forceinline__ void tile_row_mask(const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
+                                              int64_t ts, int64_t T, int K, int vt, int64_t Tp, int64_t m0,
+                                              uint32_t (&mk)[P1_MASKW], int& kc0) {
+#pragma unroll
+  for (int w = 0; w < P1_MASKW; ++w) mk[w] = 0u;
+  kc0 = K;
+  if (ts >= T) return;
+  kc0 = starts[(int64_t)vt * Tp + ts];
+  for (int kc = kc0; kc < K; kc += 8) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (kc + j < K) ? sidx[ts * K + kc + j] : SENT;
+    bool done = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t r = (int64_t)v[j] - m0;  // >= 0: sorted from the tile's first entry on
+      if (r < VT) {
+#pragma unroll
+        for (int w = 0; w < P1_MASKW; ++w) mk[w] |= ((int)(r >> 5) == w) ? (1u << (r & 31)) : 0u;
+      } else {
+        done = true;
+      }
+    }
+    if (done) break;
+  }
+}
+
+// The retained rows this lane holds in token column fn: their logits go to
+// z_S, and sm[fm] receives the lane's bits (bit 8g + r = element 4g + r of
+// block fm).  mk: the token's tile mask, kc0 its first sorted position.
+__device__ __forceinline__ void pass1_gather(const Acc<TC>& acc, int fn, const uint32_t (&mk)[P1_MASKW], int kc0,
+                                             int64_t t, int K, float* __restrict__ zS, int wm, int lane,
+                                             uint32_t (&sm)[TC::FM]) {
+  const int h4 = 4 * (lane >> 5);  // this lane's rows: h4 + r of each group of 8
+  uint32_t any = 0u;
+#pragma unroll
+  for (int fm = 0; fm < TC::FM; ++fm) {
+    sm[fm] = ((wm ? mk[TC::FM + fm] : mk[fm]) >> h4) & 0x0F0F0F0Fu;
+    any |= sm[fm];
+  }
+  if (any == 0u) return;
+  int base = kc0;
+  if (wm) {
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm) base += __builtin_popcount(mk[fm]);
+  }
+#pragma unroll
+  for (int fm = 0; fm < TC::FM; ++fm) {
+    const uint32_t w = wm ? mk[TC::FM + fm] : mk[fm];
+    if (sm[fm]) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int bit = 8 * (e >> 2) + h4 + (e & 3);
+        if ((w >> bit) & 1u) zS[t * K + base + __builtin_popcount(w & ((1u << bit) - 1u))] = acc.v[fm][fn][e];
+      }
+    }
+    base += __builtin_popcount(w);
   }
 }
 
@@ -226,70 +306,34 @@ __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const b
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   const int tid = threadIdx.x;
-
-  // thread tid owns token n0 + tid for the gather: first retained index >= m0,
-  // fetched before the main loop and parked in LDS past the operand stages
-  // (nothing stays live in registers across the loop)
-  const int64_t ts = n0 + tid;
+  uint32_t* park = (uint32_t*)((char*)lds + TC::LDS_BYTES);
   {
-    int kc = K, vn = SENT;
-    if (ts < T) {
-      kc = starts[(int64_t)vt * Tp + ts];
-      vn = kc < K ? sidx[ts * K + kc] : SENT;
-    }
-    int* park = (int*)((char*)lds + TC::LDS_BYTES);
-    park[tid] = kc;
-    park[TC::NT + tid] = vn;
+    uint32_t mk[P1_MASKW];
+    int kc0;
+    tile_row_mask(sidx, starts, n0 + tid, T, K, vt, Tp, m0, mk, kc0);
+#pragma unroll
+    for (int w = 0; w < P1_MASKW; ++w) park[w * TC::NT + tid] = mk[w];
+    park[P1_MASKW * TC::NT + tid] = (uint32_t)kc0;
   }
 
   Acc<TC> acc;
   gemm_tile_pipe<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
-  __syncthreads();  // every wavefront is done with the operand stages
-  int kcur, vnext;
-  {
-    const int* park = (const int*)((const char*)lds + TC::LDS_BYTES);
-    kcur = park[tid];
-    vnext = park[TC::NT + tid];
-  }
-  __syncthreads();  // parked values read before the epilogue reuses that LDS
+  __syncthreads();  // every wavefront is done with the operand stages (and the masks are parked)
 
-  float* red = (float*)lds;
-  char* Z = (char*)lds + P1_RED;
   if (MASK) mask_rows(acc, (int)(V - m0), wm, lane);
-  pass1_reduce(acc, red, wm, wn, lane);
-
-  // gather, one half of the tile's vocabulary rows at a time
-  const int rb = 4 * (lane >> 5);
+  uint32_t sm[TC::FN][TC::FM];
 #pragma unroll
-  for (int half = 0; half < TC::WM; ++half) {
-    if (wm == half) {
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int col = acc_col<TC>(wn, fn, lane);
+    uint32_t mk[P1_MASKW];
 #pragma unroll
-      for (int fn = 0; fn < TC::FN; ++fn) {
-        const int tl = acc_col<TC>(wn, fn, lane);
-        char* row = Z + tl * (TC::TM * 4);
-#pragma unroll
-        for (int fm = 0; fm < TC::FM; ++fm)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int vr = fm * 32 + 8 * g + rb;  // multiple of 4
-            *(f32x4*)(row + (((vr >> 2) ^ (tl & 31)) << 4)) =
-                f32x4{acc.v[fm][fn][4 * g], acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]};
-          }
-      }
-    }
-    __syncthreads();
-    const int vh1 = (int)m0 + (half + 1) * TC::TM;
-    if (vnext < vh1) {
-      const char* row = Z + tid * (TC::TM * 4);
-      while (vnext < vh1) {
-        const int vr = vnext - (int)m0 - half * TC::TM;
-        zS[ts * K + kcur] = *(const float*)(row + (((vr >> 2) ^ (tid & 31)) << 4) + (vr & 3) * 4);
-        ++kcur;
-        vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
-      }
-    }
-    __syncthreads();
+    for (int w = 0; w < P1_MASKW; ++w) mk[w] = park[w * TC::NT + col];
+    const int kc0 = (int)park[P1_MASKW * TC::NT + col];
+    pass1_gather(acc, fn, mk, kc0, n0 + col, K, zS, wm, lane, sm[fn]);
   }
+  float* red = (float*)lds;
+  pass1_reduce(acc, sm, red, wm, wn, lane);
+  __syncthreads();
   // merge the WM wavefront rows of the tile and write one partial per token
   for (int col = threadIdx.x; col < TT; col += TC::NT) {
     float m = -KD_INF, s = 0.f;
@@ -354,13 +398,38 @@ __global__ __launch_bounds__(256) void k_label_logit(const bf16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // combine: one wavefront per token.  All per-token math in fp64.
 // ---------------------------------------------------------------------------
+// Pass 1's partials cover the vocabulary outside S, so per token
+//   lse_off = log sum_{v not in S} e^z,  lse_S = log sum_{v in S} e^z,
+//   lse = logaddexp(lse_off, lse_S),    m_p = e^(lse_off - lse),
+// all sums of positive terms.  With the student's lse given instead (pass 1
+// skipped), m_p = -expm1(lse_S - lse) and lse_off = lse + log m_p.
+//
+// The backward's dz is written as
+//   off S:  A e^(z - B)           (dense; A = TK_ALPHA, B = TK_B, scaled)
+//   on S:   coef                  (the full dz of the entry, fp64 -> fp32)
+//   at y:   TK_YR                 (the full dz of a label / sampled token
+//                                  outside S, which pass 2 writes)
+// B = lse, A = the mode's dense coefficient alpha, except in KD_TAIL with
+// m_q > 0, whose off-S gradient (Q + m_q + lam - m_q / m_p) p equals
+// ((Q + m_q + lam) m_p - m_q) e^(z - lse_off): B = lse_off keeps the
+// exponent and the amplitude bounded however small m_p is.  On S the
+// m_q / m_p terms of the dense coefficient and of the residual cancel
+// exactly, so coef takes (Q + m_q + lam) p - q directly.
+//
 // Tokens y per token (labels; -1 = none):
 //  * cross-entropy term (ce_weight != 0): L += ce_weight (lse - z_y),
-//    alpha += ce_weight, residual -ce_weight at y (added to r_y when y is in S);
+//    alpha += ce_weight, residual -ce_weight at y;
 //  * KD_REVERSE_TT (y = the sampled token, tly its teacher log-prob): when y
 //    is outside S, with l = z_y - lse - tly: L += l, alpha -= l, residual +l.
 // ylab[t] = y when y carries a residual outside S (pass 2 writes that entry),
 // else -1.
+__device__ __forceinline__ double logaddexp_d(double a, double b) {
+  if (a == -INFINITY) return b;
+  if (b == -INFINITY) return a;
+  const double m = fmax(a, b);
+  return m + log1p(exp(-fabs(a - b)));
+}
+
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int64_t Tp, int mode, float scale,
                                                  const float2* __restrict__ part, const float* __restrict__ zS,
                                                  const int32_t* __restrict__ sidx, const float* __restrict__ stlp,
@@ -373,14 +442,31 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
-  // logsumexp over the per-tile partials (or given)
-  double lse;
+
+  const float* tk = tok + t * TOKF;
+  const int nv = (int)tk[TK_NV];
+  const double Q = tk[TK_Q], lseq = tk[TK_LSEQ];
+  // retained-logit logsumexp
+  double zmax = -INFINITY;
+  for (int k = lane; k < nv; k += 64) zmax = fmax(zmax, (double)zS[t * K + k]);
+  for (int o = 32; o > 0; o >>= 1) zmax = fmax(zmax, __shfl_xor(zmax, o, 64));
+  double es = 0.0;
+  for (int k = lane; k < nv; k += 64) es += exp((double)zS[t * K + k] - zmax);
+  es = wave_sum_f64(es);
+  const double lseS = (nv > 0) ? zmax + log(es) : -INFINITY;
+
+  double lse, lse_off, mp;
   if (lse_in != nullptr) {
     lse = (double)lse_in[t];
+    mp = (nv > 0) ? -expm1(lseS - lse) : 1.0;
+    if (mp < 0.0) mp = 0.0;
+    lse_off = mp > 0.0 ? lse + log(mp) : -INFINITY;
   } else {
+    // logsumexp of the per-tile partials outside S
     double m = -INFINITY, s = 0.0;
     for (int vt = lane; vt < nVT; vt += 64) {
       const float2 p = part[(int64_t)vt * Tp + t];
+      if (p.x == -KD_INF) continue;
       const double mn = fmax(m, (double)p.x);
       s = (m == -INFINITY ? 0.0 : s * exp(m - mn)) + (double)p.y * exp((double)p.x - mn);
       m = mn;
@@ -389,22 +475,11 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
     for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
     s = (m == -INFINITY) ? 0.0 : s * exp(m - M);
     s = wave_sum_f64(s);
-    lse = M + log(s);
+    lse_off = (s > 0.0) ? M + log(s) : -INFINITY;
+    lse = logaddexp_d(lse_off, lseS);
+    mp = (lse_off == -INFINITY) ? 0.0 : exp(lse_off - lse);
   }
 
-  const float* tk = tok + t * TOKF;
-  const int nv = (int)tk[TK_NV];
-  const double Q = tk[TK_Q], lseq = tk[TK_LSEQ];
-  // student mass on S and the retained-logit logsumexp
-  double zmax = -INFINITY;
-  for (int k = lane; k < nv; k += 64) zmax = fmax(zmax, (double)zS[t * K + k]);
-  for (int o = 32; o > 0; o >>= 1) zmax = fmax(zmax, __shfl_xor(zmax, o, 64));
-  double es = 0.0;
-  for (int k = lane; k < nv; k += 64) es += exp((double)zS[t * K + k] - zmax);
-  es = wave_sum_f64(es);
-  const double lseS = (nv > 0) ? zmax + log(es) : -INFINITY;
-  double mp = (nv > 0) ? -expm1(lseS - lse) : 1.0;
-  if (mp < 0.0) mp = 0.0;
   const double mq = (mode == KD_TAIL || mode == KD_TAIL_REVERSE) ? (double)m_q[t] : 0.0;
   const double tiny = 1.1754943508222875e-38;
   const double mps = mp > tiny ? mp : tiny;
@@ -441,8 +516,9 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
   if (mode == KD_FULL) L += Q * lse;
   const double Lkd = L;  // the distillation term alone (REVERSE's gradient uses it)
 
+  // dense coefficient alpha_S as it acts on S (TAIL's -m_q/m_p acts off S only)
   double alpha = 0.0;
-  if (mode == KD_TAIL) alpha = Q + mq - ratio;
+  if (mode == KD_TAIL) alpha = Q + mq;
   if (mode == KD_TAIL_REVERSE) alpha = -rev_A;
   if (mode == KD_FULL) alpha = Q;
   if (mode == KD_REVERSE_TT) alpha = -L;  // -sum_S p a, a = log p - log q
@@ -466,37 +542,53 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int K, int nVT, int6
     alpha -= ell;
     yres = ell;
   }
+  // off-S dense term A e^(z - B)
+  double A = alpha, B = lse;
+  if (mode == KD_TAIL && mq > 0.0) {
+    if (lse_off == -INFINITY) {
+      A = 0.0;  // S covers the vocabulary: nothing lies off S
+      B = 0.0;
+    } else {
+      A = alpha * mp - mq;
+      B = lse_off;
+    }
+  }
   for (int k = lane; k < K; k += 64) {
-    double r = 0.0;
+    double g = 0.0;  // dL/dz at the entry
     if (k < nv) {
       const double z = zS[t * K + k], tl = stlp[t * K + k];
-      const double q = exp(tl);
+      const double q = exp(tl), p = exp(z - lse);
+      double r;
       if (mode == KD_RENORM) {
         r = exp(z - lseS) - exp(tl - lseq);
-      } else if (mode == KD_TAIL) {
-        r = -q + ratio * exp(z - lse);
-      } else if (mode == KD_TAIL_REVERSE) {
-        r = exp(z - lse) * ((z - lse - tl) - tail_log);
-      } else if (mode == KD_REVERSE_TT) {
-        r = exp(z - lse) * (z - lse - tl);
-      } else if (mode == KD_FULL) {
+      } else if (mode == KD_TAIL || mode == KD_FULL) {
         r = -q;
+      } else if (mode == KD_TAIL_REVERSE) {
+        r = p * ((z - lse - tl) - tail_log);
+      } else if (mode == KD_REVERSE_TT) {
+        r = p * (z - lse - tl);
       } else {
         const double lph = z - lseS, lqh = tl - lseq;
         r = exp(lph) * (lph - lqh - Lkd);
       }
       if (has_y && !tt && sidx[t * K + k] == y) r -= lam;
+      g = alpha * p + r;
     }
-    coef[t * K + k] = (float)(scale * r);
+    coef[t * K + k] = (float)(scale * g);
   }
-  if (ylab != nullptr && lane == 0) ylab[t] = (has_y && !y_in_s && yres != 0.0) ? y : -1;
+  // the full dz at y when it lies outside S
+  double gy = 0.0;
+  const bool y_out = has_y && !y_in_s && yres != 0.0;
+  if (y_out) gy = (A != 0.0 ? A * exp((double)tk[TK_ZY] - B) : 0.0) + yres;
+  if (ylab != nullptr && lane == 0) ylab[t] = y_out ? y : -1;
   if (lane == 0) {
     float* tw = tok + t * TOKF;
     tw[TK_LSE] = (float)lse;
-    tw[TK_ALPHA] = (float)(scale * alpha);
+    tw[TK_ALPHA] = (float)(scale * A);
+    tw[TK_B] = (float)B;
     tw[TK_L] = (float)L;
     tw[TK_MP] = (float)mp;
-    tw[TK_YR] = (float)(scale * yres);
+    tw[TK_YR] = (float)(scale * gy);
     if (loss_tok) loss_tok[t] = (float)L;
     if (lse_out) lse_out[t] = (float)lse;
     if (mp_out) mp_out[t] = (float)mp;
@@ -521,7 +613,8 @@ __global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const
 
 // ---------------------------------------------------------------------------
 // pass 2 (dense modes): recompute the z^T tile of one vocabulary chunk and
-// write dz = alpha * exp(z - lse) (+ r on S) as bf16 token rows,
+// write dz = A * exp(z - B) off S and the combine's full dz on S as bf16
+// token rows,
 // dz [Tp][Cp].  The tile is staged in LDS as E[t][v] (512-byte token rows,
 // 16-byte chunks XOR-swizzled by zdz_swz(t)) and leaves in 16-byte stores,
 // 32 threads per row.  Both backward GEMMs read dz in this one layout (the
@@ -536,8 +629,8 @@ static_assert(TC::LDS_BYTES + (2 * TC::FN + 2) * TC::NT * 4 <= ZDZ_LDS, "pass-2 
 __device__ __forceinline__ int zdz_swz(int t) { return ((t & 3) << 3) | ((t >> 2) & 7); }
 
 
-// Dense part of dz for one tile into E: alpha * exp(z - lse) as bf16, zero
-// for padding tokens (nl = -inf) and for rows masked to -inf.
+// Dense part of dz for one tile into E: A * exp(z - B) as bf16 (the token's
+// off-S term), zero for padding tokens (nl = -inf) and for rows masked to -inf.
 __device__ __forceinline__ void zdz_dense(const Acc<TC>& acc, char* E, int64_t n0, int64_t T,
                                           const float (&lse_t)[TC::FN], const float (&al_t)[TC::FN], int wm, int wn,
                                           int lane) {
@@ -592,7 +685,7 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
     for (int fn = 0; fn < TC::FN; ++fn) {
       const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
       const bool ok = t < T;
-      park[(2 * fn) * TC::NT + tid] = ok ? tok[t * TOKF + TK_LSE] : 0.f;
+      park[(2 * fn) * TC::NT + tid] = ok ? tok[t * TOKF + TK_B] : 0.f;
       park[(2 * fn + 1) * TC::NT + tid] = ok ? tok[t * TOKF + TK_ALPHA] : 0.f;
     }
     int kc = K, vn = SENT;
@@ -625,25 +718,22 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
   if (MASK) mask_rows(acc, (int)(c1 - m0), wm, lane);  // tile rows inside the chunk
   zdz_dense(acc, E, n0, T, lse_t, al_t, wm, wn, lane);
   __syncthreads();
-  // sparse term on S: dz = alpha * exp(z - lse) + r with z gathered in pass 1
+  // entries on S: their full dz, formed in fp64 by the combine
   if (vnext < vend) {
-    const float al = tok[ts * TOKF + TK_ALPHA], ls = tok[ts * TOKF + TK_LSE];
     char* row = E + tid * (VT * 2);
     const int sw = zdz_swz(tid);
     while (vnext < vend) {
       const int vl = vnext - (int)m0;
-      const float val = al * __expf(zS[ts * K + kcur] - ls) + coef[ts * K + kcur];
-      *(bf16_t*)(row + (((vl >> 3) ^ sw) << 4) + (vl & 7) * 2) = f32_to_bf16(val);
+      *(bf16_t*)(row + (((vl >> 3) ^ sw) << 4) + (vl & 7) * 2) = f32_to_bf16(coef[ts * K + kcur]);
       ++kcur;
       vnext = kcur < K ? sidx[ts * K + kcur] : SENT;
     }
   }
-  // label / sampled token outside S: dz = alpha * exp(z_y - lse) + its residual
+  // label / sampled token outside S: its full dz, also from the combine
   if (ylab != nullptr && ts < T) {
     const int y = ylab[ts];
     if (y >= m0 && y < vend) {
-      const float* tk = tok + ts * TOKF;
-      const float val = tk[TK_ALPHA] * __expf(tk[TK_ZY] - tk[TK_LSE]) + tk[TK_YR];
+      const float val = tok[ts * TOKF + TK_YR];
       const int vl = y - (int)m0;
       *(bf16_t*)(E + tid * (VT * 2) + (((vl >> 3) ^ zdz_swz(tid)) << 4) + (vl & 7) * 2) = f32_to_bf16(val);
     }
@@ -1398,6 +1488,8 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.mode = mode;
   p.ce = ce;
   p.dense = (mode == KD_TAIL || mode == KD_FULL || mode == KD_TAIL_REVERSE || mode == KD_REVERSE_TT || ce);
+  // the sparse backward's CSR offsets and positions are int32
+  if (!p.dense && (uint64_t)T * (uint64_t)K >= ((uint64_t)1 << 31)) return false;
   p.Kp2 = 1;
   while (p.Kp2 < K) p.Kp2 <<= 1;
   p.Tp = kd_round_up(T > 0 ? T : 1, TT);
@@ -1448,13 +1540,13 @@ static T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
 
 }  // namespace
 
-extern "C" size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk) {
+extern "C" size_t kd_topk_loss_workspace(int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode, int32_t chunk) {
   LossPlan p;
   if (!plan_loss(T, d, V, K, mode, chunk, false, p)) return 0;
   return p.total;
 }
 
-extern "C" size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk,
+extern "C" size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode, int32_t chunk,
                                             float ce_weight) {
   LossPlan p;
   if (!plan_loss(T, d, V, K, mode, chunk, ce_weight != 0.f, p)) return 0;
@@ -1490,6 +1582,9 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   const bool ce = ce_weight != 0.f;
   if (ce && T > 0 && !labels) return kd_fail(KD_EINVAL, "ce_weight != 0 needs labels");
   const bool with_y = ce || (mode == KD_REVERSE_TT && labels != nullptr);
+  if (!(mode == KD_TAIL || mode == KD_FULL || mode == KD_TAIL_REVERSE || mode == KD_REVERSE_TT || ce) && T > 0 &&
+      (uint64_t)T * (uint64_t)K >= ((uint64_t)1 << 31))
+    return kd_fail(KD_EUNSUPPORTED, "sparse modes need T*K < 2^31 (got T=%lld K=%d)", (long long)T, (int)K);
   if (!plan_loss(T, d, V, K, mode, chunk, ce, p))
     return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0, and chunk*d, T*d, T*chunk bf16 each < 4 GiB)",
                    (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
@@ -1590,7 +1685,7 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
 
 extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
                                           const float* teacher_logp, const float* m_q, int64_t T, int64_t d,
-                                          int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale,
+                                          int64_t V, int32_t K, kd_mode mode, int32_t chunk, float scale,
                                           float* loss, float* loss_tok, float* lse, float* m_p, float* dh,
                                           float* dW, void* ws, size_t ws_bytes, void* stream) {
   return loss_impl(h, W, idx, teacher_logp, m_q, nullptr, 0.f, nullptr, T, d, V, K, mode, chunk, scale, loss, loss_tok,
@@ -1601,7 +1696,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd_selected(const kd_bf16* h, const kd_bf
                                                    const float* teacher_logp, const float* m_q,
                                                    const float* student_lse, const float* student_logits,
                                                    const int32_t* sampled, const float* teacher_logp_sampled,
-                                                   int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode,
+                                                   int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode,
                                                    int32_t chunk, float scale, float* loss, float* loss_tok,
                                                    float* lse, float* m_p, float* dh, float* dW, void* ws,
                                                    size_t ws_bytes, void* stream) {
@@ -1616,7 +1711,7 @@ extern "C" kd_status kd_topk_loss_fwd_bwd_selected(const kd_bf16* h, const kd_bf
 extern "C" kd_status kd_topk_loss_fwd_bwd_ce(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
                                              const float* teacher_logp, const float* m_q, const int32_t* labels,
                                              float ce_weight, int64_t T, int64_t d, int64_t V, int32_t K,
-                                             int32_t mode, int32_t chunk, float scale, float* loss,
+                                             kd_mode mode, int32_t chunk, float scale, float* loss,
                                              float* loss_tok, float* lse, float* m_p, float* dh, float* dW,
                                              void* ws, size_t ws_bytes, void* stream) {
   if (mode == KD_REVERSE_TT) return kd_fail(KD_EINVAL, "KD_REVERSE_TT takes sampled tokens: kd_topk_loss_fwd_bwd_tt");
