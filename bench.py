@@ -42,7 +42,9 @@ HEAD_CFG = dict(T=32768, d=2560, V=151936, K=64, chunk=8192, seed=0)
 QWEN17_CFG = dict(T=4096, d=2048, V=151936, K=15, chunk=8192, seed=1)
 CACHE_CFG = dict(T=16384, d=4096, V=151936, K=256, rho=(0.9, 0.95))
 LLAMA_CFG = dict(T=8192, d=2048, V=128256, K=256, K_rev=16, chunk=8192)
-GEMM_KERNELS = {"k_pass1": 2, "k_zdz": 2, "k_dhdw": 4, "k_cache_gemm": 2}  # x T*d*V FLOP per step
+GEMM_KERNELS = {"k_pass1": 2, "k_zdz": 2, "k_dhdw": 4, "k_cache_gemm": 2,   # x T*d*V FLOP per step
+                "k_pass1_store": 2}
+TOKEN_BLOCK = 8192      # tokens per block of the token-block option
 TEACHER = "Zipf-like logits, exponent 1.2, noise 0.3"
 
 
@@ -260,11 +262,13 @@ def main():
 
     out = loss_out(torch, kd, dev, T, d, V)
 
-    def make_step(md, TT=T, fresh_out=False):
-        ws = torch.empty(kd.loss_workspace_bytes(TT, d, V, K, md, chunk), dtype=torch.uint8, device=dev)
+    def make_step(md, TT=T, fresh_out=False, tb=0):
+        ws = torch.empty(kd.loss_workspace_bytes(TT, d, V, K, md, chunk, token_block=tb), dtype=torch.uint8,
+                         device=dev)
         o = loss_out(torch, kd, dev, TT, d, V) if fresh_out else out
         hh, ii, tt_, mm = hd[:TT], idx[:TT], tlp[:TT], mq[:TT]
-        return lambda: kd.loss_fwd_bwd(hh, Wd, ii, tt_, mm, mode=md, chunk=chunk, workspace=ws, out=o)
+        return lambda: kd.loss_fwd_bwd(hh, Wd, ii, tt_, mm, mode=md, chunk=chunk, workspace=ws, out=o,
+                                       token_block=tb)
 
     torch.cuda.reset_peak_memory_stats()
     step = make_step(mode)
@@ -300,6 +304,24 @@ def main():
         res["other_mode"] = {"mode": {kd.FULL: "full", kd.TAIL: "tail"}[other], "ms_per_step": ms2,
                              "tokens_per_s": T / (ms2 * 1e-3), "mfma_frac_step": cr2 / (ms2 * 1e-3) / PEAK_BF16}
         log(f"[bench] other mode: {ms2:.3f} ms/step")
+
+    if not args.no_extras and mode in (kd.TAIL, kd.FULL):
+        res["token_block"] = {"token_block": TOKEN_BLOCK, "note": "kd_topk_loss_fwd_bwd_tokblock: the block's logits "
+                              "kept as bf16 instead of recomputed in the backward (6TdV executed)"}
+        for md, name in ((kd.TAIL, "tail"), (kd.FULL, "full")):
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            fn = make_step(md, tb=TOKEN_BLOCK)
+            ms_tb = time_steps(torch, fn, args.steps, 2)
+            res["token_block"][name] = {
+                "ms_per_step": ms_tb, "tokens_per_s": T / (ms_tb * 1e-3),
+                "mfma_frac_step": credited_flop(kd, md, T, d, V, K) / (ms_tb * 1e-3) / PEAK_BF16,
+                "peak_mem_bytes": torch.cuda.max_memory_allocated()}
+            if md == mode and not args.no_profile:
+                prof_tb = kernel_profile(kd, torch, fn, 3)
+                res["token_block"][name]["kernels_ms_per_step"] = {k: round(v[0], 4) for k, v in prof_tb.items()}
+            del fn
+        log(f"[bench] token block: {res['token_block']}")
 
     if not args.no_memscan:
         res["memscan"] = memscan(torch, kd, dev, make_step, mode, cfg, args.steps)
@@ -350,8 +372,21 @@ def memscan(torch, kd, dev, make_step, mode, cfg, steps):
         ms = time_steps(torch, fn, steps, 1)
         out[str(T)] = {"peak_bytes_above_inputs": peak, "first_call_s": first, "ms_per_step": ms,
                        "tokens_per_s": T / (ms * 1e-3), "mfma_frac_step": 6 * T * d * V / (ms * 1e-3) / PEAK_BF16}
-        log(f"[bench] memscan T={T}: {out[str(T)]}")
         del fn
+        if mode in (kd.TAIL, kd.FULL):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            fn = make_step(mode, T, fresh_out=True, tb=TOKEN_BLOCK)
+            fn()
+            torch.cuda.synchronize()
+            peak_tb = torch.cuda.max_memory_allocated() - base
+            ms_tb = time_steps(torch, fn, steps, 1)
+            out[str(T)]["token_block"] = {"peak_bytes_above_inputs": peak_tb, "ms_per_step": ms_tb,
+                                          "tokens_per_s": T / (ms_tb * 1e-3),
+                                          "mfma_frac_step": 6 * T * d * V / (ms_tb * 1e-3) / PEAK_BF16}
+            del fn
+        log(f"[bench] memscan T={T}: {out[str(T)]}")
     return out
 
 
@@ -374,10 +409,12 @@ def bench_qwen17(torch, kd, synth, dev, steps):
         "tail_reverse": (kd.TAIL_REVERSE, {}),
         "reverse_tt": (kd.REVERSE_TT, {"labels": y, "labels_teacher_logp": tly}),
         "tail+ce0.1": (kd.TAIL, {"labels": y, "ce_weight": 0.1}),
+        "tail_token_block": (kd.TAIL, {"token_block": TOKEN_BLOCK}),
+        "full_token_block": (kd.FULL, {"token_block": TOKEN_BLOCK}),
     }
     for name, (md, kw) in cases.items():
-        ws = torch.empty(kd.loss_workspace_bytes(T, d, V, K, md, chunk, kw.get("ce_weight", 0.0)),
-                         dtype=torch.uint8, device=dev)
+        ws = torch.empty(kd.loss_workspace_bytes(T, d, V, K, md, chunk, kw.get("ce_weight", 0.0),
+                                                 kw.get("token_block", 0)), dtype=torch.uint8, device=dev)
         fn = lambda: kd.loss_fwd_bwd(hd, Wd, idx, tlp, mq, mode=md, chunk=chunk, workspace=ws, out=out, **kw)
         ms = time_steps(torch, fn, steps, 2)
         cr = credited_flop(kd, md, T, d, V, K)

@@ -128,6 +128,39 @@ kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, const int32_t
                                float* dh, float* dW,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace kd_topk_loss_fwd_bwd_tokblock needs (0 for
+ * invalid sizes, or when token_block (rounded up to 256) times V (rounded
+ * up to 256) bf16 elements reach 4 GiB).  Linear in T plus the logit block
+ * token_block x V x 2 bytes for the dense modes. */
+size_t kd_topk_loss_tokblock_workspace(int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode,
+                                       int32_t token_block);
+
+/* kd_topk_loss_fwd_bwd without the backward's recompute: the token-block
+ * option of the dense modes (KD_TAIL, KD_FULL, KD_TAIL_REVERSE, KD_REVERSE_TT
+ * without sampled tokens).  [FK sec. 4.3] weighs chunking against
+ * recomputation: the vocabulary-chunked call evaluates the LM head twice
+ * (8 T d V FLOP for a 6 T d V step); here tokens are taken token_block at a
+ * time (rounded up to 256) and the block's logits are kept in the
+ * workspace as bf16 exp(z - m) (m a per-256-row maximum), so the head is
+ * evaluated once and dz = A exp(z - B) is formed from them in place.  The
+ * [T, V] logits are never stored: scratch is token_block x V x 2 bytes plus
+ * terms linear in T.  dW accumulates over the blocks in the GEMM epilogue
+ * (no atomics; outputs are bitwise reproducible).
+ *
+ * In / out as kd_topk_loss_fwd_bwd (no chunk argument).  The forward
+ * outputs (loss, loss_tok, lse, m_p) equal those of kd_topk_loss_fwd_bwd
+ * bitwise; dh and dW differ by the rounding of dz (two bf16 roundings
+ * instead of one).  The sparse modes (KD_RENORM, KD_REVERSE), which have no
+ * dense backward to recompute, take the kd_topk_loss_fwd_bwd path.
+ * token_block <= 0 is KD_EINVAL. */
+kd_status kd_topk_loss_fwd_bwd_tokblock(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                        const float* teacher_logp, const float* m_q,
+                                        int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode,
+                                        int32_t token_block, float scale,
+                                        float* loss, float* loss_tok, float* lse, float* m_p,
+                                        float* dh, float* dW,
+                                        void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace kd_topk_loss_fwd_bwd_ce needs (0 for invalid
  * sizes).  A nonzero ce_weight sends every mode through the dense backward. */
 size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode, int32_t chunk,

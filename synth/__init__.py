@@ -156,9 +156,8 @@ def zipf_teacher_logits_device(rows: int, V: int, seed: int, device, first_row: 
         blk = row // BLOCK
         r1 = min(rows, (blk + 1) * BLOCK - first_row)
         gen.manual_seed(int(np.random.SeedSequence([int(seed), STREAM_TEACHER, int(blk)]).generate_state(1)[0]))
-        n_blk = min(BLOCK, (blk + 1) * BLOCK) - blk * BLOCK
-        keys = torch.rand((n_blk, V), dtype=torch.float64, device=device, generator=gen)
-        eps = torch.randn((n_blk, V), dtype=torch.float32, device=device, generator=gen)
+        keys = torch.rand((BLOCK, V), dtype=torch.float64, device=device, generator=gen)
+        eps = torch.randn((BLOCK, V), dtype=torch.float32, device=device, generator=gen)
         perm = torch.argsort(keys, dim=1)
         blk_rows = base[perm] + noise * eps
         o0 = row - blk * BLOCK

@@ -36,9 +36,9 @@ def _sample_rows(T, V, idx, rng, n_tok=12, n_voc=40, chunk=CHUNK):
     return np.array(toks), np.array(sorted(voc))
 
 
-def _gpu(h, W, idx, tlp, mq, mode):
+def _gpu(h, W, idx, tlp, mq, mode, token_block=0):
     out = kd.loss_fwd_bwd(h.to(DEV), W.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV),
-                          torch.from_numpy(mq).to(DEV), mode=mode, chunk=CHUNK)
+                          torch.from_numpy(mq).to(DEV), mode=mode, chunk=CHUNK, token_block=token_block)
     torch.cuda.synchronize()
     return {k: getattr(out, k).cpu().numpy() for k in out._fields}
 
@@ -77,6 +77,9 @@ def test_qwen3_1p7b_head_full_size(qwen17_head, mode):
     toks, voc = _sample_rows(T, V, idx, np.random.default_rng(1))
     r = sampled_reference(h64, W64, idx, tlp, mq, mode, toks, voc, log=say)
     _check(g, r, toks, voc, f"T=4096 V=151936 K=15 mode={oracle.MODE_NAMES[mode]}")
+    if mode in (kd.TAIL, kd.TAIL_REVERSE):
+        gt = _gpu(h, W, idx, tlp, mq, mode, token_block=2048)  # two token blocks
+        _check(gt, r, toks, voc, f"T=4096 V=151936 K=15 mode={oracle.MODE_NAMES[mode]}, token blocks of 2048")
     if mode == kd.RENORM:
         # sparse backward: vocabulary rows outside every support are exactly zero
         used = np.zeros(V, bool)
@@ -193,8 +196,9 @@ def test_qwen3_4b_head_32k_tokens_tail_full_and_linear_memory():
     """T=32,768, d=2560, V=151,936, K=64 (the long-context workload): tail and
     full modes against the oracle over every token (loss, and per-token loss,
     lse and m_p of all 32,768 tokens; dh on sampled tokens; dW on sampled
-    vocabulary rows, each summing over all tokens), and peak memory linear
-    in T over 4K/8K/16K/32K."""
+    vocabulary rows, each summing over all tokens), by the vocabulary-chunked
+    call and by the token-block option (4 blocks of 8192), and peak memory
+    linear in T over 4K/8K/16K/32K."""
     d, V, K, Tmax = 2560, 151936, 64, 32768
     say("generating T=32768 d=2560 V=151936 K=64 inputs")
     h, W = synth.student_head(Tmax, d, V, seed=4)
@@ -216,6 +220,10 @@ def test_qwen3_4b_head_32k_tokens_tail_full_and_linear_memory():
                 say(f"T={T}: peak above inputs {peaks[T] / 2**30:.3f} GiB")
             if T == Tmax:
                 gs[mode] = {k: getattr(out, k).cpu().numpy() for k in out._fields}
+                del out
+                out = kd.loss_fwd_bwd(hd, Wd, i_d, t_d, m_d, mode=mode, token_block=8192)
+                torch.cuda.synchronize()
+                gs[("tb", mode)] = {k: getattr(out, k).cpu().numpy() for k in out._fields}
             del out
         del hd, i_d, t_d, m_d
         torch.cuda.empty_cache()
@@ -231,6 +239,8 @@ def test_qwen3_4b_head_32k_tokens_tail_full_and_linear_memory():
                                    log=say)
     for mode in (kd.TAIL, kd.FULL):
         _check(gs[mode], refs[mode], toks, voc, f"T=32768 d=2560 V=151936 K=64 mode={oracle.MODE_NAMES[mode]}")
+        _check(gs[("tb", mode)], refs[mode], toks, voc,
+               f"T=32768 d=2560 V=151936 K=64 mode={oracle.MODE_NAMES[mode]}, token blocks of 8192")
         # loss is the scaled sum of the per-token losses
         assert rel_err(gs[mode]["loss"], gs[mode]["loss_tok"].astype(np.float64).sum() / Tmax) <= 1e-5
 

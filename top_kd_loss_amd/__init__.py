@@ -33,6 +33,9 @@ _SIGS = {
     "kd_topk_loss_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_loss_ce_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _f32]),
+    "kd_topk_loss_tokblock_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+    "kd_topk_loss_fwd_bwd_tokblock": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                                     _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_loss_fwd_bwd_ce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, _i32, _i32,
                                                _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_kl_hidden_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32]),
@@ -119,7 +122,10 @@ class LossOut(NamedTuple):
     m_p: torch.Tensor       # [T] fp32
 
 
-def loss_workspace_bytes(T: int, d: int, V: int, K: int, mode: int, chunk: int, ce_weight: float = 0.0) -> int:
+def loss_workspace_bytes(T: int, d: int, V: int, K: int, mode: int, chunk: int, ce_weight: float = 0.0,
+                         token_block: int = 0) -> int:
+    if token_block:
+        return int(lib().kd_topk_loss_tokblock_workspace(T, d, V, K, mode, token_block))
     if ce_weight:
         return int(lib().kd_topk_loss_ce_workspace(T, d, V, K, mode, chunk, ce_weight))
     return int(lib().kd_topk_loss_workspace(T, d, V, K, mode, chunk))
@@ -131,14 +137,17 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
                  out: Optional[LossOut] = None, labels: Optional[torch.Tensor] = None,
                  ce_weight: float = 0.0, labels_teacher_logp: Optional[torch.Tensor] = None,
                  student_lse: Optional[torch.Tensor] = None,
-                 student_logits: Optional[torch.Tensor] = None) -> LossOut:
+                 student_logits: Optional[torch.Tensor] = None, token_block: int = 0) -> LossOut:
     """Fused LM head + top-K KD loss, forward and backward (kd_topk_loss_fwd_bwd;
     with labels [T] int32 (-1 = none) and ce_weight > 0, kd_topk_loss_fwd_bwd_ce
     adds the weighted hard-label cross-entropy term; with mode REVERSE_TT,
     labels are the sampled tokens and labels_teacher_logp [T] the teacher's
     log-probabilities at them, kd_topk_loss_fwd_bwd_tt).  student_lse [T] and
     student_logits [T, K] (e.g. lse and val of cache_build(h, W, None, K), the
-    selection of idx) skip the forward pass (kd_topk_loss_fwd_bwd_selected)."""
+    selection of idx) skip the forward pass (kd_topk_loss_fwd_bwd_selected).
+    token_block > 0 takes the token-block path (kd_topk_loss_fwd_bwd_tokblock):
+    the dense modes keep each block's [token_block, V] logits (bf16) instead
+    of recomputing them in the backward; chunk is then unused."""
     if isinstance(mode, str):
         mode = MODE_BY_NAME[mode]
     dev = h.device
@@ -165,10 +174,16 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
         _need(student_logits, "student_logits", torch.float32, (T, K), dev)
     ce = ce_weight != 0.0
     tt = mode == REVERSE_TT and labels is not None
+    if token_block and (sel or ce or labels is not None):
+        raise ValueError("the token-block path takes no labels, sampled tokens or given student logits")
     if scale is None:
         scale = 1.0 / max(T, 1)
     L = lib()
-    ws_bytes = loss_workspace_bytes(T, d, V, K, mode, chunk, ce_weight)
+    ws_bytes = loss_workspace_bytes(T, d, V, K, mode, chunk, ce_weight, token_block)
+    if ws_bytes == 0 and token_block:
+        _check(L.kd_topk_loss_fwd_bwd_tokblock(None, None, None, None, None, T, d, V, K, mode, token_block, scale,
+                                               None, None, None, None, None, None, None, 0, None),
+               "kd_topk_loss_fwd_bwd_tokblock")
     if ws_bytes == 0:
         _check(L.kd_topk_loss_fwd_bwd_ce(None, None, None, None, None, None, ce_weight, T, d, V, K, mode, chunk,
                                          scale, None, None, None, None, None, None, None, 0, None),
@@ -180,7 +195,13 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
             f32 = dict(dtype=torch.float32, device=dev)
             out = LossOut(torch.empty((), **f32), torch.empty((T, d), **f32), torch.empty((V, d), **f32),
                           torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32))
-        if sel:
+        if token_block:
+            st = L.kd_topk_loss_fwd_bwd_tokblock(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
+                                                 T, d, V, K, mode, token_block, scale,
+                                                 _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
+                                                 _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
+                                                 _stream(dev))
+        elif sel:
             st = L.kd_topk_loss_fwd_bwd_selected(_ptr(h), _ptr(W), _ptr(idx), _ptr(teacher_logp), _ptr(m_q),
                                                  _ptr(student_lse), _ptr(student_logits),
                                                  _ptr(labels) if tt else None,
@@ -206,7 +227,8 @@ def loss_fwd_bwd(h: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, teacher_lo
                                         _ptr(out.loss), _ptr(out.loss_tok), _ptr(out.lse), _ptr(out.m_p),
                                         _ptr(out.dh), _ptr(out.dW), _ptr(workspace), workspace.numel(),
                                         _stream(dev))
-    _check(st, "kd_topk_loss_fwd_bwd_selected" if sel else "kd_topk_loss_fwd_bwd_tt" if tt
+    _check(st, "kd_topk_loss_fwd_bwd_tokblock" if token_block else "kd_topk_loss_fwd_bwd_selected" if sel
+           else "kd_topk_loss_fwd_bwd_tt" if tt
            else "kd_topk_loss_fwd_bwd_ce" if ce else "kd_topk_loss_fwd_bwd")
     return out
 

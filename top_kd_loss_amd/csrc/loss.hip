@@ -294,14 +294,53 @@ __device__ __forceinline__ void pass1_gather(const Acc<TC>& acc, int fn, const u
   }
 }
 
+// Token-block variant (STORE): the tile's logits also leave as
+// E = bf16(exp(z - m)) token rows [n][ldE], with m the tile's maximum over
+// the token's vocabulary rows outside S; retained rows, rows past the
+// vocabulary end and padding tokens give 0.  The tile is transposed through
+// LDS (the pass-2 layout) for 16-byte coalesced stores.
+constexpr int P1S_LDS = (VT * TT * 2 > P1_LDS) ? VT * TT * 2 : P1_LDS;
+__device__ __forceinline__ int zdz_swz(int t);
+
+__device__ __forceinline__ void pass1_store_E(const Acc<TC>& acc, const uint32_t (&sm)[TC::FN][TC::FM],
+                                              const float (&mt)[TC::FN], char* Et, int64_t n0, int64_t T, int wm,
+                                              int wn, int lane) {
+  const int rbase = wm * TC::TM + 4 * (lane >> 5);
+#pragma unroll
+  for (int fn = 0; fn < TC::FN; ++fn) {
+    const int tl = acc_col<TC>(wn, fn, lane);
+    const float nl = (n0 + tl < T && mt[fn] != -KD_INF) ? -mt[fn] * KD_LOG2E : -KD_INF;
+    char* row = Et + tl * (VT * 2);
+    const int sw = zdz_swz(tl);
+#pragma unroll
+    for (int fm = 0; fm < TC::FM; ++fm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ret = (sm[fn][fm] >> (8 * g + r)) & 1u;
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc.v[fm][fn][g * 4 + r], KD_LOG2E, nl));
+          x[r] = ret ? 0.f : e;
+        }
+        const int vl = rbase + fm * 32 + 8 * g;
+        uint2 pk;
+        pk.x = pack_bf16x2(x[0], x[1]);
+        pk.y = pack_bf16x2(x[2], x[3]);
+        *(uint2*)(row + (((vl >> 3) ^ sw) << 4) + (vl & 7) * 2) = pk;
+      }
+  }
+}
+
 // One pass-1 tile; MASK: the tile runs past the vocabulary end (own code
 // path, so the common one carries no masking registers).
-template <bool MASK>
+template <bool MASK, bool STORE = false>
 __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                   int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
                                                   int64_t Tp, const int32_t* __restrict__ sidx,
                                                   const int32_t* __restrict__ starts, float* __restrict__ zS,
-                                                  float2* __restrict__ part, int vt, int tt, bf16_t* lds) {
+                                                  float2* __restrict__ part, int vt, int tt, bf16_t* lds,
+                                                  bf16_t* __restrict__ Eg = nullptr, int64_t ldE = 0) {
   const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
@@ -347,6 +386,40 @@ __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const b
     const int64_t t = n0 + col;
     if (t < T) part[(int64_t)vt * Tp + t] = make_float2(m, s);
   }
+  if constexpr (STORE) {
+    float mt[TC::FN];
+#pragma unroll
+    for (int fn = 0; fn < TC::FN; ++fn) {
+      const int col = acc_col<TC>(wn, fn, lane);
+      mt[fn] = fmaxf(red[col * 2], red[(TT + col) * 2]);
+    }
+    __syncthreads();  // red is read before the E tile overwrites it
+    char* Et = (char*)lds;
+    pass1_store_E(acc, sm, mt, Et, n0, T, wm, wn, lane);
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < TT / 8; ++it) {
+      const int tl = it * 8 + (tid >> 5), c = tid & 31;
+      const u32x4 q = *(const u32x4*)(Et + tl * (VT * 2) + ((c ^ zdz_swz(tl)) << 4));
+      *(u32x4*)(Eg + (n0 + tl) * ldE + m0 + c * 8) = q;
+    }
+  }
+}
+
+// Token-block pass 1: as k_pass1, and the tile's E rows go to Eg [nTT*TT][ldE].
+__global__ __launch_bounds__(256, 1) void k_pass1_store(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
+                                                        int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
+                                                        int64_t Tp, const int32_t* __restrict__ sidx,
+                                                        const int32_t* __restrict__ starts, float* __restrict__ zS,
+                                                        float2* __restrict__ part, bf16_t* __restrict__ Eg,
+                                                        int64_t ldE) {
+  extern __shared__ __align__(16) bf16_t lds[];
+  int vt, tt;
+  if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 8, vt, tt)) return;
+  if ((int64_t)(vt + 1) * VT > V)
+    pass1_tile<true, true>(W, h, T, d, V, K, nVT, nTT, Tp, sidx, starts, zS, part, vt, tt, lds, Eg, ldE);
+  else
+    pass1_tile<false, true>(W, h, T, d, V, K, nVT, nTT, Tp, sidx, starts, zS, part, vt, tt, lds, Eg, ldE);
 }
 
 __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
@@ -767,6 +840,46 @@ __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, co
 }
 
 // ---------------------------------------------------------------------------
+// Token-block backward input: E (from k_pass1_store) becomes dz in place.
+// Off S, dz = A e^(z - B) = A e^(m - B) E with m the tile maximum of the
+// pass-1 partial; one thread per 8 consecutive vocabulary rows of a token
+// row (16-byte loads and stores, RNE to bf16).  Padding token rows stay 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dz_scale(bf16_t* __restrict__ E, int64_t ldE, int64_t T, int64_t Tp,
+                                                  const float2* __restrict__ part, const float* __restrict__ tok) {
+  const int64_t t = blockIdx.y;
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (t >= T || c >= ldE) return;
+  const float A = tok[t * TOKF + TK_ALPHA], B = tok[t * TOKF + TK_B];
+  const float m = part[(c / VT) * Tp + t].x;
+  const float f = (A == 0.f || m == -KD_INF) ? 0.f : A * expf(m - B);
+  u32x4* p = (u32x4*)(E + t * ldE + c);
+  u32x4 q = *p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = pack_bf16x2(f * __uint_as_float(q[i] << 16), f * __uint_as_float(q[i] & 0xffff0000u));
+  *p = q;
+}
+
+// The entries on S (the combine's full dz) and at a label / sampled token
+// outside S: thread k < K of token t writes its sorted entry, thread K the
+// token's label entry.
+__global__ __launch_bounds__(256) void k_dz_entries(bf16_t* __restrict__ E, int64_t ldE, int64_t T, int K,
+                                                    const int32_t* __restrict__ sidx, const float* __restrict__ coef,
+                                                    const float* __restrict__ tok, const int32_t* __restrict__ ylab) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * (K + 1)) return;
+  const int64_t t = i / (K + 1);
+  const int k = (int)(i % (K + 1));
+  if (k < K) {
+    if (k < (int)tok[t * TOKF + TK_NV]) E[t * ldE + sidx[t * K + k]] = f32_to_bf16(coef[t * K + k]);
+  } else if (ylab != nullptr) {
+    const int y = ylab[t];
+    if (y >= 0) E[t * ldE + y] = f32_to_bf16(tok[t * TOKF + TK_YR]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dh / dW GEMMs of one chunk in a single launch.  Both are computed as
 // transposed tiles (rows = feature j, columns = token t or vocabulary row v)
 // so that each lane's accumulator group e = 4g..4g+3 holds four consecutive
@@ -780,14 +893,21 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
                                                  const bf16_t* __restrict__ h,
                                                  int64_t T, int64_t d, int64_t Tp, int64_t Cp, int64_t c0,
                                                  int64_t clen, int kdh, int first_chunk, int nTT, int nDT, int nCT,
-                                                 int grid_dh, float* __restrict__ dh, float* __restrict__ dW) {
+                                                 int grid_dh, int dw_first, int dw_accum, float* __restrict__ dh,
+                                                 float* __restrict__ dW) {
   extern __shared__ __align__(16) bf16_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   Acc<TC> acc;
-  if ((int)blockIdx.x < grid_dh) {
+  // the class of tiles with the longer k-loop is dispatched first, so the
+  // short ones fill the CUs at the end of the launch
+  const int grid_dw = (int)gridDim.x - grid_dh;
+  const bool is_dh = dw_first ? (int)blockIdx.x >= grid_dw : (int)blockIdx.x < grid_dh;
+  const int bid = dw_first ? (is_dh ? (int)blockIdx.x - grid_dw : (int)blockIdx.x)
+                           : (is_dh ? (int)blockIdx.x : (int)blockIdx.x - grid_dh);
+  if (is_dh) {
     int dj, ti;
-    if (!tile_of(blockIdx.x, grid_dh, nDT, nTT, 4, dj, ti)) return;
+    if (!tile_of(bid, grid_dh, nDT, nTT, 4, dj, ti)) return;
     const int64_t m0 = (int64_t)dj * TC::BM, n0 = (int64_t)ti * TC::BN;
     gemm_tile_pipe<TC, true, false>(W + c0 * d, d, m0, d, dz, Cp, n0, Tp, kdh, lds, acc, (int)clen);
 #pragma unroll
@@ -814,7 +934,7 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
     }
   } else {
     int dj, ci;
-    if (!tile_of(blockIdx.x - grid_dh, gridDim.x - grid_dh, nDT, nCT, 4, dj, ci)) return;
+    if (!tile_of(bid, grid_dw, nDT, nCT, 4, dj, ci)) return;
     const int64_t m0 = (int64_t)dj * TC::BM, n0 = (int64_t)ci * TC::BN;
     gemm_tile_pipe<TC, true, true>(h, d, m0, d, dz, Cp, n0, clen, (int)Tp, lds, acc, (int)T, (int)Tp);
 #pragma unroll
@@ -825,9 +945,12 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int64_t j = m0 + acc_row<TC>(wm, fm, 4 * g, lane);
-          if (v < clen && j < d)
-            *(f32x4*)(dW + (c0 + v) * d + j) = f32x4{acc.v[fm][fn][4 * g], acc.v[fm][fn][4 * g + 1],
-                                                     acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]};
+          if (v < clen && j < d) {
+            f32x4 x = f32x4{acc.v[fm][fn][4 * g], acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2],
+                            acc.v[fm][fn][4 * g + 3]};
+            if (dw_accum) x += *(const f32x4*)(dW + (c0 + v) * d + j);
+            *(f32x4*)(dW + (c0 + v) * d + j) = x;
+          }
         }
     }
   }
@@ -1464,6 +1587,7 @@ namespace {
 
 struct LossPlan {
   int64_t T, d, V, Tp, Cp, C;
+  int64_t TB, Vp;                                    // token-block path: tokens per block, E row pitch (0: chunked)
   int K, Kp2, mode, nVT, nTT, nDT, nchunks;
   bool ce, dense;                                    // label term; dense backward
   size_t o_sidx, o_stlp, o_zS, o_coef, o_tok, o_starts, o_part, o_err, o_ylab;
@@ -1476,9 +1600,12 @@ static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ce: a hard-label cross-entropy term is present (its dense gradient makes
 // every mode take the dense backward).
+// tb > 0 (dense modes): the token-block path, tb tokens (rounded up to 256)
+// per block with their [tb, V] bf16 logit block kept in the workspace.
 static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, bool ce,
-                      LossPlan& p) {
+                      LossPlan& p, int64_t tb = 0) {
   if (T < 0 || d <= 0 || V <= 0 || K < 1 || K > KMAX || K > V || d % 64 != 0 || d > 16384 || chunk <= 0) return false;
+  if (tb < 0) return false;
   if (mode < KD_RENORM || mode > KD_REVERSE_TT) return false;
   if (V > (int64_t)1 << 30 || T > (int64_t)1 << 26) return false;
   p.T = T;
@@ -1521,7 +1648,15 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   }
   p.o_dz = 0;
   p.o_cnt = p.o_off = p.o_fill = p.o_entt = p.o_entr = p.o_seg = 0;
-  if (p.dense) {
+  p.TB = p.Vp = 0;
+  if (p.dense && tb > 0) {
+    p.TB = kd_round_up(tb, TT);
+    if (p.TB > p.Tp) p.TB = p.Tp;
+    p.Vp = kd_round_up(V, VT);
+    // the dW GEMM reads the block as an MN-major operand with 32-bit byte offsets
+    if ((uint64_t)p.TB * (uint64_t)p.Vp * 2u >= lim || (uint64_t)p.Vp * (uint64_t)d * 2u >= lim) return false;
+    p.o_dz = o; o = align_up(o + (size_t)p.TB * p.Vp * 2);
+  } else if (p.dense) {
     p.o_dz = o; o = align_up(o + (size_t)p.Tp * p.Cp * 2);
   } else {
     p.o_cnt = o; o = align_up(o + (size_t)(V + 1) * 4);
@@ -1553,6 +1688,13 @@ extern "C" size_t kd_topk_loss_ce_workspace(int64_t T, int64_t d, int64_t V, int
   return p.total;
 }
 
+extern "C" size_t kd_topk_loss_tokblock_workspace(int64_t T, int64_t d, int64_t V, int32_t K, kd_mode mode,
+                                                 int32_t token_block) {
+  LossPlan p;
+  if (token_block <= 0 || !plan_loss(T, d, V, K, mode, 8192, false, p, token_block)) return 0;
+  return p.total;
+}
+
 #define KD_LAUNCH_CHECK()                                                              \
   do {                                                                                 \
     hipError_t e_ = hipGetLastError();                                                 \
@@ -1567,7 +1709,8 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
                            const float* m_q, const int32_t* labels, float ce_weight, const float* tly, int64_t T,
                            int64_t d, int64_t V, int32_t K, int32_t mode, int32_t chunk, float scale, float* loss,
                            float* loss_tok, float* lse, float* m_p, float* dh, float* dW, void* ws, size_t ws_bytes,
-                           void* stream, const float* st_lse = nullptr, const float* st_z = nullptr) {
+                           void* stream, const float* st_lse = nullptr, const float* st_z = nullptr,
+                           int64_t tb = 0) {
   LossPlan p;
   const bool given = st_lse != nullptr || st_z != nullptr;
   if (given && T > 0 && (st_lse == nullptr || st_z == nullptr))
@@ -1585,7 +1728,8 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   if (!(mode == KD_TAIL || mode == KD_FULL || mode == KD_TAIL_REVERSE || mode == KD_REVERSE_TT || ce) && T > 0 &&
       (uint64_t)T * (uint64_t)K >= ((uint64_t)1 << 31))
     return kd_fail(KD_EUNSUPPORTED, "sparse modes need T*K < 2^31 (got T=%lld K=%d)", (long long)T, (int)K);
-  if (!plan_loss(T, d, V, K, mode, chunk, ce, p))
+  if (tb > 0 && given) return kd_fail(KD_EINVAL, "the token-block path computes the student's logits itself");
+  if (!plan_loss(T, d, V, K, mode, chunk, ce, p, tb))
     return kd_fail(KD_EINVAL, "invalid sizes T=%lld d=%lld V=%lld K=%d chunk=%d (need 1<=K<=min(V,1024), d%%64==0, d<=16384, chunk>0, and chunk*d, T*d, T*chunk bf16 each < 4 GiB)",
                    (long long)T, (long long)d, (long long)V, (int)K, (int)chunk);
   if (!loss || !dW || !W) return kd_fail(KD_EINVAL, "null required pointer (loss, W, dW)");
@@ -1619,6 +1763,51 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   KD_LAUNCH(k_prep, dim3((unsigned)T), dim3(64), 0, s, idx, teacher_logp, given ? st_z : (const float*)nullptr, T, V,
             (int)K, p.Kp2, p.nVT, p.Tp, sidx, stlp, given ? zS : (float*)nullptr, starts, tok, err);
   KD_LAUNCH_CHECK();
+  if (p.TB > 0) {
+    // Token-block path: per block of TB tokens, pass 1 keeps the block's
+    // logits as E (bf16), the combine gives the block's coefficients, E
+    // becomes dz in place and one dh / dW launch covers the whole
+    // vocabulary (dh written, dW accumulated over the blocks).
+    KD_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
+    int32_t* ylab = with_y ? at<int32_t>(ws, p.o_ylab) : nullptr;
+    if (with_y) {
+      KD_LAUNCH(k_label_logit, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, (const bf16_t*)h, (const bf16_t*)W,
+                labels, T, d, V, tok, err);
+      KD_LAUNCH_CHECK();
+    }
+    bf16_t* E = at<bf16_t>(ws, p.o_dz);
+    const int nDT = p.nDT;
+    for (int64_t t0 = 0; t0 < T; t0 += p.TB) {
+      const int64_t tb = (T - t0 < p.TB) ? T - t0 : p.TB;
+      const int nTTb = (int)kd_ceil_div(tb, TT);
+      const int64_t rows = (int64_t)nTTb * TT;
+      const int g1 = grid_of(p.nVT * nTTb);
+      KD_LAUNCH(k_pass1_store, dim3(g1), dim3(TC::NT), P1S_LDS, s, (const bf16_t*)W, (const bf16_t*)h + t0 * d, tb, d,
+                V, (int)K, p.nVT, nTTb, p.Tp, sidx + t0 * K, starts + t0, zS + t0 * K, part + t0, E, p.Vp);
+      KD_LAUNCH(k_combine, dim3((unsigned)kd_ceil_div(tb, 4)), dim3(256), 0, s, tb, (int)K, p.nVT, p.Tp, (int)mode,
+                scale, part + t0, zS + t0 * K, sidx + t0 * K, stlp + t0 * K, m_q ? m_q + t0 : nullptr,
+                with_y ? labels + t0 : nullptr, ce_weight, tly ? tly + t0 : nullptr, V, tok + t0 * TOKF, coef + t0 * K,
+                ylab ? ylab + t0 : nullptr, loss_tok ? loss_tok + t0 : nullptr, lse ? lse + t0 : nullptr,
+                m_p ? m_p + t0 : nullptr, (const float*)nullptr);
+      KD_LAUNCH(k_dz_scale, dim3((unsigned)kd_ceil_div(p.Vp, 2048), (unsigned)tb), dim3(256), 0, s, E, p.Vp, tb, p.Tp,
+                (const float2*)part + t0, (const float*)tok + t0 * TOKF);
+      KD_LAUNCH(k_dz_entries, dim3((unsigned)kd_ceil_div(tb * (K + 1), 256)), dim3(256), 0, s, E, p.Vp, tb, (int)K,
+                (const int32_t*)sidx + t0 * K, (const float*)coef + t0 * K, (const float*)tok + t0 * TOKF,
+                (const int32_t*)(ylab ? ylab + t0 : nullptr));
+      KD_LAUNCH_CHECK();
+      const int kdh = (int)kd_round_up(V, 64);
+      const int gdh = grid_of(nTTb * nDT);
+      const int nCTw = (int)kd_ceil_div(V, TC::BN);
+      const int gdw = grid_of(nCTw * nDT);
+      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, (const bf16_t*)E, (const bf16_t*)W,
+                (const bf16_t*)h + t0 * d, tb, d, rows, p.Vp, (int64_t)0, V, kdh, 1, nTTb, nDT, nCTw, gdh,
+                rows > kdh ? 1 : 0, t0 > 0 ? 1 : 0, dh + t0 * d, dW);
+      KD_LAUNCH_CHECK();
+    }
+    KD_LAUNCH(k_loss_sum, dim3(1), dim3(1024), 0, s, T, scale, tok, err, loss);
+    KD_LAUNCH_CHECK();
+    return KD_OK;
+  }
   if (!given) {
     // zero the gathered logits so padding slots read as finite values
     KD_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, s, (int32_t*)zS, T * K, 0);
@@ -1656,7 +1845,7 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
       const int nCTw = (int)kd_ceil_div(clen, TC::BN);
       const int gdw = grid_of(nCTw * p.nDT);
       KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0, clen,
-                         kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, dh, dW);
+                         kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, p.Tp > kdh ? 1 : 0, 0, dh, dW);
       KD_LAUNCH_CHECK();
     }
   } else {
@@ -1690,6 +1879,17 @@ extern "C" kd_status kd_topk_loss_fwd_bwd(const kd_bf16* h, const kd_bf16* W, co
                                           float* dW, void* ws, size_t ws_bytes, void* stream) {
   return loss_impl(h, W, idx, teacher_logp, m_q, nullptr, 0.f, nullptr, T, d, V, K, mode, chunk, scale, loss, loss_tok,
                    lse, m_p, dh, dW, ws, ws_bytes, stream);
+}
+
+extern "C" kd_status kd_topk_loss_fwd_bwd_tokblock(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
+                                                   const float* teacher_logp, const float* m_q, int64_t T, int64_t d,
+                                                   int64_t V, int32_t K, kd_mode mode, int32_t token_block,
+                                                   float scale, float* loss, float* loss_tok, float* lse, float* m_p,
+                                                   float* dh, float* dW, void* ws, size_t ws_bytes, void* stream) {
+  if (token_block <= 0) return kd_fail(KD_EINVAL, "token_block must be > 0 (got %d)", (int)token_block);
+  const bool dense = mode == KD_TAIL || mode == KD_FULL || mode == KD_TAIL_REVERSE || mode == KD_REVERSE_TT;
+  return loss_impl(h, W, idx, teacher_logp, m_q, nullptr, 0.f, nullptr, T, d, V, K, mode, 8192, scale, loss, loss_tok,
+                   lse, m_p, dh, dW, ws, ws_bytes, stream, nullptr, nullptr, dense ? token_block : 0);
 }
 
 extern "C" kd_status kd_topk_loss_fwd_bwd_selected(const kd_bf16* h, const kd_bf16* W, const int32_t* idx,
@@ -1867,7 +2067,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     const int gdw = grid_of(nCTw * p.nDT);
     KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)dz, (const bf16_t*)W,
                        (const bf16_t*)h, T, d, p.Tp, p.Cp, c0, clen, kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh,
-                       dh, dW);
+                       p.Tp > kdh ? 1 : 0, 0, dh, dW);
     KD_LAUNCH_CHECK();
   }
   KD_LAUNCH(k_kl_finish, dim3((unsigned)kd_ceil_div(T, 32)), dim3(1024), 0, s, T, p.nVT, p.Tp, (const float*)partQZ,
