@@ -359,6 +359,22 @@ kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K,
                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
                        float* teacher_logp, void* ws, size_t ws_bytes, void* stream);
 
+/* kd_topk_rows for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument; the per-row fallback flags live in a static
+ * device array of the library (1,048,576 rows, 4 MiB per device, held
+ * until the process ends).  Calls nothing that allocates.
+ * Same inputs, outputs and results as kd_topk_rows; T above 1,048,576 is
+ * refused with KD_EUNSUPPORTED.  The array is the current device's: all
+ * calls on one device share it, and every call rewrites the flags of its
+ * rows before reading them, so calls in stream order are independent;
+ * calls that overlap on one device (two streams, or two host threads at
+ * once) race on it and must not be issued. */
+kd_status kd_topk_rows_noalloc(const float* z, int64_t T, int64_t V, int32_t K,
+                               const float* rho_host, int32_t n_rho,
+                               int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
+                               float* teacher_logp, void* stream);
+
 /* Teacher hidden-state recovery from k cached log-probabilities [TG abstract
  * and Table 1: the retained set determines the teacher's distribution from
  * k = d + 1 on].  Per position t, the least-squares solution of

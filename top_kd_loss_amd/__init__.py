@@ -59,6 +59,7 @@ _SIGS = {
     "kd_topk_rows_workspace": (_sz, [_i64, _i64, _i32, _i32]),
     "kd_topk_rows": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                     _vp]),
+    "kd_topk_rows_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kd_last_error": (ctypes.c_char_p, []),
     "kd_version": (ctypes.c_char_p, []),
     "kd_profile_begin": (ctypes.c_int, []),
@@ -406,6 +407,23 @@ def topk_rows(z: torch.Tensor, K: int, rho: Sequence[float] = (),
                             _ptr(o.k_rho) if n else None, _ptr(o.teacher_logp), _ptr(workspace),
                             workspace.numel(), _stream(dev))
     _check(st, "kd_topk_rows")
+    return o
+
+
+def topk_rows_noalloc(z: torch.Tensor, K: int, rho: Sequence[float] = (), out: Optional[CacheOut] = None) -> CacheOut:
+    """kd_topk_rows_noalloc: the row pass with the library's static device
+    scratch instead of a workspace (at most 1,048,576 rows; calls on one
+    device must not overlap).  `out` (a CacheOut of the right shapes) lets
+    the caller allocate nothing either."""
+    dev = z.device
+    T, V = z.shape
+    _need(z, "z", torch.float32, (T, V), dev)
+    arr, n = _rho_arr(rho)
+    with torch.cuda.device(dev):
+        o = out if out is not None else _cache_out(T, K, n, dev)
+        st = lib().kd_topk_rows_noalloc(_ptr(z), T, V, K, arr, n, _ptr(o.idx), _ptr(o.val), _ptr(o.lse), _ptr(o.m_q),
+                                        _ptr(o.k_rho) if n else None, _ptr(o.teacher_logp), _stream(dev))
+    _check(st, "kd_topk_rows_noalloc")
     return o
 
 

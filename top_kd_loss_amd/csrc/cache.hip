@@ -31,9 +31,18 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/kdtopk.h"
 #include "gemm.h"
 #include "kd_internal.h"
+
+// Scratch of kd_topk_rows_noalloc: one fallback flag per row, for callers
+// that cannot allocate.  Each device holds its own copy until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// returns for that device.
+constexpr int64_t KD_NOALLOC_ROWS = (int64_t)1 << 20;
+static __device__ __align__(256) int32_t scratch[KD_NOALLOC_ROWS];
 
 namespace {
 
@@ -1297,6 +1306,47 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
   }
+  return KD_OK;
+}
+
+// Device address of `scratch` on the current device, taken once per device.
+static kd_status noalloc_scratch(int32_t** out) {
+  static std::mutex mu;
+  static int32_t* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kd_fail(KD_EHIP, "hipGetDevice failed");
+  if (dev >= 64) return kd_fail(KD_EUNSUPPORTED, "device %d beyond the 64 this library tracks", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return kd_fail(KD_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = (int32_t*)p;
+  }
+  *out = addr[dev];
+  return KD_OK;
+}
+
+extern "C" kd_status kd_topk_rows_noalloc(const float* z, int64_t T, int64_t V, int32_t K, const float* rho_host,
+                                          int32_t n_rho, int32_t* idx, float* val, float* lse, float* m_q,
+                                          int32_t* k_rho, float* teacher_logp, void* stream) {
+  if (T < 0 || V <= 0 || K < 1 || K > KMAX || K > V || n_rho < 0 || n_rho > RHO_MAX || V >= ((int64_t)1 << 31))
+    return kd_fail(KD_EINVAL, "invalid sizes T=%lld V=%lld K=%d n_rho=%d", (long long)T, (long long)V, (int)K, (int)n_rho);
+  kd_status st = check_rho(rho_host, n_rho);
+  if (st != KD_OK) return st;
+  if (T > KD_NOALLOC_ROWS)
+    return kd_fail(KD_EUNSUPPORTED, "kd_topk_rows_noalloc takes at most %lld rows per call (got %lld)",
+                   (long long)KD_NOALLOC_ROWS, (long long)T);
+  if (T == 0) return KD_OK;
+  if (!z || !idx || !val || !lse || !m_q || (n_rho > 0 && !k_rho)) return kd_fail(KD_EINVAL, "null required pointer");
+  int32_t* flags = nullptr;
+  st = noalloc_scratch(&flags);
+  if (st != KD_OK) return st;
+  launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, teacher_logp, flags, nullptr, 0,
+              (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
   return KD_OK;
 }
 
