@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--no-memscan", action="store_true",
                     help="skip peak memory and tokens/s vs T (4K..32K) on the headline workload")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="also time the vendor GEMM (torch.mm: hipBLASLt) on the three LM-head GEMM shapes of the "
+                         "headline workload, for context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device copies of 1 GiB (fp32) for HBM counter calibration")
     args = ap.parse_args()
@@ -326,6 +329,10 @@ def main():
     if not args.no_memscan:
         res["memscan"] = memscan(torch, kd, dev, make_step, mode, cfg, args.steps)
 
+    if args.gemm_reference:
+        res["gemm_reference"] = gemm_reference(torch, dev, cfg)
+        log(f"[bench] vendor GEMM reference: {res['gemm_reference']}")
+
     zt_rows = None
     if not args.no_cpu_baseline:
         zt_rows = synth.zipf_teacher_logits_device(2048, V, cfg["seed"], dev).cpu().numpy()
@@ -349,6 +356,31 @@ def main():
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def gemm_reference(torch, dev, cfg, steps=5):
+    """The vendor bf16 GEMM (torch.mm, hipBLASLt on ROCm; fp32 accumulation,
+    bf16 output) on the LM-head GEMM shapes of one 8192-token block of the
+    headline workload: logits h W^T (pass 1 and its recompute), dW = dz^T h
+    and dh = dz W, with contiguous operands.  Context for the library's own
+    kernels, which carry the loss epilogues as well."""
+    T, d, V = 8192, cfg["d"], cfg["V"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    h = torch.randn((T, d), device=dev, generator=g).to(torch.bfloat16)
+    Wt = (torch.randn((d, V), device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)   # W^T
+    dz = (torch.randn((T, V), device=dev, generator=g) * 1e-5).to(torch.bfloat16)
+    dzt = dz.t().contiguous()
+    W = Wt.t().contiguous()
+    out = {}
+    for name, a, b in (("logits h W^T", h, Wt), ("dW = dz^T h", dzt, h), ("dh = dz W", dz, W)):
+        ms = time_steps(torch, lambda: torch.mm(a, b), steps, 2)
+        fl = 2.0 * a.shape[0] * a.shape[1] * b.shape[1]
+        out[name] = {"M": a.shape[0], "N": b.shape[1], "K": a.shape[1], "ms": ms,
+                     "TFLOP_s": fl / (ms * 1e-3) / 1e12, "frac_of_2.5PF": fl / (ms * 1e-3) / PEAK_BF16}
+    del h, Wt, dz, dzt, W
+    torch.cuda.empty_cache()
+    return out
 
 
 def memscan(torch, kd, dev, make_step, mode, cfg, steps):
