@@ -393,6 +393,31 @@ kd_status kd_teacher_recover(const int32_t* idx, const float* teacher_logp, cons
                              int64_t T, int64_t d, int64_t V, int32_t k, float* g_hat, float* c_hat,
                              void* stream);
 
+/* Bytes of device workspace kd_teacher_recover_ws needs (0 for invalid
+ * sizes): per position one fp64 copy of the system (max(k, d+1) rows, even
+ * pitch) plus four fp64 vectors, and one int32 flag. */
+size_t kd_teacher_recover_workspace(int64_t T, int64_t d, int32_t k);
+
+/* kd_teacher_recover at the widths of real teachers (d in the thousands;
+ * k and d + 2 up to 65,536), with the system in a caller-owned workspace
+ * and solved by many workgroups [TG abstract and Table 1: from k = d + 1
+ * cached log-probabilities on, the teacher's distribution is determined].
+ * Per position, fp64:
+ *   k >= d + 1: the least-squares solution of [U_S, -1] (g; c) = log q_S - b_S
+ *               by Householder QR (column by column, every trailing column
+ *               updated in parallel) and back substitution;
+ *   k <= d:     the system is underdetermined (the teacher is not
+ *               identifiable from S): the minimum-norm solution, by
+ *               Householder QR of the transposed system, R^T w = y and
+ *               x = Q [w; 0].
+ * In / out as kd_teacher_recover (1 <= k <= V; at most 65,535 positions per
+ * call); ws of kd_teacher_recover_workspace(T, d, k) bytes, 8-byte aligned.
+ * Non-finite outputs when the system is singular; NaN for a position with an
+ * index out of range. */
+kd_status kd_teacher_recover_ws(const int32_t* idx, const float* teacher_logp, const kd_bf16* U, const float* b,
+                                int64_t T, int64_t d, int64_t V, int32_t k, float* g_hat, float* c_hat,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Message describing the last non-KD_OK status returned on this thread. */
 const char* kd_last_error(void);
 

@@ -53,6 +53,8 @@ _SIGS = {
     "kd_kl_hidden_cached_lse_fwd_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                                        _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_teacher_recover": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "kd_teacher_recover_workspace": (_sz, [_i64, _i64, _i32]),
+    "kd_teacher_recover_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
     "kd_topk_cache_build_workspace": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "kd_topk_cache_build": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -320,9 +322,13 @@ def kl_hidden_fwd_bwd(h: torch.Tensor, W: torch.Tensor, g: torch.Tensor, U: torc
 
 
 def teacher_recover(idx: torch.Tensor, teacher_logp: torch.Tensor, U: torch.Tensor,
-                    b: Optional[torch.Tensor] = None):
-    """Teacher hidden state and logsumexp from k >= d + 1 cached log-probs
-    (kd_teacher_recover): returns (g_hat [T, d] fp32, c_hat [T] fp32)."""
+                    b: Optional[torch.Tensor] = None, multi_workgroup: Optional[bool] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Teacher hidden state and logsumexp from k cached log-probs: returns
+    (g_hat [T, d] fp32, c_hat [T] fp32).  The one-workgroup solver in LDS
+    (kd_teacher_recover) serves small systems with k >= d + 1; wide heads,
+    and k <= d (the minimum-norm solution), take the multi-workgroup one
+    (kd_teacher_recover_ws).  multi_workgroup forces the choice."""
     dev = idx.device
     T, k = idx.shape
     V, d = U.shape
@@ -333,9 +339,21 @@ def teacher_recover(idx: torch.Tensor, teacher_logp: torch.Tensor, U: torch.Tens
         _need(b, "b", torch.float32, (V,), dev)
     g_hat = torch.empty((T, d), dtype=torch.float32, device=dev)
     c_hat = torch.empty(T, dtype=torch.float32, device=dev)
+    kp = k + 1 if k % 2 == 0 else k
+    if multi_workgroup is None:
+        multi_workgroup = k < d + 1 or (d + 2) * kp > 19968
     with torch.cuda.device(dev):
-        _check(lib().kd_teacher_recover(_ptr(idx), _ptr(teacher_logp), _ptr(U), _ptr(b), T, d, V, k,
-                                        _ptr(g_hat), _ptr(c_hat), _stream(dev)), "kd_teacher_recover")
+        if multi_workgroup:
+            L = lib()
+            nb = int(L.kd_teacher_recover_workspace(T, d, k))
+            if workspace is None or workspace.numel() < nb:
+                workspace = torch.empty(max(nb, 8), dtype=torch.uint8, device=dev)
+            _check(L.kd_teacher_recover_ws(_ptr(idx), _ptr(teacher_logp), _ptr(U), _ptr(b), T, d, V, k,
+                                           _ptr(g_hat), _ptr(c_hat), _ptr(workspace), workspace.numel(),
+                                           _stream(dev)), "kd_teacher_recover_ws")
+        else:
+            _check(lib().kd_teacher_recover(_ptr(idx), _ptr(teacher_logp), _ptr(U), _ptr(b), T, d, V, k,
+                                            _ptr(g_hat), _ptr(c_hat), _stream(dev)), "kd_teacher_recover")
     return g_hat, c_hat
 
 
