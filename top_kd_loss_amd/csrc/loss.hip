@@ -401,7 +401,8 @@ __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const b
     for (int it = 0; it < TT / 8; ++it) {
       const int tl = it * 8 + (tid >> 5), c = tid & 31;
       const u32x4 q = *(const u32x4*)(Et + tl * (VT * 2) + ((c ^ zdz_swz(tl)) << 4));
-      *(u32x4*)(Eg + (n0 + tl) * ldE + m0 + c * 8) = q;
+      // streamed past the caches: the block of E is far larger than them
+      __builtin_nontemporal_store(q, (u32x4*)(Eg + (n0 + tl) * ldE + m0 + c * 8));
     }
   }
 }
@@ -854,11 +855,11 @@ __global__ __launch_bounds__(256) void k_dz_scale(bf16_t* __restrict__ E, int64_
   const float m = part[(c / VT) * Tp + t].x;
   const float f = (A == 0.f || m == -KD_INF) ? 0.f : A * expf(m - B);
   u32x4* p = (u32x4*)(E + t * ldE + c);
-  u32x4 q = *p;
+  u32x4 q = __builtin_nontemporal_load(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     q[i] = pack_bf16x2(f * __uint_as_float(q[i] << 16), f * __uint_as_float(q[i] & 0xffff0000u));
-  *p = q;
+  __builtin_nontemporal_store(q, p);
 }
 
 // The entries on S (the combine's full dz) and at a label / sampled token
