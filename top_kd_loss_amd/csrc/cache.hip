@@ -779,11 +779,11 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
 // lowest bin) are flagged for k_topk_rows_exact.
 // ---------------------------------------------------------------------------
 constexpr int RF = 512;                        // threads of the fast row kernel
-constexpr int NBL = 4096;                      // value bins
+constexpr int NBL = 8192;                      // value bins
 constexpr int BPT = NBL / RF;                  // bins per thread in the scans
-constexpr float BIN_INVW = 128.f;              // bins per unit of logit
-constexpr float BIN_W = 1.f / 128.f;
-constexpr int CAPK = 2048;                     // top-K candidates
+constexpr float BIN_INVW = 256.f;              // bins per unit of logit
+constexpr float BIN_W = 1.f / 256.f;
+constexpr int CAPK = 1536;                     // top-K candidates
 constexpr int CAPR = 2048;                     // crossing-bin candidates, all targets
 constexpr int CNT_SHIFT = 46;
 constexpr unsigned long long MASS_MASK = (1ull << CNT_SHIFT) - 1ull;
@@ -792,10 +792,12 @@ constexpr int64_t VFAST_MAX = ((int64_t)1 << 18) - 1;  // bin counts fit 18 bits
 struct FastShared {
   union {
     unsigned long long hist[NBL];  // pass B and the scans
-    double m[CAPR];                // candidate masses by rank (after pass C)
+    struct {
+      unsigned long long poolR[CAPR];  // crossing-bin candidates (pass C)
+      double m[CAPR];                  // candidate masses by rank
+    } c;
   } u;
   unsigned long long poolK[CAPK];  // ((~key) << 32) | index
-  unsigned long long poolR[CAPR];
   unsigned long long scan_m[RF / 64];
   int scan_c[RF / 64];
   double red_d[RF / 64];
@@ -806,9 +808,11 @@ struct FastShared {
   int tau_ok;
   int bK, aboveK, nbK, fillK;
   int bR[RHO_MAX], cntAboveR[RHO_MAX], nR[RHO_MAX], fillR[RHO_MAX], segR[RHO_MAX];
-  unsigned long long massAboveR[RHO_MAX];
+  unsigned long long massAboveR[RHO_MAX], massR[RHO_MAX];
+  int kres[RHO_MAX];               // k_rho resolved from the histogram alone (0: not resolved)
   float rho[RHO_MAX];
 };
+static_assert(sizeof(FastShared) <= 80 * 1024, "two rows per CU");
 
 // Value bin of x below the row maximum: monotone non-increasing in x
 // (rounded subtraction, exact scaling by 128); -inf goes to the last bin.
@@ -916,12 +920,12 @@ __device__ __forceinline__ void fast_emit_topk(FastShared& S, int nKc, int K, co
       idx_out[row * K + r] = (int32_t)i;
       val_out[row * K + r] = x;
       if (logp_out != nullptr) logp_out[row * K + r] = (float)((double)x - lse);
-      S.u.m[r] = exp((double)x - lse);
+      S.u.c.m[r] = exp((double)x - lse);
     }
   }
   __syncthreads();
   double kept = 0.0;
-  for (int r = tid; r < K; r += RF) kept += S.u.m[r];
+  for (int r = tid; r < K; r += RF) kept += S.u.c.m[r];
   kept = fast_block_sum(kept, S);
   if (tid == 0) {
     lse_out[row] = (float)lse;
@@ -953,7 +957,7 @@ __device__ __forceinline__ void fast_tau(const float* a, int n, int K, FastShare
   __syncthreads();
 }
 
-__global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
+__global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
                                                   int n_rho, float rho0, float rho1, float rho2, float rho3,
                                                   float rho4, float rho5, float rho6, float rho7,
                                                   const float* __restrict__ tmax, int n_tmax,
@@ -980,12 +984,12 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     if (tid == 0) flags[row] = 1;
     return;
   }
-  // Without k_rho targets the top-K candidates can be collected during pass B
-  // already: every element >= tau (a lower bound of the K-th largest value,
-  // from the producer's tile maxima or the threads' maxima of pass A).
-  bool onepass = false;
+  // The top-K candidates are collected during pass B already: every element
+  // >= tau, a lower bound of the K-th largest value (from the producer's
+  // tile maxima or the threads' maxima of pass A).
   float tau = 0.f;
-  if (n_rho == 0) {
+  bool collectK = false;
+  {
     float* a = (float*)S.u.hist;
     int n;
     if (tmax != nullptr) {
@@ -997,18 +1001,17 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     }
     __syncthreads();
     fast_tau(a, n, K, S);
-    onepass = S.tau_ok != 0;
+    collectK = S.tau_ok != 0;
     tau = S.tau;
+    if (tid == 0) S.fillK = 0;
     __syncthreads();  // a[] is overwritten by the histogram below
   }
 
-  if (onepass) {
+  if (n_rho == 0 && collectK) {
     // ---- B': one read: the exponential sum (fp64 per thread, then the fixed
     // block order: deterministic) and the elements >= tau.  The top K are
     // among them; more than CAPK of them (a huge tie) sends the row to the
     // exact kernel.
-    if (tid == 0) S.fillK = 0;
-    __syncthreads();
     double acc = 0.0;
     row_loop_pipe<RF>(
         zr, V, vec,
@@ -1031,16 +1034,21 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     return;
   }
 
-  // ---- B: packed (count, fixed-point mass) histogram of the value bins
+  // ---- B: packed (count, fixed-point mass) histogram of the value bins,
+  // and the elements >= tau
   for (int i = tid; i < NBL; i += RF) S.u.hist[i] = 0ull;
   __syncthreads();
   row_loop_pipe<RF>(
       zr, V, vec,
-      [&](int64_t, float x, int) {
+      [&](int64_t i, float x, int) {
         const int b = vbin(x, zmax);
         const float m = __builtin_amdgcn_exp2f((x - vedge(b, zmax)) * KD_LOG2E);
         const unsigned long long w = (1ull << CNT_SHIFT) | (unsigned long long)(uint32_t)fmaf(m, 8388608.f, 0.5f);
         atomicAdd(&S.u.hist[b], w);
+        if (collectK && x >= tau) {
+          const int slot = atomicAdd(&S.fillK, 1);
+          if (slot < CAPK) S.poolK[slot] = cand_key(x, i);
+        }
       },
       [](int64_t, bool) {});
   __syncthreads();
@@ -1101,6 +1109,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
           S.bR[j] = b;
           S.cntAboveR[j] = cc;
           S.massAboveR[j] = cm;
+          S.massR[j] = bm[i];
           S.nR[j] = bc[i];
         }
       cm = nm;
@@ -1108,20 +1117,50 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     }
   }
   __syncthreads();
-  // candidate segments: one per distinct crossing bin; fall back when the
-  // candidates do not fit or a crossing lies in the last (unbounded) bin
-  const int bK = S.bK;
-  const int nKc = S.aboveK + S.nbK;
+  // k_rho from the crossing bin's (count, mass) when that pins it: with
+  // R = rho - (mass above the bin) and the bin's n masses in
+  // [m_lo, m_hi] (its edges) summing to M, the top i of them sum to at most
+  // min(i m_hi, M - (n - i) m_lo) and at least i M / n, so the first i whose
+  // partial sum reaches R lies in [i_lo, i_hi]; equal bounds give it without
+  // looking at the bin's elements.  (1e-6 relative margins cover the
+  // rounding of the fixed-point masses and of the bin edges.)
+  if (tid < n_rho) {
+    const int j = tid;
+    int kr = 0;
+    const int b = S.bR[j], n = S.nR[j];
+    if (b >= 0 && b < NBL - 1 && n > 0) {
+      const double inv_total = 1.0 / (double)total;
+      const double R = (double)rhos[j] - (double)S.massAboveR[j] * inv_total;
+      const double M = (double)S.massR[j] * inv_total;
+      const double eb = (double)vedge(b, zmax) - lse;
+      const double m_hi = exp(eb) * (1.0 + 1e-6), m_lo = exp(eb - (double)BIN_W) * (1.0 - 1e-6);
+      if (R > 0.0 && M > 0.0) {
+        double ilo = ceil(R / m_hi);
+        const double ilo2 = ceil((double)n - (M - R) / m_lo);
+        ilo = fmax(ilo, ilo2);
+        const double ihi = ceil(R * (double)n / (M * (1.0 - 1e-6)));
+        if (ilo == ihi && ilo >= 1.0 && ilo <= (double)n) kr = S.cntAboveR[j] + (int)ilo;
+      }
+    }
+    S.kres[j] = kr;
+  }
+  __syncthreads();
+  // candidate segments of the crossing bins still to rank: one per distinct
+  // bin; fall back when the candidates do not fit or a crossing lies in the
+  // last (unbounded) bin
+  const bool topk_ok = collectK && S.fillK >= K && S.fillK <= CAPK;
+  const int bK = topk_ok ? -1 : S.bK;
+  const int nKc = topk_ok ? S.fillK : S.aboveK + S.nbK;
   int bR[RHO_MAX], seg[RHO_MAX];
   bool own[RHO_MAX];
   int used = 0;
-  bool fail = (bK < 0) || (nKc > CAPK);
+  bool fail = !topk_ok && (S.bK < 0 || nKc > CAPK);
 #pragma unroll
   for (int j = 0; j < RHO_MAX; ++j) {
     bR[j] = -1;
     seg[j] = 0;
     own[j] = false;
-    if (j < n_rho) {
+    if (j < n_rho && S.kres[j] == 0) {
       bR[j] = S.bR[j];
       if (bR[j] < 0 || bR[j] == NBL - 1) fail = true;
       int first = j;
@@ -1137,9 +1176,10 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     if (tid == 0) flags[row] = 1;
     return;
   }
+  const bool needC = bK >= 0 || used > 0;
   if (tid == 0) {
     flags[row] = 0;
-    S.fillK = 0;
+    if (!topk_ok) S.fillK = 0;
 #pragma unroll
     for (int j = 0; j < RHO_MAX; ++j) {
       S.fillR[j] = 0;
@@ -1148,42 +1188,49 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
   }
   __syncthreads();
 
-  // ---- C: collect the candidates (rare: the LDS slot atomics run only for
-  // the lanes holding one)
-  row_loop_pipe<RF>(
-      zr, V, vec,
-      [&](int64_t i, float x, int) {
-        const int b = vbin(x, zmax);
-        // the bins are recomputed exactly as in pass B, so the counts match;
-        // the bounds tests only keep LDS writes inside the pools regardless
-        if (b <= bK) {
-          const int slot = atomicAdd(&S.fillK, 1);
-          if (slot < CAPK) S.poolK[slot] = cand_key(x, i);
-        }
-        int jr = -1;  // the first target with this crossing bin owns its segment
+  if (needC) {
+    // ---- C: collect the candidates still needed (rare: the LDS slot
+    // atomics run only for the lanes holding one)
+    row_loop_pipe<RF>(
+        zr, V, vec,
+        [&](int64_t i, float x, int) {
+          const int b = vbin(x, zmax);
+          // the bins are recomputed exactly as in pass B, so the counts match;
+          // the bounds tests only keep LDS writes inside the pools regardless
+          if (b <= bK) {
+            const int slot = atomicAdd(&S.fillK, 1);
+            if (slot < CAPK) S.poolK[slot] = cand_key(x, i);
+          }
+          int jr = -1;  // the first target with this crossing bin owns its segment
 #pragma unroll
-        for (int j = RHO_MAX - 1; j >= 0; --j) jr = (b == bR[j]) ? j : jr;  // bR[j] = -1 past n_rho
-        if (jr >= 0) {
-          const int slot = S.segR[jr] + atomicAdd(&S.fillR[jr], 1);
-          if (slot < CAPR) S.poolR[slot] = cand_key(x, i);
-        }
-      },
-      [](int64_t, bool) {});
-  __syncthreads();
+          for (int j = RHO_MAX - 1; j >= 0; --j) jr = (b == bR[j]) ? j : jr;  // bR[j] = -1: resolved or unused
+          if (jr >= 0) {
+            const int slot = S.segR[jr] + atomicAdd(&S.fillR[jr], 1);
+            if (slot < CAPR) S.u.c.poolR[slot] = cand_key(x, i);
+          }
+        },
+        [](int64_t, bool) {});
+    __syncthreads();
+  }
 
   fast_emit_topk(S, nKc, K, zr, row, lse, idx_out, val_out, lse_out, mq_out, logp_out);
 
-  // k_rho: masses of the crossing bin's elements in rank order, then the
-  // first rank where the mass from the top reaches rho
+  // k_rho: resolved from the histogram, or the masses of the crossing bin's
+  // elements in rank order, then the first rank where the mass from the top
+  // reaches rho
   const double inv_total = 1.0 / (double)total;
   for (int j = 0; j < n_rho; ++j) {
+    if (S.kres[j] > 0) {
+      if (tid == 0) krho_out[row * n_rho + j] = S.kres[j];
+      continue;
+    }
     const int s0 = S.segR[j], n = S.nR[j];
     for (int p = tid; p < n; p += RF) {
-      const unsigned long long mine = S.poolR[s0 + p];
+      const unsigned long long mine = S.u.c.poolR[s0 + p];
       int r = 0;
 #pragma unroll 8
-      for (int q = 0; q < n; ++q) r += (S.poolR[s0 + q] < mine) ? 1 : 0;
-      S.u.m[r] = exp((double)cand_value(mine) - lse);
+      for (int q = 0; q < n; ++q) r += (S.u.c.poolR[s0 + q] < mine) ? 1 : 0;
+      S.u.c.m[r] = exp((double)cand_value(mine) - lse);
     }
     __syncthreads();
     // thread tid scans ranks [tid*per, tid*per + per) after the masses of
@@ -1191,7 +1238,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     const int per = (n + RF - 1) / RF;
     const int r0 = tid * per, r1 = min(n, r0 + per);
     double own_sum = 0.0;
-    for (int r = r0; r < r1; ++r) own_sum += S.u.m[r];
+    for (int r = r0; r < r1; ++r) own_sum += S.u.c.m[r];
     double x = own_sum;
     const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
@@ -1207,7 +1254,7 @@ __global__ __launch_bounds__(RF) void k_topk_rows(const float* __restrict__ z, i
     int hit = n;
     const double target = (double)S.rho[j];
     for (int r = r0; r < r1; ++r) {
-      base += S.u.m[r];
+      base += S.u.c.m[r];
       if (base >= target) {
         hit = r;
         break;
