@@ -76,18 +76,30 @@ def workload_key(cfg: dict, mode: str) -> str:
     return f"{mode} T={cfg['T']} d={cfg['d']} V={cfg['V']} K={cfg['K']} chunk={cfg['chunk']}"
 
 
+def cache_workload_key() -> str:
+    c = CACHE_CFG
+    return f"cache_build T={c['T']} d={c['d']} V={c['V']} K={c['K']} rho={','.join(str(r) for r in c['rho'])}"
+
+
+def rows_workload_key(n_rho: int) -> str:
+    rho = ",".join(str(r) for r in CACHE_CFG["rho"][:n_rho]) or "none"
+    return f"topk_rows rows=2048 V={CACHE_CFG['V']} K={CACHE_CFG['K']} N(0,1.1) rho={rho}"
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on this workload and on the current sources of that
     kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path)).get(kernel)
+        recs = json.load(open(path)).get("records", [])
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("sources") != kernel_sources_hash(kernel_family(kernel)) or rec.get("workload") != workload:
-        return None
-    return rec.get("bytes_per_launch")
+    src = kernel_sources_hash(kernel_family(kernel))
+    for rec in recs:
+        if rec.get("kernel") == kernel and rec.get("workload") == workload and rec.get("sources") == src:
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def teacher_cache_device(torch, kd, synth, dev, T, V, K, seed, rows=2048):
@@ -233,6 +245,12 @@ def main():
                          "headline workload, for context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device copies of 1 GiB (fp32) for HBM counter calibration")
+    ap.add_argument("--token-block", type=int, default=0,
+                    help="time the token-block option (kd_topk_loss_fwd_bwd_tokblock, this many tokens per block) "
+                         "as the step instead of the vocabulary-chunked call")
+    ap.add_argument("--only", choices=["cache_build", "topk_rows"],
+                    help="only run the teacher-cache build (T=16384, d=4096) or the standalone row pass and print "
+                         "its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); multi-GPU runs are not part of this build",
@@ -256,6 +274,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 4 * n, "copies": 4}), flush=True)
         return
+    if args.only == "cache_build":
+        print(json.dumps(bench_cache_build(torch, kd, synth, dev, steps=max(1, args.steps))), flush=True)
+        return
+    if args.only == "topk_rows":
+        print(json.dumps(bench_topk_rows(torch, kd, dev, steps=max(1, args.steps))), flush=True)
+        return
     cfg = HEAD_CFG
     T, d, V, K, chunk = cfg["T"], cfg["d"], cfg["V"], cfg["K"], cfg["chunk"]
     mode = kd.MODE_BY_NAME[args.mode]
@@ -274,19 +298,20 @@ def main():
                                        token_block=tb)
 
     torch.cuda.reset_peak_memory_stats()
-    step = make_step(mode)
+    step = make_step(mode, tb=args.token_block)
     ms = time_steps(torch, step, args.steps, args.warmup)
     peak_mem = torch.cuda.max_memory_allocated()
     log(f"[bench] {args.mode}: {ms:.3f} ms/step")
     tdv = T * d * V
     credited = credited_flop(kd, mode, T, d, V, K)
-    wl = workload_key(cfg, args.mode)
+    wl = workload_key(cfg, args.mode) + (f" token_block={args.token_block}" if args.token_block else "")
     res = {
         "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"long-context Qwen3-4B-shaped student head, {args.mode} mode", "T": T, "d": d,
-                   "V": V, "K": K, "chunk": chunk, "mode": args.mode, "teacher": TEACHER},
+                   "V": V, "K": K, "chunk": chunk, "mode": args.mode, "teacher": TEACHER,
+                   "path": f"token blocks of {args.token_block}" if args.token_block else "vocabulary-chunked"},
         "mfma_frac_step": credited / (ms * 1e-3) / PEAK_BF16,
         "credited_flop_per_step": credited,
         "peak_mem_bytes": peak_mem,
@@ -562,7 +587,8 @@ def bench_topk_rows(torch, kd, dev, steps=5):
         ms = time_steps(torch, lambda: kd.topk_rows(z, K, rho, workspace=ws), steps, 2)
         alg = T * (4 * V) + T * (12 * K + 8 + 4 * len(rho))
         gbps = alg / (ms * 1e-3) / 1e9
-        res[name] = {"rho": list(rho), "ms_per_call": ms, "algorithmic_GBps": gbps, "hbm_frac": gbps * 1e9 / PEAK_HBM}
+        res[name] = {"rho": list(rho), "ms_per_call": ms, "algorithmic_GBps": gbps, "hbm_frac": gbps * 1e9 / PEAK_HBM,
+                     "algorithmic_bytes": alg, "traffic": measured_traffic("k_topk_rows", rows_workload_key(len(rho)))}
     del z
     torch.cuda.empty_cache()
     return res
@@ -587,6 +613,9 @@ def bench_cache_build(torch, kd, synth, dev, steps=3):
             "gemm_ms": gemm_ms, "gemm_mfma_frac": 2 * T * d * V / (gemm_ms * 1e-3) / PEAK_BF16 if gemm_ms else None,
             "rows_ms": rows_ms, "rows_algorithmic_GBps": rows_bytes / (rows_ms * 1e-3) / 1e9 if rows_ms else None,
             "rows_hbm_frac": rows_bytes / (rows_ms * 1e-3) / PEAK_HBM if rows_ms else None,
+            "rows_algorithmic_bytes_per_launch": rows_bytes // (T // 2048),
+            "rows_traffic": measured_traffic("k_topk_rows", cache_workload_key()),
+            "gemm_traffic": measured_traffic("k_cache_gemm", cache_workload_key()),
             "kernels_ms_per_call": {k: round(v[0], 4) for k, v in prof.items()}}
 
 
