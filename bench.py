@@ -65,10 +65,15 @@ def kernel_family(kernel: str) -> str:
 
 
 def kernel_sources_hash(family: str = "loss") -> str:
+    """Hash of the code a kernel family is built from: comments (the sources
+    use // only) and blank lines do not count."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "top_kd_loss_amd", "csrc")
     for f in KERNEL_SOURCES[family]:
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        for line in open(os.path.join(csrc, f), encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

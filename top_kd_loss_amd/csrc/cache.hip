@@ -9,13 +9,14 @@
 // Losing Accuracy").
 //
 // Row pass, one workgroup per row, in two kernels:
-//   k_topk_rows (fast)  value bins of width 1/128 below the row maximum (the
-//      maximum comes from the GEMM epilogue's per-tile maxima, or from a
-//      first streaming read); one streaming read builds packed
-//      (count, fixed-point mass) bins, whose exact integer prefix sums give
-//      logsumexp, the bin of the K-th largest value and each rho's crossing
-//      bin; a second read collects the elements of those bins, which are
-//      ordered exactly in LDS.  Rows it cannot finish are flagged.
+//   k_topk_rows (fast)  value bins of width 1/256 below the row maximum (the
+//      maximum, and a lower bound of the K-th largest value, come from the
+//      GEMM epilogue's per-tile maxima, or from a first streaming read); one
+//      streaming read builds packed (count, fixed-point mass) bins, whose
+//      exact integer prefix sums give logsumexp and each rho's crossing bin,
+//      and collects the top-K candidates; a crossing bin whose count and mass
+//      do not pin k_rho is collected by a second read and ordered exactly in
+//      LDS.  Rows it cannot finish are flagged.
 //   k_topk_rows_exact  for the flagged rows (or every row when V >= 2^18):
 //      radix digits of order-preserving keys, refined until exact:
 //   1  an 11-bit radix histogram of order-preserving keys with, per bin, the
@@ -757,21 +758,25 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
 
 // ---------------------------------------------------------------------------
 // Fast row pass: one workgroup of RF threads per row, up to three streaming
-// reads of the row.  Without k_rho targets and with a lower bound tau of the
-// K-th largest value (from the partial maxima of A), B and C collapse into
-// one read that sums exp(z - zmax) and collects the elements >= tau.
-//   A  the row maximum zmax;
+// reads of the row (one when the producer's tile maxima are given and every
+// k_rho is pinned by its bin).
+//   A  the row maximum zmax and a lower bound tau of the K-th largest value
+//      (K distinct elements are >= it): from the producer's per-tile maxima,
+//      or from a read of the row and the threads' maxima;
 //   B  a histogram over NBL value bins below zmax, bin b holding the values
-//      with floor(128 (zmax - z)) = b (the last bin also everything lower).
-//      A bin packs its count (bits 46..63) and the sum of
-//      round(2^23 exp(z - e_b)), e_b = zmax - b/128 its upper edge, into one
-//      64-bit word: one LDS atomic per element, integer sums independent of
-//      the atomic order.  The bin masses, rescaled to a common 2^-44 fixed
-//      point relative to exp(zmax), give logsumexp, the bin of the K-th
-//      largest value and, per rho, the bin where the mass accumulated from
-//      the top reaches rho of the total (exact integer prefix sums);
-//   C  collect the elements of the bins down to the K-th one (the top-K
-//      candidates) and those of the crossing bins, then order them in LDS by
+//      with floor(256 (zmax - z)) = b (the last bin also everything lower),
+//      and the elements >= tau (the top-K candidates).  A bin packs its
+//      count (bits 46..63) and the sum of round(2^23 exp(z - e_b)),
+//      e_b = zmax - b/256 its upper edge, into one 64-bit word: one LDS
+//      atomic per element, integer sums independent of the atomic order.
+//      The bin masses, rescaled to a common 2^-44 fixed point relative to
+//      exp(zmax), give logsumexp, the bin of the K-th largest value and, per
+//      rho, the bin where the mass accumulated from the top reaches rho of
+//      the total (exact integer prefix sums).  Without k_rho targets no
+//      histogram is built: the read sums exp(z - zmax) instead;
+//   C  only for what B left open: the elements of a crossing bin whose count
+//      and mass do not pin k_rho (and of the bins down to the K-th one when
+//      the candidates were not collected), ordered in LDS by
 //      (value desc, index asc): the top-K and each k_rho follow exactly.
 // The bin of a value is a monotone function of it, so equal values share a
 // bin and every bin above another holds only larger values.  Rows this path
@@ -815,11 +820,11 @@ struct FastShared {
 static_assert(sizeof(FastShared) <= 80 * 1024, "two rows per CU");
 
 // Value bin of x below the row maximum: monotone non-increasing in x
-// (rounded subtraction, exact scaling by 128); -inf goes to the last bin.
+// (rounded subtraction, exact scaling by 256); -inf goes to the last bin.
 __device__ __forceinline__ int vbin(float x, float zmax) {
   return (int)fminf(fmaxf((zmax - x) * BIN_INVW, 0.f), (float)(NBL - 1));  // in [0, NBL) for any input
 }
-// Upper edge of bin b, rounded once (b / 128 is exact).
+// Upper edge of bin b, rounded once (b / 256 is exact).
 __device__ __forceinline__ float vedge(int b, float zmax) { return fmaf(-(float)b, BIN_W, zmax); }
 
 __device__ __forceinline__ float fast_block_max(float v, FastShared& S) {
