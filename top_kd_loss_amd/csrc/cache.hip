@@ -9,7 +9,7 @@
 // Losing Accuracy").
 //
 // Row pass, one workgroup per row, in two kernels:
-//   k_topk_rows (fast)  value bins of width 1/256 below the row maximum (the
+//   k_topk_rows (fast)  value bins of width 1/512 below the row maximum (the
 //      maximum, and a lower bound of the K-th largest value, come from the
 //      GEMM epilogue's per-tile maxima, or from a first streaming read); one
 //      streaming read builds packed (count, fixed-point mass) bins, whose
@@ -764,10 +764,10 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
 //      (K distinct elements are >= it): from the producer's per-tile maxima,
 //      or from a read of the row and the threads' maxima;
 //   B  a histogram over NBL value bins below zmax, bin b holding the values
-//      with floor(256 (zmax - z)) = b (the last bin also everything lower),
+//      with floor(512 (zmax - z)) = b (the last bin also everything lower),
 //      and the elements >= tau (the top-K candidates).  A bin packs its
 //      count (bits 46..63) and the sum of round(2^23 exp(z - e_b)),
-//      e_b = zmax - b/256 its upper edge, into one 64-bit word: one LDS
+//      e_b = zmax - b/512 its upper edge, into one 64-bit word: one LDS
 //      atomic per element, integer sums independent of the atomic order.
 //      The bin masses, rescaled to a common 2^-44 fixed point relative to
 //      exp(zmax), give logsumexp, the bin of the K-th largest value and, per
@@ -786,8 +786,8 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
 constexpr int RF = 512;                        // threads of the fast row kernel
 constexpr int NBL = 8192;                      // value bins
 constexpr int BPT = NBL / RF;                  // bins per thread in the scans
-constexpr float BIN_INVW = 256.f;              // bins per unit of logit
-constexpr float BIN_W = 1.f / 256.f;
+constexpr float BIN_INVW = 512.f;              // bins per unit of logit (NBL bins cover 16 below the maximum)
+constexpr float BIN_W = 1.f / 512.f;
 constexpr int CAPK = 1536;                     // top-K candidates
 constexpr int CAPR = 2048;                     // crossing-bin candidates, all targets
 constexpr int CNT_SHIFT = 46;
@@ -810,7 +810,7 @@ struct FastShared {
   int red_i[RF / 64];
   unsigned long long total_q;
   float tau;                       // lower bound of the K-th largest value (single-pass collection)
-  int tau_ok;
+  int tau_ok, tau_b;
   int bK, aboveK, nbK, fillK;
   int bR[RHO_MAX], cntAboveR[RHO_MAX], nR[RHO_MAX], fillR[RHO_MAX], segR[RHO_MAX];
   unsigned long long massAboveR[RHO_MAX], massR[RHO_MAX];
@@ -820,11 +820,11 @@ struct FastShared {
 static_assert(sizeof(FastShared) <= 80 * 1024, "two rows per CU");
 
 // Value bin of x below the row maximum: monotone non-increasing in x
-// (rounded subtraction, exact scaling by 256); -inf goes to the last bin.
+// (rounded subtraction, exact scaling by 512); -inf goes to the last bin.
 __device__ __forceinline__ int vbin(float x, float zmax) {
   return (int)fminf(fmaxf((zmax - x) * BIN_INVW, 0.f), (float)(NBL - 1));  // in [0, NBL) for any input
 }
-// Upper edge of bin b, rounded once (b / 256 is exact).
+// Upper edge of bin b, rounded once (b / 512 is exact).
 __device__ __forceinline__ float vedge(int b, float zmax) { return fmaf(-(float)b, BIN_W, zmax); }
 
 __device__ __forceinline__ float fast_block_max(float v, FastShared& S) {
@@ -938,28 +938,121 @@ __device__ __forceinline__ void fast_emit_topk(FastShared& S, int nKc, int K, co
   }
 }
 
-// Lower bound of the K-th largest value of a row from n partial maxima a[]
-// (each the maximum of a disjoint part of the row): the partial maximum of
-// rank K - 1 in (value desc, position asc) order.  K distinct elements of the
-// row are >= it, so it is <= the K-th largest element.  a[] is in LDS;
-// S.tau_ok stays 0 when n < K or no value has that rank (NaN present).
-__device__ __forceinline__ void fast_tau(const float* a, int n, int K, FastShared& S) {
-  if (threadIdx.x == 0) S.tau_ok = 0;
+// Lower bound tau of the K-th largest value of a row from n partial maxima
+// a[] (each the maximum of a disjoint part of the row, so n distinct
+// elements): the maxima are counted in TAU_NB bins of width 1/16 below the
+// row maximum, b is the bin where the count from the top reaches K, and tau
+// is the smallest maximum in bins 0..b.  At least K maxima, hence K distinct
+// elements of the row, are >= tau; it lies at most one bin below the maximum
+// of rank K.  a[] is in LDS (n <= NBL values, the counts after them);
+// S.tau_ok stays 0 when fewer than K of the maxima are numbers.
+constexpr int TAU_NB = 512;
+__device__ __forceinline__ int tau_bin(float x, float zmax) {
+  return (int)fminf(fmaxf((zmax - x) * 16.f, 0.f), (float)(TAU_NB - 1));
+}
+
+// S.tau_b = the first of TAU_NB bins where the count from bin 0 reaches K
+// (-1 when the counts sum to less): wavefront 0 scans, 8 bins per lane.
+__device__ __forceinline__ void tau_crossing(const int* cnt, int K, FastShared& S) {
+  const int tid = threadIdx.x;
+  if (tid >= 64) return;
+  constexpr int PER = TAU_NB / 64;
+  int c[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = cnt[tid * PER + i];
+    sum += c[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (tid >= o) incl += y;
+  }
+  int run = incl - sum;
+  if (run < K && incl >= K) {  // this lane holds the crossing
+    int b = -1;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      run += c[i];
+      if (b < 0 && run >= K) b = tid * PER + i;
+    }
+    S.tau_b = b;
+  }
+}
+
+__device__ __forceinline__ void fast_tau(const float* a, int n, int K, float zmax, FastShared& S) {
+  int* cnt = (int*)(S.u.hist + NBL / 2);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < TAU_NB; i += RF) cnt[i] = 0;
+  if (tid == 0) {
+    S.tau_ok = 0;
+    S.tau_b = -1;
+  }
   __syncthreads();
   if (n >= K)
-    for (int p = threadIdx.x; p < n; p += RF) {
+    for (int p = tid; p < n; p += RF) {
       const float x = a[p];
-      int r = 0;
-      for (int q = 0; q < n; ++q) {
-        const float y = a[q];
-        r += (y > x || (y == x && q < p)) ? 1 : 0;
-      }
-      if (r == K - 1) {
-        S.tau = x;
-        S.tau_ok = 1;
-      }
+      if (x == x) atomicAdd(&cnt[tau_bin(x, zmax)], 1);
     }
   __syncthreads();
+  if (n >= K) tau_crossing(cnt, K, S);
+  __syncthreads();
+  const int b = S.tau_b;
+  float m = KD_INF;
+  if (b >= 0)
+    for (int p = tid; p < n; p += RF) {
+      const float x = a[p];
+      if (x == x && tau_bin(x, zmax) <= b) m = fminf(m, x);
+    }
+  m = -fast_block_max(-m, S);
+  if (b >= 0 && tid == 0) {
+    S.tau = m;
+    S.tau_ok = 1;
+  }
+  __syncthreads();
+}
+
+// Trims the top-K candidate pool (the nKc elements >= tau) to the elements
+// in or above the bin of the K-th largest one, TAU_NB bins spanning
+// [tau, zmax].  The bin is monotone in the value, so the first bin where the
+// count from the top reaches K is that element's bin and the kept ones
+// include every element >= it: about K of them are ranked instead of nKc.
+// Returns the new count (nKc when there is little to trim).
+__device__ __forceinline__ int fast_trim_pool(FastShared& S, int nKc, int K, float zmax, float tau) {
+  const float span = zmax - tau;
+  if (nKc <= K + 32 || !(span > 0.f) || !(span < KD_INF)) return nKc;
+  const float inv = (float)TAU_NB / span;
+  int* cnt = (int*)(S.u.hist + NBL / 2);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < TAU_NB; i += RF) cnt[i] = 0;
+  if (tid == 0) S.tau_b = -1;
+  __syncthreads();
+  constexpr int PT = (CAPK + RF - 1) / RF;
+  unsigned long long c[PT];
+  int bb[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int p = tid + i * RF;
+    c[i] = 0ull;
+    bb[i] = TAU_NB;
+    if (p < nKc) {
+      c[i] = S.poolK[p];
+      bb[i] = (int)fminf(fmaxf((zmax - cand_value(c[i])) * inv, 0.f), (float)(TAU_NB - 1));
+      atomicAdd(&cnt[bb[i]], 1);
+    }
+  }
+  __syncthreads();
+  tau_crossing(cnt, K, S);
+  if (tid == 0) S.fillK = 0;
+  __syncthreads();
+  const int b = S.tau_b;
+  if (b < 0) return nKc;  // cannot happen with nKc >= K numbers; the pool is untouched
+#pragma unroll
+  for (int i = 0; i < PT; ++i)
+    if (bb[i] <= b) S.poolK[atomicAdd(&S.fillK, 1)] = c[i];
+  __syncthreads();
+  return S.fillK;
 }
 
 __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_rows(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
@@ -998,14 +1091,14 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
     float* a = (float*)S.u.hist;
     int n;
     if (tmax != nullptr) {
-      n = n_tmax <= NBL * 2 ? n_tmax : 0;
+      n = n_tmax <= NBL ? n_tmax : 0;
       for (int p = tid; p < n; p += RF) a[p] = tmax[row * n_tmax + p];
     } else {
       n = RF;
       a[tid] = mx;
     }
     __syncthreads();
-    fast_tau(a, n, K, S);
+    fast_tau(a, n, K, zmax, S);
     collectK = S.tau_ok != 0;
     tau = S.tau;
     if (tid == 0) S.fillK = 0;
@@ -1035,7 +1128,8 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
       return;
     }
     if (tid == 0) flags[row] = 0;
-    fast_emit_topk(S, nKc, K, zr, row, (double)zmax + log(total), idx_out, val_out, lse_out, mq_out, logp_out);
+    const int nKt = fast_trim_pool(S, nKc, K, zmax, tau);
+    fast_emit_topk(S, nKt, K, zr, row, (double)zmax + log(total), idx_out, val_out, lse_out, mq_out, logp_out);
     return;
   }
 
@@ -1218,7 +1312,8 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
     __syncthreads();
   }
 
-  fast_emit_topk(S, nKc, K, zr, row, lse, idx_out, val_out, lse_out, mq_out, logp_out);
+  const int nKt = topk_ok ? fast_trim_pool(S, nKc, K, zmax, tau) : nKc;
+  fast_emit_topk(S, nKt, K, zr, row, lse, idx_out, val_out, lse_out, mq_out, logp_out);
 
   // k_rho: resolved from the histogram, or the masses of the crossing bin's
   // elements in rank order, then the first rank where the mass from the top

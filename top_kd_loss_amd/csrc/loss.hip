@@ -85,7 +85,13 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
   __shared__ float val[KMAX];
   __shared__ float zv[KMAX];
   const int lane = threadIdx.x;
-  const int64_t t = blockIdx.x;
+  // Consecutive tokens run on one XCD (workgroups are dealt to the 8 XCDs in
+  // turn; the grid is a multiple of 8), so the cursor starts of neighbouring
+  // tokens, 4 bytes apart in each tile's row, merge into whole lines in that
+  // XCD's L2 instead of being written back as partial lines by 8 of them.
+  const int64_t per = (int64_t)gridDim.x / 8;
+  const int64_t t = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= T) return;
   bool bad = false;
   for (int k = lane; k < Kp2; k += 64) {
     int id = SENT;
@@ -1761,7 +1767,7 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   float2* part = at<float2>(ws, p.o_part);
   const int lds = TC::LDS_BYTES;
 
-  KD_LAUNCH(k_prep, dim3((unsigned)T), dim3(64), 0, s, idx, teacher_logp, given ? st_z : (const float*)nullptr, T, V,
+  KD_LAUNCH(k_prep, dim3((unsigned)(8 * kd_ceil_div(T, 8))), dim3(64), 0, s, idx, teacher_logp, given ? st_z : (const float*)nullptr, T, V,
             (int)K, p.Kp2, p.nVT, p.Tp, sidx, stlp, given ? zS : (float*)nullptr, starts, tok, err);
   KD_LAUNCH_CHECK();
   if (p.TB > 0) {
