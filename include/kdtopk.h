@@ -345,15 +345,21 @@ kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, const float* b
                               int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,
                               float* teacher_logp, void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of device workspace kd_topk_rows needs (4 bytes per row, rounded up
- * to 256; 0 for invalid sizes). */
+/* Bytes of device workspace kd_topk_rows needs (0 for invalid sizes): 4
+ * bytes per row (fallback flags) rounded up to 256, and with k_rho targets
+ * (n_rho > 0, V < 2^18) a record of 240 bytes per row plus 4 KiB per row and
+ * target for the crossing bins whose count and mass do not pin k_rho (those
+ * rows are finished by a second launch that reads them with several
+ * workgroups). */
 size_t kd_topk_rows_workspace(int64_t T, int64_t V, int32_t K, int32_t n_rho);
 
 /* The row pass of the cache build on caller-provided fp32 logits z [T, V]
  * (no NaN) [TG Fig. 3: keep the k largest teacher logits of each row, with
  * the discarded tail mass; SS: the adaptive support k_rho]: same outputs
  * (teacher_logp may be NULL) and ordering rules as kd_topk_cache_build.  On
- * identical fp32 inputs the selected indices and values are exact. */
+ * identical fp32 inputs the selected indices and values are exact.  ws must
+ * be 16-byte aligned and hold kd_topk_rows_workspace(T, V, K, n_rho) bytes
+ * (KD_ENOWS otherwise); its contents need no initialization. */
 kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K,
                        const float* rho_host, int32_t n_rho,
                        int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho,

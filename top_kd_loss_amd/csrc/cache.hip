@@ -49,6 +49,10 @@ namespace {
 
 using CC = PipeCfg<256, 256, 2, 2>;
 constexpr int RT = 1024;      // threads of the row kernel
+// Row flags set by the fast kernel: done, for the exact kernel, crossing
+// bins deferred (collected by k_rows_cross, ranked by the exact kernel's
+// launch).
+constexpr int F_DONE = 0, F_EXACT = 1, F_DEFER = 2;
 constexpr int NB = 2048;      // radix bins per digit (11 bits)
 constexpr int CAP = 4096;     // candidate capacity (LDS)
 constexpr int KMAX = 1024;
@@ -166,6 +170,91 @@ __device__ __forceinline__ uint32_t fkey(float x) {
   uint32_t u = __float_as_uint(x);
   if (u == 0x80000000u) u = 0;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int RF = 512;                        // threads of the fast row kernel
+
+// Deferred crossing bins.  A row whose top-K is settled but whose k_rho for
+// some target is not pinned by its crossing bin's count and mass is handed
+// to k_rows_cross instead of being read again by its own workgroup (which
+// would hold its CU past the other rows): the state below, and up to CAPX
+// elements of the crossing bin per (row, target) in the candidate buffer.
+constexpr int CAPX = 512;   // crossing-bin elements per (row, target)
+constexpr int NSX = 16;     // slices of one deferred row
+constexpr int XL = 4096;    // rows per k_rows_cross launch
+constexpr int XG = 768;     // workgroups of k_rows_cross (three per CU)
+struct CrossRow {
+  double lse;
+  double base[RHO_MAX];     // mass above the crossing bin / total
+  float zmax;
+  int pad;
+  int b[RHO_MAX];           // crossing bin, -1 when resolved
+  int n[RHO_MAX];           // elements in it
+  int above[RHO_MAX];       // elements above it
+  int fill[RHO_MAX];        // elements collected so far
+  float rho[RHO_MAX];
+};
+
+// Sort key: ascending order = value descending, then index ascending.
+__device__ __forceinline__ unsigned long long cand_key(float x, int64_t i) {
+  return ((unsigned long long)(~fkey(x)) << 32) | (unsigned long long)i;
+}
+__device__ __forceinline__ float cand_value(unsigned long long c) {
+  const uint32_t k = ~(uint32_t)(c >> 32);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// k_rho inside a crossing bin: the bin's n candidates (keys, unordered) are
+// ranked by (value desc, index asc), their masses exp(z - lse) stored by rank
+// in m[], and the first rank r where base0 + the masses of ranks 0..r
+// reaches target is returned (n when none).  Thread t of RF adds ranks
+// [t*per, t*per + per) (per = ceil(n / RF)), the thread totals combine in
+// thread order (a wavefront scan, then the wavefronts in order): the sums,
+// hence the result, depend only on the candidates.  Both row kernels use it.
+__device__ __forceinline__ int crossing_rank(const unsigned long long* keys, int n, double lse, double base0,
+                                             double target, double* m, double* red_d, int* red_i) {
+  const int tid = threadIdx.x;
+  const bool act = tid < RF;  // a larger block: its threads past RF only pass the barriers
+  for (int p = tid; act && p < n; p += RF) {
+    const unsigned long long mine = keys[p];
+    int r = 0;
+#pragma unroll 8
+    for (int q = 0; q < n; ++q) r += (keys[q] < mine) ? 1 : 0;
+    m[r] = exp((double)cand_value(mine) - lse);
+  }
+  __syncthreads();
+  const int per = (n + RF - 1) / RF;
+  const int r0 = act ? tid * per : n, r1 = min(n, r0 + per);
+  double own_sum = 0.0;
+  for (int r = r0; r < r1; ++r) own_sum += m[r];
+  double x = own_sum;
+  const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(x, o, 64);
+    if (lane >= o) x += t;
+  }
+  if (act && lane == 63) red_d[w] = x;
+  __syncthreads();
+  double base = base0 + (x - own_sum);
+  for (int i = 0; act && i < w; ++i) base += red_d[i];
+  __syncthreads();
+  int hit = n;
+  for (int r = r0; r < r1; ++r) {
+    base += m[r];
+    if (base >= target) {
+      hit = r;
+      break;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) hit = min(hit, __shfl_xor(hit, o, 64));
+  if (act && lane == 0) red_i[w] = hit;
+  __syncthreads();
+  int h = red_i[0];
+  for (int i = 1; i < RF / 64; ++i) h = min(h, red_i[i]);
+  __syncthreads();
+  return h;
 }
 
 constexpr int RHO_GROUP = 2;  // k_rho targets refined together in one pass
@@ -516,7 +605,7 @@ struct HistRun {
   __device__ __forceinline__ void flush(int*, unsigned long long*) {}
 };
 
-// Exact row pass for the rows the fast pass flagged (flags[row] != 0), or
+// Exact row pass for the rows the fast pass flagged (F_EXACT, F_DEFER_EXACT), or
 // for every row when flags is NULL.
 __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict__ z, int64_t ldz, int64_t V, int K,
                                                         int n_rho, float rho0, float rho1, float rho2, float rho3,
@@ -524,10 +613,38 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
                                                         const int32_t* __restrict__ flags,
                                                         int32_t* __restrict__ idx_out, float* __restrict__ val_out,
                                                         float* __restrict__ lse_out, float* __restrict__ mq_out,
-                                                        int32_t* __restrict__ krho_out, float* __restrict__ logp_out) {
+                                                        int32_t* __restrict__ krho_out, float* __restrict__ logp_out,
+                                                        const CrossRow* __restrict__ cross,
+                                                        const unsigned long long* __restrict__ xcand) {
   __shared__ RowShared S;
   const int64_t row = blockIdx.x;
-  if (flags != nullptr && flags[row] == 0) return;
+  if (flags != nullptr) {
+    const int f = flags[row];
+    if (f == F_DEFER && cross != nullptr) {
+      // the fast kernel's deferred crossing bins: rank each one's elements
+      // (collected by k_rows_cross); a count that does not match the
+      // histogram's falls through to the exact pass of the whole row
+      const CrossRow& c = cross[row];
+      bool ok = true;
+      for (int j = 0; j < n_rho; ++j)
+        if (c.b[j] >= 0 && (c.fill[j] != c.n[j] || c.n[j] > CAPX || c.n[j] < 1)) ok = false;
+      if (ok) {
+        unsigned long long* keys = (unsigned long long*)&S.u;
+        double* mass = (double*)&S.u + CAPX;
+        for (int j = 0; j < n_rho; ++j) {
+          if (c.b[j] < 0) continue;
+          const int n = c.n[j];
+          for (int p = threadIdx.x; p < n; p += RT) keys[p] = xcand[(row * n_rho + j) * CAPX + p];
+          __syncthreads();
+          const int hit = crossing_rank(keys, n, c.lse, c.base[j], (double)c.rho[j], mass, S.red_d, S.scan_i);
+          if (threadIdx.x == 0) krho_out[row * n_rho + j] = c.above[j] + (hit < n ? hit + 1 : n);
+        }
+        return;
+      }
+    } else if (f != F_EXACT) {
+      return;
+    }
+  }
   const float* zr = z + row * ldz;
   const int tid = threadIdx.x;
   const bool vec = ((V & 3) == 0) && ((((uintptr_t)zr) & 15) == 0);
@@ -783,7 +900,6 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
 // cannot finish (non-finite maximum, too many candidates, a crossing in the
 // lowest bin) are flagged for k_topk_rows_exact.
 // ---------------------------------------------------------------------------
-constexpr int RF = 512;                        // threads of the fast row kernel
 constexpr int NBL = 8192;                      // value bins
 constexpr int BPT = NBL / RF;                  // bins per thread in the scans
 constexpr float BIN_INVW = 512.f;              // bins per unit of logit (NBL bins cover 16 below the maximum)
@@ -818,6 +934,7 @@ struct FastShared {
   float rho[RHO_MAX];
 };
 static_assert(sizeof(FastShared) <= 80 * 1024, "two rows per CU");
+
 
 // Value bin of x below the row maximum: monotone non-increasing in x
 // (rounded subtraction, exact scaling by 512); -inf goes to the last bin.
@@ -898,14 +1015,7 @@ __device__ __forceinline__ void fast_excl_scan(unsigned long long m, int c, Fast
   tc = all_c;
 }
 
-// Sort key: ascending order = value descending, then index ascending.
-__device__ __forceinline__ unsigned long long cand_key(float x, int64_t i) {
-  return ((unsigned long long)(~fkey(x)) << 32) | (unsigned long long)i;
-}
-__device__ __forceinline__ float cand_value(unsigned long long c) {
-  const uint32_t k = ~(uint32_t)(c >> 32);
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
+
 
 // Top K of the nKc candidates in S.poolK (every element ranked above a
 // candidate is a candidate): rank by key, write idx / val, and lse and the
@@ -1062,7 +1172,7 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
                                                   int32_t* __restrict__ flags, int32_t* __restrict__ idx_out,
                                                   float* __restrict__ val_out, float* __restrict__ lse_out,
                                                   float* __restrict__ mq_out, int32_t* __restrict__ krho_out,
-                                                  float* __restrict__ logp_out) {
+                                                  float* __restrict__ logp_out, CrossRow* __restrict__ cross) {
   __shared__ FastShared S;
   const int64_t row = blockIdx.x;
   const float* zr = z + row * ldz;
@@ -1079,7 +1189,7 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
   }
   const float zmax = fast_block_max(mx, S);
   if (!(fabsf(zmax) <= 3.4028234663852886e38f)) {  // all -inf, +inf present, or NaN only
-    if (tid == 0) flags[row] = 1;
+    if (tid == 0) flags[row] = F_EXACT;
     return;
   }
   // The top-K candidates are collected during pass B already: every element
@@ -1124,10 +1234,10 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
     const double total = fast_block_sum(acc, S);  // its barriers also complete the pool
     const int nKc = S.fillK;
     if (nKc < K || nKc > CAPK) {
-      if (tid == 0) flags[row] = 1;
+      if (tid == 0) flags[row] = F_EXACT;
       return;
     }
-    if (tid == 0) flags[row] = 0;
+    if (tid == 0) flags[row] = F_DONE;
     const int nKt = fast_trim_pool(S, nKc, K, zmax, tau);
     fast_emit_topk(S, nKt, K, zr, row, (double)zmax + log(total), idx_out, val_out, lse_out, mq_out, logp_out);
     return;
@@ -1270,14 +1380,34 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
       if (own[j]) used += S.nR[j];
     }
   }
-  if (used > CAPR) fail = true;
+  // with the top-K settled, unpinned targets go to k_rows_cross when a state
+  // array is given (each crossing bin holding at most CAPX elements)
+  bool defer = cross != nullptr && topk_ok && used > 0;
+#pragma unroll
+  for (int j = 0; j < RHO_MAX; ++j)
+    if (defer && own[j] && S.nR[j] > CAPX) fail = true;
+  if (!defer && used > CAPR) fail = true;
   if (fail) {
-    if (tid == 0) flags[row] = 1;
+    if (tid == 0) flags[row] = F_EXACT;
     return;
   }
-  const bool needC = bK >= 0 || used > 0;
+  const bool needC = bK >= 0 || (used > 0 && !defer);
+  if (tid == 0 && defer) {
+    CrossRow& c = cross[row];
+    c.lse = lse;
+    c.zmax = zmax;
+#pragma unroll
+    for (int j = 0; j < RHO_MAX; ++j) {
+      c.b[j] = bR[j];
+      c.n[j] = bR[j] >= 0 ? S.nR[j] : 0;
+      c.above[j] = S.cntAboveR[j];
+      c.fill[j] = 0;
+      c.base[j] = (double)S.massAboveR[j] * (1.0 / (double)total);
+      c.rho[j] = rhos[j];
+    }
+  }
   if (tid == 0) {
-    flags[row] = 0;
+    flags[row] = defer ? F_DEFER : F_DONE;
     if (!topk_ok) S.fillK = 0;
 #pragma unroll
     for (int j = 0; j < RHO_MAX; ++j) {
@@ -1324,52 +1454,146 @@ __global__ __launch_bounds__(RF) __attribute__((amdgpu_waves_per_eu(4))) void k_
       if (tid == 0) krho_out[row * n_rho + j] = S.kres[j];
       continue;
     }
+    if (defer) continue;  // k_rows_cross writes it
     const int s0 = S.segR[j], n = S.nR[j];
-    for (int p = tid; p < n; p += RF) {
-      const unsigned long long mine = S.u.c.poolR[s0 + p];
-      int r = 0;
-#pragma unroll 8
-      for (int q = 0; q < n; ++q) r += (S.u.c.poolR[s0 + q] < mine) ? 1 : 0;
-      S.u.c.m[r] = exp((double)cand_value(mine) - lse);
-    }
-    __syncthreads();
-    // thread tid scans ranks [tid*per, tid*per + per) after the masses of
-    // the ranks before them (their thread totals, in thread order)
-    const int per = (n + RF - 1) / RF;
-    const int r0 = tid * per, r1 = min(n, r0 + per);
-    double own_sum = 0.0;
-    for (int r = r0; r < r1; ++r) own_sum += S.u.c.m[r];
-    double x = own_sum;
-    const int lane = tid & 63, w = tid >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double t = __shfl_up(x, o, 64);
-      if (lane >= o) x += t;
-    }
-    if (lane == 63) S.red_d[w] = x;
-    __syncthreads();
-    double base = (double)S.massAboveR[j] * inv_total + (x - own_sum);
-    for (int i = 0; i < w; ++i) base += S.red_d[i];
-    __syncthreads();
-    int hit = n;
-    const double target = (double)S.rho[j];
-    for (int r = r0; r < r1; ++r) {
-      base += S.u.c.m[r];
-      if (base >= target) {
-        hit = r;
-        break;
-      }
-    }
-    hit = fast_block_min(hit, S);
+    const int hit = crossing_rank(S.u.c.poolR + s0, n, lse, (double)S.massAboveR[j] * inv_total, (double)S.rho[j],
+                                  S.u.c.m, S.red_d, S.red_i);
     if (tid == 0) krho_out[row * n_rho + j] = S.cntAboveR[j] + (hit < n ? hit + 1 : n);
     __syncthreads();
   }
 }
 
+// The deferred rows among r0 .. r0 + nr - 1 (nr <= XL) in row order, into
+// list[]; returns their number (the same list in every workgroup: the flags
+// do not change during k_rows_cross).
+__device__ __forceinline__ int deferred_list(const int32_t* flags, int64_t r0, int nr, int* list, int* wcount) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int PT = XL / RF;  // thread t looks at rows PT*t .. PT*t + PT - 1
+  bool dfr[PT];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int r = tid * PT + i;
+    const int f = r < nr ? flags[r0 + r] : F_DONE;
+    dfr[i] = f == F_DEFER;
+    cnt += dfr[i] ? 1 : 0;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wcount[w] = incl;
+  __syncthreads();
+  int off = incl - cnt, total = 0;
+  for (int i = 0; i < RF / 64; ++i) {
+    if (i < w) off += wcount[i];
+    total += wcount[i];
+  }
+#pragma unroll
+  for (int i = 0; i < PT; ++i)
+    if (dfr[i]) list[off++] = tid * PT + i;
+  __syncthreads();
+  return total;
+}
+
+// Deferred crossing bins: the workgroups take (row, slice) items of the
+// deferred rows in turn, read the slice and append the elements of the row's
+// crossing bins (recomputed exactly as in the histogram read) to its
+// buffers.  No workgroup waits for another: the ranking is done by the exact
+// kernel's launch, which follows.
+__global__ __launch_bounds__(RF) void k_rows_cross(const float* __restrict__ z, int64_t ldz, int64_t V, int64_t r0,
+                                                   int nr, int n_rho, const int32_t* __restrict__ flags,
+                                                   CrossRow* __restrict__ cross,
+                                                   unsigned long long* __restrict__ xcand) {
+  __shared__ int list[XL];
+  __shared__ int wcount[RF / 64];
+  __shared__ unsigned long long lbuf[RHO_MAX][CAPX];  // the slice's elements per target, then one global append
+  __shared__ int lfill[RHO_MAX], gbase[RHO_MAX];
+  const int tid = threadIdx.x;
+  const int total = deferred_list(flags, r0, nr, list, wcount);
+  const int64_t per = ((V + NSX - 1) / NSX + 3) & ~(int64_t)3;
+  const bool vec = ((V & 3) == 0) && ((((uintptr_t)z) & 15) == 0) && ((ldz & 3) == 0);
+  for (int it = blockIdx.x; it < total * NSX; it += gridDim.x) {
+    const int rl = list[it / NSX];  // row - r0
+    const int slice = it % NSX;
+    CrossRow* c = cross + rl;
+    const float zmax = c->zmax;
+    int bj[RHO_MAX], blo = NBL, bhi = -1;
+#pragma unroll
+    for (int j = 0; j < RHO_MAX; ++j) {
+      bj[j] = j < n_rho ? c->b[j] : -1;
+      if (bj[j] >= 0) {
+        blo = min(blo, bj[j]);
+        bhi = max(bhi, bj[j]);
+      }
+    }
+    const float* zr = z + (r0 + rl) * ldz;
+    const int64_t s0 = (int64_t)slice * per, s1 = min(V, s0 + per);
+    if (tid < RHO_MAX) lfill[tid] = 0;
+    __syncthreads();
+    auto take = [&](int64_t i, float x) {
+      const int b = vbin(x, zmax);
+      if (b < blo || b > bhi) return;  // nearly every element
+#pragma unroll
+      for (int j = 0; j < RHO_MAX; ++j)
+        if (b == bj[j]) {
+          const int slot = atomicAdd(&lfill[j], 1);
+          if (slot < CAPX) lbuf[j][slot] = cand_key(x, i);
+        }
+    };
+    if (vec) {
+      // 8 loads per thread in flight, then their elements
+      const float4* z4 = (const float4*)zr;
+      const int64_t a4 = s0 / 4, b4 = s1 / 4;
+      for (int64_t base = a4 + tid; base < b4; base += (int64_t)RF * 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i4 = base + (int64_t)u * RF;
+          v[u] = z4[i4 < b4 ? i4 : b4 - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i4 = base + (int64_t)u * RF;
+          if (i4 < b4) {
+            take(4 * i4, v[u].x);
+            take(4 * i4 + 1, v[u].y);
+            take(4 * i4 + 2, v[u].z);
+            take(4 * i4 + 3, v[u].w);
+          }
+        }
+      }
+    } else {
+      for (int64_t i = s0 + tid; i < s1; i += RF) take(i, zr[i]);
+    }
+    __syncthreads();
+    // one global append per target: reserve the range, then copy (a count
+    // past CAPX is kept so that the ranking launch sees the mismatch)
+    if (tid < n_rho && lfill[tid] > 0) gbase[tid] = atomicAdd(&c->fill[tid], lfill[tid]);
+    __syncthreads();
+    for (int j = 0; j < n_rho; ++j) {
+      const int nl = min(lfill[j], CAPX);
+      for (int p = tid; p < nl; p += RF)
+        if (gbase[j] + p < CAPX) xcand[((int64_t)rl * n_rho + j) * CAPX + gbase[j] + p] = lbuf[j][p];
+    }
+    __syncthreads();
+  }
+}
+
+// Workspace of the deferred crossing bins for `rows` rows: the per-row state,
+// then CAPX candidates per (row, target).  None without k_rho targets or
+// when the fast kernel does not run.
+static size_t cross_bytes(int64_t rows, int64_t V, int n_rho) {
+  if (n_rho == 0 || V > VFAST_MAX) return 0;
+  return (size_t)kd_round_up(rows * (int64_t)sizeof(CrossRow), 256) + (size_t)rows * n_rho * CAPX * 8;
+}
+
 struct CachePlan {
   int64_t Tb;
   int nVT;
-  size_t zbytes, o_flags, o_tmax, total;
+  size_t zbytes, o_flags, o_tmax, o_cross, total;
 };
 
 static bool plan_cache(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho, CachePlan& p) {
@@ -1386,7 +1610,8 @@ static bool plan_cache(int64_t T, int64_t d, int64_t V, int32_t K, int32_t n_rho
   p.zbytes = (size_t)tb * V * 4;
   p.o_flags = p.zbytes;
   p.o_tmax = p.o_flags + (size_t)kd_round_up(tb * 4, 256);
-  p.total = p.o_tmax + (size_t)kd_round_up(tb * p.nVT * 4, 256);
+  p.o_cross = p.o_tmax + (size_t)kd_round_up(tb * p.nVT * 4, 256);
+  p.total = p.o_cross + cross_bytes(tb, V, n_rho);
   return true;
 }
 
@@ -1400,18 +1625,29 @@ static kd_status check_rho(const float* rho_host, int32_t n_rho) {
 // Fast pass over all rows, then the exact pass over the rows it flagged
 // (every row when V is beyond the fast pass's packed counts).  `flags` holds
 // `rows` int32; tmax (optional) the rows' maxima in n_tmax parts each.
+// The row pass: the fast kernel, the deferred crossing bins (when `cross`
+// holds cross_bytes(rows, V, n_rho); else the fast kernel reads those rows
+// again itself), and the exact kernel for the flagged rows.
 static void launch_rows(const float* z, int64_t ldz, int64_t rows, int64_t V, int K, const float* rho, int n_rho,
                         int32_t* idx, float* val, float* lse, float* m_q, int32_t* k_rho, float* logp,
-                        int32_t* flags, const float* tmax, int n_tmax, hipStream_t s) {
+                        int32_t* flags, const float* tmax, int n_tmax, void* cross, hipStream_t s) {
   float r[RHO_MAX] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < n_rho; ++j) r[j] = rho[j];
   const bool fast = V <= VFAST_MAX;
+  CrossRow* cr = (fast && n_rho > 0) ? (CrossRow*)cross : nullptr;
+  unsigned long long* xc =
+      cr ? (unsigned long long*)((char*)cross + kd_round_up(rows * (int64_t)sizeof(CrossRow), 256)) : nullptr;
   if (fast)
     KD_LAUNCH(k_topk_rows, dim3((unsigned)rows), dim3(RF), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
-                       r[4], r[5], r[6], r[7], tmax, n_tmax, flags, idx, val, lse, m_q, k_rho, logp);
+                       r[4], r[5], r[6], r[7], tmax, n_tmax, flags, idx, val, lse, m_q, k_rho, logp, cr);
+  for (int64_t r0 = 0; cr && r0 < rows; r0 += XL) {
+    const int nr = (int)(rows - r0 < XL ? rows - r0 : XL);
+    KD_LAUNCH(k_rows_cross, dim3(XG), dim3(RF), 0, s, z, ldz, V, r0, nr, n_rho, flags, cr + r0,
+              xc + r0 * n_rho * CAPX);
+  }
   KD_LAUNCH(k_topk_rows_exact, dim3((unsigned)rows), dim3(RT), 0, s, z, ldz, V, K, n_rho, r[0], r[1], r[2], r[3],
                      r[4], r[5], r[6], r[7], fast ? (const int32_t*)flags : nullptr, idx, val, lse, m_q, k_rho,
-                     logp);
+                     logp, (const CrossRow*)cr, (const unsigned long long*)xc);
 }
 
 }  // namespace
@@ -1449,7 +1685,7 @@ extern "C" kd_status kd_topk_cache_build(const kd_bf16* g, const kd_bf16* U, con
                        (const bf16_t*)U, b, tb, d, V, nTT, nVT, z, tmax);
     launch_rows(z, V, tb, V, K, rho_host, n_rho, idx + t0 * K, val + t0 * K, lse + t0, m_q + t0,
                 n_rho ? k_rho + t0 * n_rho : nullptr, teacher_logp ? teacher_logp + t0 * K : nullptr,
-                (int32_t*)((char*)ws + p.o_flags), tmax, nVT, s);
+                (int32_t*)((char*)ws + p.o_flags), tmax, nVT, (char*)ws + p.o_cross, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
   }
@@ -1490,7 +1726,7 @@ extern "C" kd_status kd_topk_rows_noalloc(const float* z, int64_t T, int64_t V, 
   int32_t* flags = nullptr;
   st = noalloc_scratch(&flags);
   if (st != KD_OK) return st;
-  launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, teacher_logp, flags, nullptr, 0,
+  launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, teacher_logp, flags, nullptr, 0, nullptr,
               (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
@@ -1499,7 +1735,8 @@ extern "C" kd_status kd_topk_rows_noalloc(const float* z, int64_t T, int64_t V, 
 
 extern "C" size_t kd_topk_rows_workspace(int64_t T, int64_t V, int32_t K, int32_t n_rho) {
   if (T < 0 || V <= 0 || K < 1 || K > KMAX || K > V || n_rho < 0 || n_rho > RHO_MAX) return 0;
-  return (size_t)kd_round_up((T > 0 ? T : 1) * 4, 256);  // per-row fallback flags
+  // per-row fallback flags, then the deferred crossing bins
+  return (size_t)kd_round_up((T > 0 ? T : 1) * 4, 256) + cross_bytes(T > 0 ? T : 1, V, n_rho);
 }
 
 extern "C" kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t K, const float* rho_host,
@@ -1511,10 +1748,12 @@ extern "C" kd_status kd_topk_rows(const float* z, int64_t T, int64_t V, int32_t 
   if (st != KD_OK) return st;
   if (T == 0) return KD_OK;
   if (!z || !idx || !val || !lse || !m_q || (n_rho > 0 && !k_rho)) return kd_fail(KD_EINVAL, "null required pointer");
-  const size_t need = (size_t)kd_round_up(T * 4, 256);
+  const size_t o_cross = (size_t)kd_round_up(T * 4, 256);
+  const size_t need = o_cross + cross_bytes(T, V, n_rho);
   if (!ws || ws_bytes < need) return kd_fail(KD_ENOWS, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+  if (!kd_aligned16(ws)) return kd_fail(KD_EINVAL, "ws must be 16-byte aligned");
   launch_rows(z, V, T, V, K, rho_host, n_rho, idx, val, lse, m_q, k_rho, teacher_logp, (int32_t*)ws, nullptr, 0,
-              (hipStream_t)stream);
+              (char*)ws + o_cross, (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return kd_fail(KD_EHIP, "launch failed: %s", hipGetErrorString(e));
   return KD_OK;
