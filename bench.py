@@ -60,8 +60,11 @@ KERNEL_SOURCES = {
 }
 
 
+ROW_KERNELS = ("k_topk_rows", "k_rows_cross", "k_topk_rows_exact")   # the row pass, all its launches
+
+
 def kernel_family(kernel: str) -> str:
-    return "cache" if kernel in ("k_cache_gemm", "k_topk_rows") else "loss"
+    return "cache" if kernel == "k_cache_gemm" or kernel in ROW_KERNELS else "loss"
 
 
 def kernel_sources_hash(family: str = "loss") -> str:
@@ -609,7 +612,7 @@ def bench_cache_build(torch, kd, synth, dev, steps=3):
     ms = time_steps(torch, fn, steps, 1)
     prof = kernel_profile(kd, torch, fn, 1)
     gemm_ms = prof.get("k_cache_gemm", (0.0, 0))[0]
-    rows_ms = prof.get("k_topk_rows", (0.0, 0))[0]
+    rows_ms = sum(prof.get(k, (0.0, 0))[0] for k in ROW_KERNELS)
     rows_bytes = T * (4 * V) + T * (12 * K + 8 + 4 * len(rho))
     del gd, Ud, bd, ws
     torch.cuda.empty_cache()
