@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
                                              const float* __restrict__ zin, int64_t T, int64_t V, int K, int Kp2,
                                              int nVT, int64_t Tp, int32_t* __restrict__ sidx,
                                              float* __restrict__ stlp, float* __restrict__ zout,
-                                             int32_t* __restrict__ starts, float* __restrict__ tok,
+                                             int2* __restrict__ starts, float* __restrict__ tok,
                                              int32_t* __restrict__ err) {
   __shared__ int key[KMAX];
   __shared__ float val[KMAX];
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
   const int lane = threadIdx.x;
   // Consecutive tokens run on one XCD (workgroups are dealt to the 8 XCDs in
   // turn; the grid is a multiple of 8), so the cursor starts of neighbouring
-  // tokens, 4 bytes apart in each tile's row, merge into whole lines in that
+  // tokens, 8 bytes apart in each tile's row, merge into whole lines in that
   // XCD's L2 instead of being written back as partial lines by 8 of them.
   const int64_t per = (int64_t)gridDim.x / 8;
   const int64_t t = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
@@ -150,7 +150,9 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
   double q = 0.0;
   for (int k = lane; k < nv; k += 64) q += exp((double)val[k] - mx);
   q = wave_sum_f64(q);
-  // vocabulary-tile cursor starts: first sorted position with idx >= vt*VT
+  // vocabulary-tile cursor starts: first sorted position with idx >= vt*VT,
+  // and the index there (SENT past the last), so that a tile learns from one
+  // load whether the token has an entry in it
   for (int vt = lane; vt < nVT; vt += 64) {
     int lo = 0, hi = nv;
     const int target = vt * VT;
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
       const int mid = (lo + hi) >> 1;
       if (key[mid] < target) lo = mid + 1; else hi = mid;
     }
-    starts[(int64_t)vt * Tp + t] = lo;
+    starts[(int64_t)vt * Tp + t] = make_int2(lo, lo < nv ? key[lo] : SENT);
   }
   if (lane == 0) {
     tok[t * TOKF + TK_NV] = (float)nv;
@@ -240,14 +242,16 @@ __device__ __forceinline__ void pass1_reduce(const Acc<TC>& acc, const uint32_t 
 // Retained-row mask of token ts inside the tile [m0, m0 + VT): bit r of word
 // r / 32 is row m0 + r.  kc0 receives the sorted position of the first
 // retained index >= m0 (K if none).  Indices are read eight at a time.
-__device__ __forceinline__ void tile_row_mask(const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
+__device__ __forceinline__ void tile_row_mask(const int32_t* __restrict__ sidx, const int2* __restrict__ starts,
                                               int64_t ts, int64_t T, int K, int vt, int64_t Tp, int64_t m0,
                                               uint32_t (&mk)[P1_MASKW], int& kc0) {
 #pragma unroll
   for (int w = 0; w < P1_MASKW; ++w) mk[w] = 0u;
   kc0 = K;
   if (ts >= T) return;
-  kc0 = starts[(int64_t)vt * Tp + ts];
+  const int2 sf = starts[(int64_t)vt * Tp + ts];
+  kc0 = sf.x;
+  if ((int64_t)sf.y - m0 >= VT) return;  // no entry in this tile (most tiles)
   for (int kc = kc0; kc < K; kc += 8) {
     int v[8];
 #pragma unroll
@@ -344,7 +348,7 @@ template <bool MASK, bool STORE = false>
 __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                   int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
                                                   int64_t Tp, const int32_t* __restrict__ sidx,
-                                                  const int32_t* __restrict__ starts, float* __restrict__ zS,
+                                                  const int2* __restrict__ starts, float* __restrict__ zS,
                                                   float2* __restrict__ part, int vt, int tt, bf16_t* lds,
                                                   bf16_t* __restrict__ Eg = nullptr, int64_t ldE = 0) {
   const int64_t m0 = (int64_t)vt * VT, n0 = (int64_t)tt * TT;
@@ -417,7 +421,7 @@ __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const b
 __global__ __launch_bounds__(256, 1) void k_pass1_store(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                         int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
                                                         int64_t Tp, const int32_t* __restrict__ sidx,
-                                                        const int32_t* __restrict__ starts, float* __restrict__ zS,
+                                                        const int2* __restrict__ starts, float* __restrict__ zS,
                                                         float2* __restrict__ part, bf16_t* __restrict__ Eg,
                                                         int64_t ldE) {
   extern __shared__ __align__(16) bf16_t lds[];
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(256, 1) void k_pass1_store(const bf16_t* __restrict
 __global__ __launch_bounds__(256, 1) void k_pass1(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                   int64_t T, int64_t d, int64_t V, int K, int nVT, int nTT,
                                                   int64_t Tp, const int32_t* __restrict__ sidx,
-                                                  const int32_t* __restrict__ starts, float* __restrict__ zS,
+                                                  const int2* __restrict__ starts, float* __restrict__ zS,
                                                   float2* __restrict__ part) {
   extern __shared__ __align__(16) bf16_t lds[];
   int vt, tt;
@@ -743,7 +747,7 @@ template <bool MASK>
 __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                 int64_t T, int64_t d, int64_t V, int K, int64_t Tp, int64_t Cp,
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
-                                                const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
+                                                const int32_t* __restrict__ sidx, const int2* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
                                                 const float* __restrict__ coef, const int32_t* __restrict__ ylab,
                                                 bf16_t* __restrict__ dz, int ct, int tt, bf16_t* lds) {
@@ -770,8 +774,9 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
     }
     int kc = K, vn = SENT;
     if (ts < T) {
-      kc = starts[(int64_t)vt * Tp + ts];
-      vn = kc < K ? sidx[ts * K + kc] : SENT;
+      const int2 sf = starts[(int64_t)vt * Tp + ts];
+      kc = sf.x;
+      vn = sf.y;
     }
     ((int*)park)[(2 * TC::FN) * TC::NT + tid] = kc;
     ((int*)park)[(2 * TC::FN + 1) * TC::NT + tid] = vn;
@@ -833,7 +838,7 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
 __global__ __launch_bounds__(256, 1) void k_zdz(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                 int64_t T, int64_t d, int64_t V, int K, int64_t Tp, int64_t Cp,
                                                 int64_t c0, int64_t c1, int nCT, int nTT,
-                                                const int32_t* __restrict__ sidx, const int32_t* __restrict__ starts,
+                                                const int32_t* __restrict__ sidx, const int2* __restrict__ starts,
                                                 const float* __restrict__ tok, const float* __restrict__ zS,
                                                 const float* __restrict__ coef, const int32_t* __restrict__ ylab,
                                                 bf16_t* __restrict__ dz) {
@@ -1646,7 +1651,7 @@ static bool plan_loss(int64_t T, int64_t d, int64_t V, int32_t K, int32_t mode, 
   p.o_zS = o; o = align_up(o + TK * 4);
   p.o_coef = o; o = align_up(o + TK * 4);
   p.o_tok = o; o = align_up(o + (size_t)p.Tp * TOKF * 4);
-  p.o_starts = o; o = align_up(o + (size_t)p.nVT * p.Tp * 4);
+  p.o_starts = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_part = o; o = align_up(o + (size_t)p.nVT * p.Tp * 8);
   p.o_err = o; o = align_up(o + 4);
   p.o_ylab = 0;
@@ -1763,7 +1768,7 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   float* zS = at<float>(ws, p.o_zS);
   float* coef = at<float>(ws, p.o_coef);
   float* tok = at<float>(ws, p.o_tok);
-  int32_t* starts = at<int32_t>(ws, p.o_starts);
+  int2* starts = at<int2>(ws, p.o_starts);
   float2* part = at<float2>(ws, p.o_part);
   const int lds = TC::LDS_BYTES;
 
