@@ -558,6 +558,15 @@ def bench_llama_k256(torch, kd, synth, dev, steps):
                                                        out=out), steps, 2)
         cr = credited_flop(kd, md, T, d, V, K)
         res[name] = {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "mfma_frac_step": cr / (ms * 1e-3) / PEAK_BF16}
+        if md == kd.RENORM:
+            # the sparse backward against its gathered bytes (2 T K d of W rows, as many of h, plus dW written)
+            prof = kernel_profile(kd, torch, lambda: kd.loss_fwd_bwd(hd, Wd, idx, tlp, mq, mode=md, chunk=chunk,
+                                                                       workspace=ws, out=out), 2)
+            gath = 2 * T * K * d
+            sdh, sdw = prof.get("k_sparse_dh", (0.0, 0))[0], prof.get("k_sparse_dw", (0.0, 0))[0]
+            res[name]["kernels_ms_per_step"] = {k: round(v[0], 4) for k, v in prof.items()}
+            res[name]["sparse_dh_gathered_GBps"] = gath / (sdh * 1e-3) / 1e9 if sdh else None
+            res[name]["sparse_dw_GBps"] = (gath + 4 * V * d) / (sdw * 1e-3) / 1e9 if sdw else None
         del ws
     wsc = torch.empty(kd.lib().kd_topk_cache_build_workspace(T, d, V, Kr, 0), dtype=torch.uint8, device=dev)
     ms_sel = time_steps(torch, lambda: kd.cache_build(hd, Wd, None, Kr, workspace=wsc), steps, 1)
