@@ -125,6 +125,31 @@ def test_misaligned_matrix_rejected_before_launch():
     assert st == 1 and b"16-byte aligned" in L.kd_last_error()
 
 
+def test_row_pass_workspace_holds_flags_and_deferred_crossing_bins():
+    """kd_topk_rows_workspace: 4 bytes per row rounded to 256, and with k_rho
+    targets a 240-byte record per row (rounded to 256) plus 512 eight-byte
+    candidate slots per row and target; rows of V >= 2^18 (the exact
+    kernel only) need the flags alone."""
+    L = kd.lib()
+    r256 = lambda x: (x + 255) // 256 * 256
+    for T, n_rho in ((2048, 0), (2048, 2), (777, 1), (1, 8)):
+        want = r256(T * 4) + (r256(T * 240) + T * n_rho * 512 * 8 if n_rho else 0)
+        assert L.kd_topk_rows_workspace(T, 151936, 256, n_rho) == want, (T, n_rho)
+    assert L.kd_topk_rows_workspace(100, 1 << 18, 16, 2) == r256(100 * 4)
+
+
+def test_row_pass_refuses_small_or_misaligned_workspace_before_launch():
+    L = kd.lib()
+    bufs, (z, idx, val, lse, mq, krho, logp, ws) = _host_ptrs(8)
+    rho = (ctypes.c_float * 2)(0.9, 0.95)
+    need = L.kd_topk_rows_workspace(4, 1000, 8, 2)
+    st = L.kd_topk_rows(z, 4, 1000, 8, rho, 2, idx, val, lse, mq, krho, logp, ws, need - 1, None)
+    assert st == 3 and b"workspace too small" in L.kd_last_error()
+    ws_off = ctypes.c_void_p(ws.value + 8)
+    st = L.kd_topk_rows(z, 4, 1000, 8, rho, 2, idx, val, lse, mq, krho, logp, ws_off, need, None)
+    assert st == 1 and b"16-byte aligned" in L.kd_last_error()
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     """No CPU fallback: without the built library every call raises."""
     monkeypatch.setattr(kd, "_lib", None)
