@@ -393,25 +393,38 @@ def main():
 
 def gemm_reference(torch, dev, cfg, steps=5):
     """The vendor bf16 GEMM (torch.mm, hipBLASLt on ROCm; fp32 accumulation,
-    bf16 output) on the LM-head GEMM shapes of one 8192-token block of the
-    headline workload: logits h W^T (pass 1 and its recompute), dW = dz^T h
-    and dh = dz W, with contiguous operands.  Context for the library's own
-    kernels, which carry the loss epilogues as well."""
-    T, d, V = 8192, cfg["d"], cfg["V"]
+    bf16 output) on the library's GEMM shapes with the library's operand
+    layouts: the logits of all T tokens from h [T, d] and W [V, d] (both
+    k-contiguous, as pass 1 and its recompute read them), dW = dz^T h and
+    dh = dz W of one 8192-row vocabulary chunk, and the teacher-cache block
+    U g (2048 tokens, d = 4096).  Context for the library's own kernels,
+    which carry the loss epilogues as well."""
+    T, d, V = cfg["T"], cfg["d"], cfg["V"]
+    C = cfg["chunk"]
     g = torch.Generator(device=dev)
     g.manual_seed(11)
     h = torch.randn((T, d), device=dev, generator=g).to(torch.bfloat16)
-    Wt = (torch.randn((d, V), device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)   # W^T
-    dz = (torch.randn((T, V), device=dev, generator=g) * 1e-5).to(torch.bfloat16)
-    dzt = dz.t().contiguous()
-    W = Wt.t().contiguous()
+    W = (torch.randn((V, d), device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+    dz = (torch.randn((T, C), device=dev, generator=g) * 1e-5).to(torch.bfloat16)
+    Wc = W[:C].contiguous()
     out = {}
-    for name, a, b in (("logits h W^T", h, Wt), ("dW = dz^T h", dzt, h), ("dh = dz W", dz, W)):
-        ms = time_steps(torch, lambda: torch.mm(a, b), steps, 2)
-        fl = 2.0 * a.shape[0] * a.shape[1] * b.shape[1]
-        out[name] = {"M": a.shape[0], "N": b.shape[1], "K": a.shape[1], "ms": ms,
-                     "TFLOP_s": fl / (ms * 1e-3) / 1e12, "frac_of_2.5PF": fl / (ms * 1e-3) / PEAK_BF16}
-    del h, Wt, dz, dzt, W
+
+    def timed(name, fn, M, N, K):
+        ms = time_steps(torch, fn, steps, 2)
+        fl = 2.0 * M * N * K
+        out[name] = {"M": M, "N": N, "K": K, "ms": ms, "TFLOP_s": fl / (ms * 1e-3) / 1e12,
+                     "frac_of_2.5PF": fl / (ms * 1e-3) / PEAK_BF16}
+
+    timed("logits h W^T", lambda: torch.mm(h, W.t()), T, V, d)
+    timed("dW = dz^T h (one chunk)", lambda: torch.mm(dz.t(), h), C, d, T)
+    timed("dh = dz W (one chunk)", lambda: torch.mm(dz, Wc), T, d, C)
+    del h, W, dz, Wc
+    torch.cuda.empty_cache()
+    c = CACHE_CFG
+    gt = torch.randn((2048, c["d"]), device=dev, generator=g).to(torch.bfloat16)
+    U = (torch.randn((c["V"], c["d"]), device=dev, generator=g) / c["d"] ** 0.5).to(torch.bfloat16)
+    timed("teacher-cache block U g", lambda: torch.mm(gt, U.t()), 2048, c["V"], c["d"])
+    del gt, U
     torch.cuda.empty_cache()
     return out
 
