@@ -3,7 +3,9 @@
 // A workgroup of WM x WN wavefronts computes a BM x BN tile; each wavefront
 // owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks
 // (v_mfma_f32_32x32x16_bf16) with fp32 accumulators in registers.  Operand
-// tiles are staged through LDS in BK = 32 slices.
+// tiles are staged through LDS in BK = 32 slices (gemm_tile_pipe, either
+// layout) or, for 256 x 256 tiles with both operands K-major, in BK = 64
+// slices (gemm_tile_kpipe, at the end of this file).
 //
 // Each operand is stored in global memory in one of two layouts:
 //   K-major  (MN = false): element (r, k) at P[r * ld + k]; the tile's rows
@@ -331,4 +333,180 @@ __device__ __forceinline__ void gemm_tile_pipe(const bf16_t* __restrict__ A, int
     pipe_iter<C, AT, BT, 1>(P, kt + 1, nk, acc);
   }
   if (kt < nk) pipe_iter<C, AT, BT, 0>(P, kt, nk, acc);
+}
+
+// ---------------------------------------------------------------------------
+// K-major pipeline: BK = 64 slices in two LDS stages, for 256 x 256 tiles of
+// four 128 x 128 wavefronts whose operands are both K-major.  Each slice
+// feeds four 16-deep substeps of 16 MFMAs; the global loads of slice kt+2
+// and the LDS stores of slice kt+1 hide behind them, so the workgroup meets
+// one barrier per 64 of K instead of per 32.  Same MFMA, accumulator layout
+// and order of the 16-deep k-chunks as gemm_tile_pipe, so C is bitwise the
+// same.
+//   iteration kt (stage kt%2 holds slice kt, complete since the last barrier):
+//     region 0: MFMAs of substep 3 of slice kt-1 | fragments of substep 0 |
+//               A loads of slice kt+2 into register set kt%2
+//     region 1: MFMAs of substep 0 | fragments of substep 1 | B loads of
+//               slice kt+2 | stores of slice kt+1 (register set (kt+1)%2)
+//               into stage (kt+1)%2, first 6 chunks
+//     region 2: MFMAs of substep 1 | fragments of substep 2 | 5 more chunks
+//     region 3: MFMAs of substep 2 | last 5 chunks | fragments of substep 3
+//     s_waitcnt lgkmcnt(0); s_barrier
+// Stage (kt+1)%2 held slice kt-1, whose last fragment reads (region 3 of the
+// previous iteration) completed before that barrier.
+// ---------------------------------------------------------------------------
+constexpr int KP_BK = 64;
+constexpr int KP_STAGE = 2 * 256 * KP_BK;                    // A and B elements of one slice
+constexpr int KPIPE_LDS = 2 * KP_STAGE * (int)sizeof(bf16_t);  // 128 KB
+
+// 128-byte K-major LDS rows: chunk c of row r at c ^ kpswz(r).  Rows 2j and
+// 2j+1 share a 256-byte bank span; (r >> 1) & 7 spreads the same chunk of 16
+// consecutive rows over the 16 sixteen-byte bank slots.
+__device__ __forceinline__ int kpswz(int r) { return (r >> 1) & 7; }
+
+struct KPipeOperand {
+  static constexpr int CPR = KP_BK / 8;  // 16-byte chunks per row slice
+  static constexpr int RSTEP = 256 / CPR;  // rows between a thread's chunks
+  static constexpr int LDN = 256 / RSTEP;  // chunks per thread per slice
+  static_assert(RSTEP % 16 == 0, "rows rr + i*RSTEP share rr's swizzle");
+  const char* base;
+  uint32_t off[LDN];
+  bf16_t* st;
+  const bf16_t* rd[4];  // fragment 0 of each k-substep (stage 0)
+
+  __device__ __forceinline__ void init(const bf16_t* P, int64_t ld, int64_t r0, int64_t r_end, bf16_t* lds_op,
+                                       int w, int lane) {
+    const int tid = threadIdx.x;
+    base = (const char*)(P + r0 * ld);
+    const int rr = tid / CPR, c = tid % CPR;
+    const int nrows = (int)(r_end - r0);
+#pragma unroll
+    for (int i = 0; i < LDN; ++i) {
+      const int r = rr + i * RSTEP;
+      off[i] = (uint32_t)(((r < nrows ? r : nrows - 1) * (int)ld + c * 8) * 2);
+    }
+    st = lds_op + rr * KP_BK + ((c ^ kpswz(rr)) << 3);
+    // fragment rows differ from l32 by multiples of 32: same swizzle
+    const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) rd[ks] = lds_op + (w * 128 + l32) * KP_BK + (((ks * 2 + kh) ^ kpswz(l32)) << 3);
+  }
+  __device__ __forceinline__ void gload(u32x4* r, int slice) const {
+    const uint32_t kb = (uint32_t)(slice * KP_BK * 2);
+#pragma unroll
+    for (int i = 0; i < LDN; ++i) r[i] = *(const u32x4*)(base + (off[i] + kb));
+  }
+  template <int I0, int I1>
+  __device__ __forceinline__ void lstore(const u32x4* r, int stage) const {
+#pragma unroll
+    for (int i = I0; i < I1; ++i) *(u32x4*)(st + stage * KP_STAGE + i * RSTEP * KP_BK) = r[i];
+  }
+  __device__ __forceinline__ bf16x8 fread(int f, int stage, int ks) const {
+    return *(const bf16x8*)(rd[ks] + stage * KP_STAGE + f * 32 * KP_BK);
+  }
+};
+
+struct KPipeState {
+  KPipeOperand a, b;
+  u32x4 ra[2][KPipeOperand::LDN], rb[2][KPipeOperand::LDN];
+  bf16x8 fa[2][4], fb[2][4];
+};
+
+template <int BUF>
+__device__ __forceinline__ void kp_fread(KPipeState& P, int stage, int ks) {
+  P.fa[BUF][0] = P.a.fread(0, stage, ks);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) P.fb[BUF][j] = P.b.fread(j, stage, ks);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) P.fa[BUF][i] = P.a.fread(i, stage, ks);
+}
+
+template <class C, int BUF>
+__device__ __forceinline__ void kp_mfma(KPipeState& P, Acc<C>& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc.v[i][j] = mfma32x32x16(P.fa[BUF][i], P.fb[BUF][j], acc.v[i][j]);
+}
+
+// 16 MFMAs with NR fragment reads, NL global loads and NS LDS stores spread
+// among them.
+template <int NR, int NL, int NS>
+__device__ __forceinline__ void kp_schedule() {
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (m < NS) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if (m < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
+template <class C, int SET, bool FIRST>
+__device__ __forceinline__ void kp_iter(KPipeState& P, int kt, int nk, Acc<C>& acc) {
+  const int s = kt & 1, sn = s ^ 1;
+  const int ld = kt + 2 < nk ? kt + 2 : nk - 1;
+  // region 0
+  if constexpr (!FIRST) kp_mfma<C, 1>(P, acc);
+  kp_fread<0>(P, s, 0);
+  P.a.gload(P.ra[SET], ld);
+  if constexpr (!FIRST) kp_schedule<8, 8, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  // region 1
+  kp_mfma<C, 0>(P, acc);
+  kp_fread<1>(P, s, 1);
+  P.b.gload(P.rb[SET], ld);
+  P.a.lstore<0, 6>(P.ra[SET ^ 1], sn);
+  kp_schedule<8, 8, 6>();
+  __builtin_amdgcn_sched_barrier(0);
+  // region 2
+  kp_mfma<C, 1>(P, acc);
+  kp_fread<0>(P, s, 2);
+  P.a.lstore<6, 8>(P.ra[SET ^ 1], sn);
+  P.b.lstore<0, 3>(P.rb[SET ^ 1], sn);
+  kp_schedule<8, 0, 5>();
+  __builtin_amdgcn_sched_barrier(0);
+  // region 3
+  kp_mfma<C, 0>(P, acc);
+  P.b.lstore<3, 8>(P.rb[SET ^ 1], sn);
+  kp_fread<1>(P, s, 3);
+  kp_schedule<8, 0, 5>();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 256 x 256 tile over K (a multiple of 64), both operands K-major, rows
+// clamped as in gemm_tile_pipe.  `lds` holds KPIPE_LDS bytes.
+template <class C>
+__device__ __forceinline__ void gemm_tile_kpipe(const bf16_t* __restrict__ A, int64_t lda, int64_t m0, int64_t m_end,
+                                                const bf16_t* __restrict__ B, int64_t ldb, int64_t n0, int64_t n_end,
+                                                int K, bf16_t* lds, Acc<C>& acc) {
+  static_assert(C::BM == 256 && C::BN == 256 && C::WM == 2 && C::WN == 2, "256 x 256 tile of 128 x 128 wavefronts");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc.v[i][j] = f32x16{};
+  KPipeState P;
+  P.a.init(A, lda, m0, m_end, lds, wm, lane);
+  P.b.init(B, ldb, n0, n_end, lds + 256 * KP_BK, wn, lane);
+  const int nk = K / KP_BK;
+  // slice 0 into stage 0, slice 1 into register set 1
+  P.a.gload(P.ra[0], 0);
+  P.b.gload(P.rb[0], 0);
+  P.a.gload(P.ra[1], 1 < nk ? 1 : nk - 1);
+  P.b.gload(P.rb[1], 1 < nk ? 1 : nk - 1);
+  P.a.lstore<0, KPipeOperand::LDN>(P.ra[0], 0);
+  P.b.lstore<0, KPipeOperand::LDN>(P.rb[0], 0);
+  __syncthreads();
+  kp_iter<C, 0, true>(P, 0, nk, acc);
+  int kt = 1;
+  for (; kt + 1 < nk; kt += 2) {
+    kp_iter<C, 1, false>(P, kt, nk, acc);
+    kp_iter<C, 0, false>(P, kt + 1, nk, acc);
+  }
+  if (kt < nk) kp_iter<C, 1, false>(P, kt, nk, acc);
+  kp_mfma<C, 1>(P, acc);  // substep 3 of the last slice
 }
