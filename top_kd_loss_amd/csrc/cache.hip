@@ -47,7 +47,7 @@ static __device__ __align__(256) int32_t scratch[KD_NOALLOC_ROWS];
 
 namespace {
 
-using CC = PipeCfg<256, 256, 2, 2>;
+using CC = GemmCfg;
 constexpr int RT = 1024;      // threads of the row kernel
 // Row flags set by the fast kernel: done, for the exact kernel, crossing
 // bins deferred (collected by k_rows_cross, ranked by the exact kernel's
@@ -80,7 +80,7 @@ __device__ __forceinline__ bool tile_of(int bid, int nblocks, int nM, int nN, in
 // bias added: 1 KB of contiguous z per wavefront store.  The maximum of each
 // token row of the tile goes to tmax[t][vt] (the row pass starts from it).
 constexpr int CG_LDS = (CC::BN / 2) * CC::BM * 4;  // 128 tokens x 256 vocabulary fp32
-static_assert(CG_LDS >= KPIPE_LDS, "epilogue staging reuses the operand stages");
+static_assert(CG_LDS >= GEMM_LDS, "epilogue staging reuses the operand stages");
 
 __device__ __forceinline__ int cg_swz(int tl) { return (tl & 31) << 1; }
 
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256, 1) void k_cache_gemm(const bf16_t* __restrict_
   if (!tile_of(blockIdx.x, gridDim.x, nVT, nTT, 4, vt, tt)) return;
   const int64_t m0 = (int64_t)vt * CC::BM, n0 = (int64_t)tt * CC::BN;
   Acc<CC> acc;
-  gemm_tile_kpipe<CC>(U, d, m0, V, g, d, n0, Tb, (int)d, lds, acc);
+  gemm_tile_pipe<CC>(U, d, m0, V, g, d, n0, Tb, (int)d, lds, acc);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / CC::WN, wn = wave % CC::WN;
   float* E = (float*)lds;

@@ -31,7 +31,7 @@
 
 namespace {
 
-using TC = PipeCfg<256, 256, 2, 2>;
+using TC = GemmCfg;
 constexpr int VT = TC::BM;        // vocabulary rows per tile (M of the z^T tile)
 constexpr int TT = TC::BN;        // tokens per tile
 constexpr int KMAX = 1024;
@@ -186,8 +186,8 @@ __global__ __launch_bounds__(64) void k_prep(const int32_t* __restrict__ idx, co
 constexpr int P1_RED = TC::WM * TT * 2 * 4;           // (max, sum) per wavefront row and token
 constexpr int P1_MASKW = VT / 32;                     // mask words per token
 constexpr int P1_PARK = (P1_MASKW + 1) * TC::NT * 4;  // masks + first positions
-constexpr int P1_LDS = KPIPE_LDS + P1_PARK;
-static_assert(P1_RED <= KPIPE_LDS, "pass-1 reduction space");
+constexpr int P1_LDS = GEMM_LDS + P1_PARK;
+static_assert(P1_RED <= GEMM_LDS, "pass-1 reduction space");
 
 // Tile rows at or past vlim (the vocabulary's end) are set to -inf in the
 // accumulators, so the epilogues below need no per-element row test: they
@@ -355,7 +355,7 @@ __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const b
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   const int tid = threadIdx.x;
-  uint32_t* park = (uint32_t*)((char*)lds + KPIPE_LDS);
+  uint32_t* park = (uint32_t*)((char*)lds + GEMM_LDS);
   {
     uint32_t mk[P1_MASKW];
     int kc0;
@@ -366,7 +366,7 @@ __device__ __forceinline__ void pass1_tile(const bf16_t* __restrict__ W, const b
   }
 
   Acc<TC> acc;
-  gemm_tile_kpipe<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
+  gemm_tile_pipe<TC>(W, d, m0, V, h, d, n0, T, (int)d, lds, acc);
   __syncthreads();  // every wavefront is done with the operand stages (and the masks are parked)
 
   if (MASK) mask_rows(acc, (int)(V - m0), wm, lane);
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(1024) void k_loss_sum(int64_t T, float scale, const
 // ---------------------------------------------------------------------------
 constexpr int ZDZ_PARK = (2 * TC::FN + 2) * TC::NT * 4;
 // the 128 KB bf16 tile, or the operand stages and the parked values
-constexpr int ZDZ_LDS = VT * TT * 2 > KPIPE_LDS + ZDZ_PARK ? VT * TT * 2 : KPIPE_LDS + ZDZ_PARK;
+constexpr int ZDZ_LDS = VT * TT * 2 > GEMM_LDS + ZDZ_PARK ? VT * TT * 2 : GEMM_LDS + ZDZ_PARK;
 
 // Bijection on 0..31: 32 consecutive rows hit 32 distinct chunk positions
 // (conflict-free stores), 4 consecutive rows fall into different aligned
@@ -765,7 +765,7 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
   const int64_t ts = n0 + tid;
   const int64_t vend = (m0 + VT < c1) ? m0 + VT : c1;
   {
-    float* park = (float*)((char*)lds + KPIPE_LDS);
+    float* park = (float*)((char*)lds + GEMM_LDS);
 #pragma unroll
     for (int fn = 0; fn < TC::FN; ++fn) {
       const int64_t t = n0 + acc_col<TC>(wn, fn, lane);
@@ -784,12 +784,12 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
   }
 
   Acc<TC> acc;
-  gemm_tile_kpipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
+  gemm_tile_pipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
   __syncthreads();  // every wavefront is done with the operand stages
   float lse_t[TC::FN], al_t[TC::FN];
   int kcur, vnext;
   {
-    const float* park = (const float*)((const char*)lds + KPIPE_LDS);
+    const float* park = (const float*)((const char*)lds + GEMM_LDS);
 #pragma unroll
     for (int fn = 0; fn < TC::FN; ++fn) {
       lse_t[fn] = park[(2 * fn) * TC::NT + tid];
@@ -982,7 +982,7 @@ __global__ __launch_bounds__(256, 1) void k_dhdw(const bf16_t* __restrict__ dz, 
 // dh / dW GEMMs of the dense path.
 // ---------------------------------------------------------------------------
 constexpr int LP_RED = TC::WM * TT * 3 * 4;  // (m, s, u) per wavefront row and token
-static_assert(LP_RED + VT * 4 <= KPIPE_LDS, "lse-pass reduction space");
+static_assert(LP_RED + VT * 4 <= GEMM_LDS, "lse-pass reduction space");
 
 // Rows of the tile's accumulators get the bias of their vocabulary row
 // (bl: the tile's VT biases in LDS).
@@ -1008,7 +1008,7 @@ __device__ __forceinline__ void lse_tile(const bf16_t* __restrict__ A, const bf1
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   Acc<TC> acc;
-  gemm_tile_kpipe<TC>(A, K, m0, V, B, K, n0, T, (int)K, lds, acc);
+  gemm_tile_pipe<TC>(A, K, m0, V, B, K, n0, T, (int)K, lds, acc);
   __syncthreads();  // every wavefront is done with the operand stages
   float* red = (float*)lds;
   if (TEACHER) {
@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(256, 1) void k_teacher_q(const bf16_t* __restrict__
   if (!tile_of(blockIdx.x, gridDim.x, nCT, nTT, 4, ct, tt)) return;
   const int64_t m0 = c0 + (int64_t)ct * VT, n0 = (int64_t)tt * TT;
   Acc<TC> acc;
-  gemm_tile_kpipe<TC>(U, dt, m0, c1, g, dt, n0, T, (int)dt, lds, acc);
+  gemm_tile_pipe<TC>(U, dt, m0, c1, g, dt, n0, T, (int)dt, lds, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   const int64_t rbase = m0 + wm * TC::TM + 4 * (lane >> 5);
@@ -1242,7 +1242,7 @@ __device__ __forceinline__ void zdz_kl_tile(const bf16_t* __restrict__ W, const 
   const int wm = wave / TC::WN, wn = wave % TC::WN;
   const int64_t tile = (int64_t)tt * nCT + ct;
   Acc<TC> acc;
-  gemm_tile_kpipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
+  gemm_tile_pipe<TC>(W, d, m0, c1, h, d, n0, T, (int)d, lds, acc);
   if (MASK) mask_rows(acc, (int)(c1 - m0), wm, lane);
   // Per-token constants and the q of the first token column are loaded before
   // the barrier; each column's loop then loads the next column's q.
@@ -1771,7 +1771,6 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
   float* tok = at<float>(ws, p.o_tok);
   int2* starts = at<int2>(ws, p.o_starts);
   float2* part = at<float2>(ws, p.o_part);
-  const int lds = TC::LDS_BYTES;
 
   KD_LAUNCH(k_prep, dim3((unsigned)(8 * kd_ceil_div(T, 8))), dim3(64), 0, s, idx, teacher_logp, given ? st_z : (const float*)nullptr, T, V,
             (int)K, p.Kp2, p.nVT, p.Tp, sidx, stlp, given ? zS : (float*)nullptr, starts, tok, err);
@@ -1812,7 +1811,7 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
       const int gdh = grid_of(nTTb * nDT);
       const int nCTw = (int)kd_ceil_div(V, TC::BN);
       const int gdw = grid_of(nCTw * nDT);
-      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, (const bf16_t*)E, (const bf16_t*)W,
+      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), GEMM_LDS, s, (const bf16_t*)E, (const bf16_t*)W,
                 (const bf16_t*)h + t0 * d, tb, d, rows, p.Vp, (int64_t)0, V, kdh, 1, nTTb, nDT, nCTw, gdh,
                 rows > kdh ? 1 : 0, t0 > 0 ? 1 : 0, dh + t0 * d, dW);
       KD_LAUNCH_CHECK();
@@ -1857,7 +1856,7 @@ static kd_status loss_impl(const kd_bf16* h, const kd_bf16* W, const int32_t* id
       const int gdh = grid_of(p.nTT * p.nDT);
       const int nCTw = (int)kd_ceil_div(clen, TC::BN);
       const int gdw = grid_of(nCTw * p.nDT);
-      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), lds, s, dz, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0, clen,
+      KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), GEMM_LDS, s, dz, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0, clen,
                          kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh, p.Tp > kdh ? 1 : 0, 0, dh, dW);
       KD_LAUNCH_CHECK();
     }
@@ -2054,10 +2053,10 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     g = (const kd_bf16*)gb;
   }
   const int g1 = grid_of(p.nVT * p.nTT);
-  KD_LAUNCH(k_lse_pass<false>, dim3(g1), dim3(TC::NT), KPIPE_LDS, s, (const bf16_t*)W, (const bf16_t*)h, d, T, V,
+  KD_LAUNCH(k_lse_pass<false>, dim3(g1), dim3(TC::NT), GEMM_LDS, s, (const bf16_t*)W, (const bf16_t*)h, d, T, V,
                      (const float*)nullptr, (const float*)nullptr, p.nVT, p.nTT, p.Tp, part, (float4*)nullptr);
   if (teacher_lse == nullptr)
-    KD_LAUNCH(k_lse_pass<true>, dim3(g1), dim3(TC::NT), KPIPE_LDS, s, (const bf16_t*)U, (const bf16_t*)g, dt, T,
+    KD_LAUNCH(k_lse_pass<true>, dim3(g1), dim3(TC::NT), GEMM_LDS, s, (const bf16_t*)U, (const bf16_t*)g, dt, T,
               V, b, gscale, p.nVT, p.nTT, p.Tp, (float2*)nullptr, partT);
   KD_LAUNCH_CHECK();
   KD_LAUNCH(k_kl_combine, dim3((unsigned)kd_ceil_div(T, 4)), dim3(256), 0, s, T, p.nVT, p.Tp, scale, part,
@@ -2069,7 +2068,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     const int64_t clen = c1 - c0;
     const int nCT = (int)kd_ceil_div(clen, VT);
     const int gz = grid_of(nCT * p.nTT);
-    KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), KPIPE_LDS, s, (const bf16_t*)U, (const bf16_t*)g, b, gscale, T,
+    KD_LAUNCH(k_teacher_q, dim3(gz), dim3(TC::NT), GEMM_LDS, s, (const bf16_t*)U, (const bf16_t*)g, b, gscale, T,
                        dt, c0, c1, nCT, p.nTT, p.Tp, (const float*)tok, qbuf, partH);
     KD_LAUNCH(k_zdz_kl, dim3(gz), dim3(TC::NT), ZK_LDS, s, (const bf16_t*)W, (const bf16_t*)h, T, d, p.Tp, p.Cp, c0,
                        c1, nCT, p.nTT, (const float*)tok, (const f32x4*)qbuf, partQZ, dz);
@@ -2078,7 +2077,7 @@ static kd_status kl_impl(const kd_bf16* h, const kd_bf16* W, const kd_bf16* g, c
     const int gdh = grid_of(p.nTT * p.nDT);
     const int nCTw = (int)kd_ceil_div(clen, TC::BN);
     const int gdw = grid_of(nCTw * p.nDT);
-    KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), TC::LDS_BYTES, s, (const bf16_t*)dz, (const bf16_t*)W,
+    KD_LAUNCH(k_dhdw, dim3(gdh + gdw), dim3(TC::NT), GEMM_LDS, s, (const bf16_t*)dz, (const bf16_t*)W,
                        (const bf16_t*)h, T, d, p.Tp, p.Cp, c0, clen, kdh, c == 0 ? 1 : 0, p.nTT, p.nDT, nCTw, gdh,
                        p.Tp > kdh ? 1 : 0, 0, dh, dW);
     KD_LAUNCH_CHECK();
