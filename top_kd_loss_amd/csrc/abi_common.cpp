@@ -35,18 +35,28 @@ bool kd_prof_active() { return g_prof_on; }
 void kd_prof_record(const char* name, hipStream_t stream, bool begin) {
   if (begin) {
     ProfRec r{name, nullptr, nullptr};
-    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
-    hipEventRecord(r.a, stream);
+    if (hipEventCreate(&r.a) != hipSuccess) return;
+    if (hipEventCreate(&r.b) != hipSuccess || hipEventRecord(r.a, stream) != hipSuccess) {
+      // an unusable record is dropped: the launch is simply not timed
+      (void)hipEventDestroy(r.a);
+      if (r.b) (void)hipEventDestroy(r.b);
+      return;
+    }
     g_prof.push_back(r);
   } else if (!g_prof.empty() && g_prof.back().name == name && g_prof.back().b) {
-    hipEventRecord(g_prof.back().b, stream);
+    ProfRec& r = g_prof.back();
+    if (hipEventRecord(r.b, stream) != hipSuccess) {
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+      g_prof.pop_back();
+    }
   }
 }
 
 extern "C" kd_status kd_profile_begin(void) {
   for (auto& r : g_prof) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   g_prof_on = true;
@@ -71,8 +81,8 @@ extern "C" int32_t kd_profile_end(int32_t max_kernels, const char** names, float
     }
     ms[i] += t;
     cnt[i] += 1;
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   const int32_t n = (int32_t)nm.size();
