@@ -77,6 +77,19 @@ def test_ragged_multi_chunk(mode):
     _compare(g, r, f"ragged mode={mode}")
 
 
+@pytest.mark.parametrize("mode", [kd.RENORM, kd.TAIL, kd.FULL])
+@pytest.mark.parametrize("d", [192, 320])
+def test_odd_slice_counts(d, mode):
+    """The matrix-core k-loops over an odd number of 64-deep slices: d = 192
+    and 320 (3 and 5) in the forward and recompute GEMMs, and V = 2454 with
+    768-row chunks leaves a last chunk of 150 rows, a dh k-loop of 3 slices."""
+    T, V, K = 300, 2454, 13
+    h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=23)
+    g = _run(h, W, idx, tlp, mq, mode, chunk=700)
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    _compare(g, r, f"odd slices d={d} mode={mode}")
+
+
 EDGE_SIZES = {
     "one_token": (1, 64, 300, 5, 8192),
     "k_max_1024": (257, 64, 2049, 1024, 512),

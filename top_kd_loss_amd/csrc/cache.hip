@@ -275,9 +275,9 @@ struct RowShared {
       unsigned long long massR[RHO_GROUP][NB];
     } late;
   } u;
-  float ref0[NB];                               // upper edge of each level-0 bin
+  float ref0[NB];                               // reference of each level-0 bin (bin_ref)
   int cnt0[NB];                                 // level-0 counts
-  unsigned long long mass0[NB];                 // level-0 fixed-point masses, each vs its bin's upper edge
+  unsigned long long mass0[NB];                 // level-0 fixed-point masses, each vs its bin's reference
   int scan_i[RT / 64];
   double red_d[RT / 64];
   int ncand, sel_bin, sel_above, sel_eq;
@@ -290,6 +290,7 @@ struct RowShared {
   int r_cnt[RHO_GROUP], r_done[RHO_GROUP];
   uint32_t r_pre[RHO_GROUP];
   double lse;
+  float zref;                                   // the row maximum (FLT_MAX when it is not finite)
 };
 
 // Largest float whose key has prefix `p` in its top `bits` bits: the upper
@@ -300,6 +301,14 @@ __device__ __forceinline__ float bin_upper(uint32_t p, int bits) {
   const float f = __uint_as_float(u);
   return (f != f || f > 3.4028234663852886e38f) ? 3.4028234663852886e38f : f;
 }
+
+// Reference of a bin's fixed-point masses: its upper edge, capped at the row
+// maximum.  Every element of the bin is <= it, so each mass exp(z - ref) is
+// <= 1; and since ref <= zmax, rounding a mass to 2^-F costs at most 2^-F of
+// exp(zmax) however wide the bin is (the first digit's bins are 32 wide for
+// values in [128, 256): against the bare edge, the row maximum itself could
+// sit 32 below it and keep only a few bits).
+__device__ __forceinline__ float bin_ref(uint32_t p, int bits, float zref) { return fminf(bin_upper(p, bits), zref); }
 
 __device__ __forceinline__ double block_sum_d(double v, RowShared& S) {
   v = wave_sum_f64(v);
@@ -648,23 +657,37 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
   const float* zr = z + row * ldz;
   const int tid = threadIdx.x;
   const bool vec = ((V & 3) == 0) && ((((uintptr_t)zr) & 15) == 0);
-  // fixed point: a mass term exp(z - edge) <= 1 is stored as round(term * 2^F)
-  // with F = 62 - bits(V), so the sums over a bin stay exact 64-bit integers;
-  // a wide level-0 bin (width 16 for values in [64, 128)) puts its largest
-  // element far below the edge, whose mass then keeps 2^-F * e^16 precision
+  // fixed point: a mass term exp(z - ref) <= 1, ref the bin's reference
+  // (bin_ref), is stored as round(term * 2^F) with F = 62 - bits(V), so the
+  // sums over a bin stay exact 64-bit integers
   const int fx_bits = 62 - (64 - __clzll((unsigned long long)V));
   const double fxs = ldexp(1.0, fx_bits);
   const double fxs_inv = ldexp(1.0, -fx_bits);
 
+  // ---- pass 0: the row maximum, which caps the bins' references
+  {
+    float mx = -KD_INF;
+    row_loop<RT>(zr, V, vec, [&](int64_t, float x) { mx = fmaxf(mx, x); });
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) S.scan_w[tid >> 6] = (double)mx;
+    __syncthreads();
+    if (tid == 0) {
+      double m = S.scan_w[0];
+      for (int i = 1; i < RT / 64; ++i) m = fmax(m, S.scan_w[i]);
+      S.zref = (fabs(m) <= 3.4028234663852886e38) ? (float)m : 3.4028234663852886e38f;
+    }
+  }
   for (int i = tid; i < NB * NCOPY; i += RT) {
     (&S.u.copies.cnt[0][0])[i] = 0;
     (&S.u.copies.mass[0][0])[i] = 0ull;
   }
-  for (int i = tid; i < NB; i += RT) S.ref0[i] = bin_upper((uint32_t)i, 11);
+  __syncthreads();
+  const float zref = S.zref;
+  for (int i = tid; i < NB; i += RT) S.ref0[i] = bin_ref((uint32_t)i, 11, zref);
   __syncthreads();
 
   // ---- pass 1: counts and masses of the first 11-bit digit; masses are
-  // exp(z - upper edge of the element's bin), so no row maximum is needed.
+  // exp(z - reference of the element's bin).
   {
     const int cp = tid & (NCOPY - 1);
     HistRun run;
@@ -792,7 +815,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
         for (int j = 0; j < RHO_GROUP; ++j) {
           if (act[j] && (k >> (32 - pb)) == pj[j]) {
             const int dg = (int)((k >> sh) & ((1u << dbits) - 1u));
-            const float ex = __expf(x - bin_upper((pj[j] << dbits) | (uint32_t)dg, pb + dbits));
+            const float ex = __expf(x - bin_ref((pj[j] << dbits) | (uint32_t)dg, pb + dbits, zref));
             run[j].add(dg, __double2ull_rn((double)ex * fxs), S.u.late.cntR[j], S.u.late.massR[j]);
           }
         }
@@ -804,7 +827,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows_exact(const float* __restrict_
         const uint32_t p = S.r_pre[j];
         auto massj = [&](int b) {
           return S.u.late.massR[j][b] > 0 ? (double)S.u.late.massR[j][b] * fxs_inv *
-                                         exp((double)bin_upper((p << dbits) | (uint32_t)b, pb + dbits) - lse) : 0.0;
+                                         exp((double)bin_ref((p << dbits) | (uint32_t)b, pb + dbits, zref) - lse) : 0.0;
         };
         int bin, ca;
         double ma;
