@@ -87,6 +87,34 @@ def test_rows_large_magnitude_logits(shift, scale):
     _check_rows(z, 64)
 
 
+def test_rows_vocab_above_2_18_exact_kernel_only():
+    """V >= 2^18 does not fit the fast kernel's 18-bit bin counts: every row
+    takes the exact radix-digit kernel (its maximum read, three digits, the
+    k_rho refinement), here with rows near zero and far from it."""
+    r = np.random.default_rng(44)
+    z = (r.standard_normal((12, 300_001)) * 1.1).astype(np.float32)
+    z[4:8] += np.float32(170.0)
+    z[8:] = (r.standard_normal((4, 300_001)) * 25.0 - 300.0).astype(np.float32)
+    _check_rows(z, 64)
+
+
+def test_cache_build_vocab_above_2_18():
+    T, d, V, K = 20, 64, 270_000, 32
+    g, U, b = synth.teacher_head(T, d, V, seed=6)
+    o = kd.cache_build(g.to(DEV), U.to(DEV), b.to(DEV), K, RHO)
+    torch.cuda.synchronize()
+    z = synth.as_f64(g) @ synth.as_f64(U).T + b.double().numpy()[None, :]
+    _, _, rlse, rmq, _ = oracle.cache_from_logits(z, K, RHO)
+    gi = o.idx.cpu().numpy()
+    np.testing.assert_allclose(o.lse.cpu().numpy(), rlse, atol=1e-4)
+    np.testing.assert_allclose(o.m_q.cpu().numpy(), rmq, atol=1e-5)
+    for t in range(T):
+        kth = np.sort(z[t])[::-1][K - 1]
+        assert np.all(z[t, gi[t]] >= kth - 2e-4) and len(set(gi[t].tolist())) == K
+        for j, rr in enumerate(RHO):
+            assert _krho_ok(z[t], rlse[t], rr, int(o.k_rho.cpu().numpy()[t, j]))
+
+
 def test_rows_ties_signed_zero_neg_inf():
     z = synth.tie_heavy_logits(24, 3001, seed=1, step=0.25, span=2.0)
     z[0, :] = 0.5                      # one big tie: lowest indices win
