@@ -180,6 +180,28 @@ def test_cache_build_small_with_bias():
             assert _krho_ok(z[t], rlse[t], r, int(gk[t, j]))
 
 
+def test_cache_build_ragged_last_token_block():
+    """T = 2 * 2048 + 300: the cache build works in blocks of 2048 tokens
+    (one GEMM and one row pass per block); the last block is partial.  Every
+    row against the oracle."""
+    T, d, V, K = 2 * 2048 + 300, 64, 3000, 16
+    g, U, b = synth.teacher_head(T, d, V, seed=12)
+    o = kd.cache_build(g.to(DEV), U.to(DEV), b.to(DEV), K, RHO)
+    torch.cuda.synchronize()
+    z = synth.as_f64(g) @ synth.as_f64(U).T + b.double().numpy()[None, :]
+    _, _, rlse, rmq, _ = oracle.cache_from_logits(z, K, RHO)
+    gi, gv, gk = o.idx.cpu().numpy(), o.val.cpu().numpy(), o.k_rho.cpu().numpy()
+    np.testing.assert_allclose(o.lse.cpu().numpy(), rlse, atol=1e-4)
+    np.testing.assert_allclose(o.m_q.cpu().numpy(), rmq, atol=1e-5)
+    np.testing.assert_allclose(gv, np.take_along_axis(z, gi.astype(np.int64), 1), atol=1e-4)
+    kth = -np.sort(-z, axis=1)[:, K - 1]
+    assert np.all(np.take_along_axis(z, gi.astype(np.int64), 1) >= kth[:, None] - 2e-4)
+    assert all(len(set(gi[t].tolist())) == K for t in range(T))
+    for t in range(0, T, 97):
+        for j, r in enumerate(RHO):
+            assert _krho_ok(z[t], rlse[t], r, int(gk[t, j])), (t, r)
+
+
 def test_cache_build_student_head_no_bias():
     T, d, V, K = 64, 64, 1024, 16
     h, W = synth.student_head(T, d, V, seed=9)

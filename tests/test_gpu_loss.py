@@ -187,6 +187,29 @@ def test_worked_example_fig2():
             assert abs(g["loss_tok"][1] - gold["full_vocab_kl_after_nats"]) < tol + 5e-3
 
 
+@pytest.mark.parametrize("mode", ALL_MODES)
+def test_contiguous_support_fills_whole_tiles(mode):
+    """Each token's support is 300 consecutive indices from a token-dependent
+    offset, so whole 256-row vocabulary tiles are retained (their off-S
+    partials are empty) next to partly retained ones and the mask words are
+    full.  Teacher log-probabilities come from Zipf-like rows (fp64
+    log-softmax, gathered at the support)."""
+    T, d, V, K = 64, 64, 3000, 300
+    h, W = synth.student_head(T, d, V, seed=41)
+    off = (np.arange(T) * 37) % (V - K)
+    idx = (off[:, None] + np.arange(K)[None, :]).astype(np.int32)
+    zt = synth.zipf_teacher_logits(T, V, seed=41).astype(np.float64)
+    lq = zt - zt.max(1, keepdims=True)
+    lq -= np.log(np.exp(lq).sum(1, keepdims=True))
+    tlp = np.take_along_axis(lq, idx, 1).astype(np.float32)
+    mq = np.clip(1.0 - np.exp(tlp.astype(np.float64)).sum(1), 0.0, 1.0).astype(np.float32)
+    if mode == kd.REVERSE:
+        mq[:] = 0.0
+    g = _run(h, W, idx, tlp, mq, mode, chunk=512)
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    _compare(g, r, f"contiguous support mode={mode}")
+
+
 def test_full_vocab_k_equals_v_is_dense_kl():
     """K = V: every forward mode equals the dense KL (computed by torch's
     kl_div on the fp64 logits), gradient p - q."""
