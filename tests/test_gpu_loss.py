@@ -124,6 +124,8 @@ def test_student_logits_far_from_zero(shift, mode):
 
 
 EDGE_SIZES = {
+    "k_1": (100, 64, 1000, 1, 512),
+    "k_2": (100, 64, 1000, 2, 512),
     "one_token": (1, 64, 300, 5, 8192),
     "k_max_1024": (257, 64, 2049, 1024, 512),
     "d_max_16384": (3, 16384, 700, 4, 8192),
@@ -134,8 +136,9 @@ EDGE_SIZES = {
 @pytest.mark.parametrize("mode", ALL_MODES)
 @pytest.mark.parametrize("case", sorted(EDGE_SIZES))
 def test_edge_sizes(case, mode):
-    """A single token; the largest K (1,024) over several chunks; the largest
-    d (16,384); a 7-word vocabulary with K = V (one partial tile)."""
+    """K = 1 and 2 (top-1 / top-2 supports); a single token; the largest K
+    (1,024) over several chunks; the largest d (16,384); a 7-word vocabulary
+    with K = V (one partial tile)."""
     T, d, V, K, chunk = EDGE_SIZES[case]
     h, W, idx, tlp, mq = _case(T, d, V, K, mode, seed=17)
     g = _run(h, W, idx, tlp, mq, mode, chunk=chunk)
