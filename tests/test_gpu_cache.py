@@ -202,6 +202,27 @@ def test_cache_build_ragged_last_token_block():
             assert _krho_ok(z[t], rlse[t], r, int(gk[t, j])), (t, r)
 
 
+@pytest.mark.parametrize("T,d,V,K", [(1, 64, 1000, 8), (50, 64, 7, 7), (33, 128, 100, 3)])
+def test_cache_build_single_token_and_tiny_vocab(T, d, V, K):
+    """One token; a vocabulary of 7 with K = V and one of 100 (a single
+    partial 256-row tile of the GEMM, one partial row of the row pass)."""
+    g, U, b = synth.teacher_head(T, d, V, seed=13)
+    o = kd.cache_build(g.to(DEV), U.to(DEV), b.to(DEV), K, RHO)
+    torch.cuda.synchronize()
+    z = synth.as_f64(g) @ synth.as_f64(U).T + b.double().numpy()[None, :]
+    _, _, rlse, rmq, _ = oracle.cache_from_logits(z, K, RHO)
+    gi, gv, gk = o.idx.cpu().numpy(), o.val.cpu().numpy(), o.k_rho.cpu().numpy()
+    np.testing.assert_allclose(o.lse.cpu().numpy(), rlse, atol=1e-4)
+    np.testing.assert_allclose(o.m_q.cpu().numpy(), rmq, atol=1e-5)
+    np.testing.assert_allclose(gv, np.take_along_axis(z, gi.astype(np.int64), 1), atol=1e-4)
+    kth = -np.sort(-z, axis=1)[:, K - 1]
+    assert np.all(np.take_along_axis(z, gi.astype(np.int64), 1) >= kth[:, None] - 2e-4)
+    assert all(len(set(gi[t].tolist())) == K for t in range(T))
+    for t in range(T):
+        for j, r in enumerate(RHO):
+            assert _krho_ok(z[t], rlse[t], r, int(gk[t, j])), (t, r)
+
+
 def test_cache_build_student_head_no_bias():
     T, d, V, K = 64, 64, 1024, 16
     h, W = synth.student_head(T, d, V, seed=9)
