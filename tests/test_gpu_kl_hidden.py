@@ -41,12 +41,15 @@ def _check(gout, r, tag):
     return e_dh, e_dw
 
 
-@pytest.mark.parametrize("shape", ["tiny", "ragged"])
+# "odd": k-loops over 3 (d = 192) and 5 (d_t = 320) slices of 64, and a last
+# 150-row chunk whose dh loop has 3
+SHAPES = {"tiny": (64, 64, 128, 1024, 8192, 0), "ragged": (300, 128, 64, 2500, 700, 3),
+          "odd": (200, 192, 320, 2454, 700, 5)}
+
+
+@pytest.mark.parametrize("shape", ["tiny", "ragged", "odd"])
 def test_kl_hidden_matches_oracle(shape):
-    if shape == "tiny":
-        T, d, dt, V, chunk, seed = 64, 64, 128, 1024, 8192, 0
-    else:
-        T, d, dt, V, chunk, seed = 300, 128, 64, 2500, 700, 3
+    T, d, dt, V, chunk, seed = SHAPES[shape]
     h, W, g, U, b = _inputs(T, d, dt, V, seed)
     gout = _gpu(h, W, g, U, b, chunk)
     r = oracle.kl_hidden_fwd_bwd(synth.as_f64(h), synth.as_f64(W), synth.as_f64(g), synth.as_f64(U),
@@ -123,12 +126,9 @@ def test_int8_quantize_codes_bit_exact():
     np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
 
 
-@pytest.mark.parametrize("shape", ["tiny", "ragged"])
+@pytest.mark.parametrize("shape", ["tiny", "ragged", "odd"])
 def test_kl_hidden_int8_cache(shape):
-    if shape == "tiny":
-        T, d, dt, V, chunk, seed = 64, 64, 128, 1024, 8192, 0
-    else:
-        T, d, dt, V, chunk, seed = 300, 128, 64, 2500, 700, 3
+    T, d, dt, V, chunk, seed = SHAPES[shape]
     h, W, g, U, b = _inputs(T, d, dt, V, seed)
     # the cache comes from the oracle's quantizer (the GPU's is checked bit-exactly above)
     rq, rs = oracle.quantize_hidden_int8(g.float().numpy())
