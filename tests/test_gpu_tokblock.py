@@ -63,6 +63,19 @@ def test_ragged_several_blocks(mode):
         assert np.array_equal(g[key].view(np.uint32), c[key].view(np.uint32)), key
 
 
+@pytest.mark.parametrize("mode", DENSE)
+def test_odd_slice_counts_two_blocks(mode):
+    """d = 192 (forward k-loop of 3 slices of 64) and V = 2454 (the dh k-loop
+    over the whole vocabulary rounded to 64: 39 slices), two token blocks
+    (256 and 144 tokens)."""
+    T, d, V, K = 400, 192, 2454, 13
+    h, W = synth.student_head(T, d, V, seed=8)
+    idx, tlp, mq = teacher_cache(T, V, K, seed=8)
+    g = _run(h, W, idx, tlp, mq, mode, token_block=256)
+    r = oracle.loss_fwd_bwd(synth.as_f64(h), synth.as_f64(W), idx, tlp, mq, mode)
+    _compare(g, r, f"odd-slice token-block mode={oracle.MODE_NAMES[mode]}")
+
+
 def test_peaked_student_tail():
     """The peaked-student case (m_p ~ 1e-11, m_q = 0.3) through the token-block
     path: the off-S factor A e^(m - B) with B = lse_off stays bounded."""
