@@ -256,9 +256,9 @@ def main():
     ap.add_argument("--token-block", type=int, default=0,
                     help="time the token-block option (kd_topk_loss_fwd_bwd_tokblock, this many tokens per block) "
                          "as the step instead of the vocabulary-chunked call")
-    ap.add_argument("--only", choices=["cache_build", "topk_rows"],
-                    help="only run the teacher-cache build (T=16384, d=4096) or the standalone row pass and print "
-                         "its JSON (for profiling)")
+    ap.add_argument("--only", choices=["cache_build", "topk_rows", "llama_k256"],
+                    help="only run the teacher-cache build (T=16384, d=4096), the standalone row pass, or the "
+                         "Llama-3.2-1B-shaped head at K=256 (sparse backward) and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); multi-GPU runs are not part of this build",
@@ -287,6 +287,9 @@ def main():
         return
     if args.only == "topk_rows":
         print(json.dumps(bench_topk_rows(torch, kd, dev, steps=max(1, args.steps))), flush=True)
+        return
+    if args.only == "llama_k256":
+        print(json.dumps(bench_llama_k256(torch, kd, synth, dev, steps=max(1, args.steps))), flush=True)
         return
     cfg = HEAD_CFG
     T, d, V, K, chunk = cfg["T"], cfg["d"], cfg["V"], cfg["K"], cfg["chunk"]
