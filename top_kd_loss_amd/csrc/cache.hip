@@ -153,7 +153,10 @@ __global__ __launch_bounds__(256, 1) void k_cache_gemm(const bf16_t* __restrict_
       if (t < Tb) {
         float* dst = z + t * V + v;
         if (vec) {
-          *(f32x4*)dst = x;
+          // streamed past the caches: the block (1.2 GB at 2048 tokens) is far
+          // larger than them, and the row pass then reads clean memory instead
+          // of competing with the write-back of dirty lines
+          __builtin_nontemporal_store(x, (f32x4*)dst);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
