@@ -832,7 +832,9 @@ __device__ __forceinline__ void zdz_tile(const bf16_t* __restrict__ W, const bf1
   for (int it = 0; it < TT / 8; ++it) {
     const int tl = it * 8 + (tid >> 5), c = tid & 31;
     const u32x4 q = *(const u32x4*)(E + tl * (VT * 2) + ((c ^ zdz_swz(tl)) << 4));
-    *(u32x4*)(dz + (n0 + tl) * Cp + vo + c * 8) = q;
+    // streamed past the caches (the chunk's dz, 0.5 GB at T = 32K, is far larger
+    // than them): k_dhdw then reads it without competing write-backs
+    __builtin_nontemporal_store(q, (u32x4*)(dz + (n0 + tl) * Cp + vo + c * 8));
   }
 }
 
@@ -1310,7 +1312,7 @@ __device__ __forceinline__ void zdz_kl_tile(const bf16_t* __restrict__ W, const 
   for (int it = 0; it < TT / 8; ++it) {
     const int tl = it * 8 + (tid >> 5), cc = tid & 31;
     const u32x4 q = *(const u32x4*)(E + tl * (VT * 2) + ((cc ^ zdz_swz(tl)) << 4));
-    *(u32x4*)(dz + (n0 + tl) * Cp + vo + cc * 8) = q;
+    __builtin_nontemporal_store(q, (u32x4*)(dz + (n0 + tl) * Cp + vo + cc * 8));  // as in k_zdz
   }
 }
 
